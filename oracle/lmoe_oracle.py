@@ -1,0 +1,318 @@
+"""CPU fp64 oracle of one Stable Latent MoE layer forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call
+this module: only tests/, the smoke check in __graft_entry__ and the
+benchmark's cpu_baseline leg use it.  It shares no code with the HIP
+library; it reads the same storage bytes (fp32, bf16 bit patterns, e4m3fn
+codes with fp32 block scales), decodes them exactly and computes every step
+in float64 with numpy, one plain step after another.
+
+Sources (the pages describe the layer only in prose; no formula is printed):
+  P1  aitrending.vip, "The 2.8-Trillion-Parameter Problem: Why Bigger Models
+      Break the Old Playbook" -- TL;DR and Technical Details bullets.
+  P2  wpnews.pro, same title, Part 1 of "Inside Kimi K3" -- the MoE passage
+      ("From a dense feed-forward layer to 896 experts"), the Stable
+      LatentMoE passage and the stabilizer passage that follows it.
+  P3  daily-ai-frontier, "苏神复盘 Kimi K3：896 个专家背后，藏着哪些关键技术取舍？"
+      -- Merged summary, LatentMoE and Stable LatentMoE bullets.
+
+Readings taken where the pages are silent (each is a documented choice):
+  * router scores are sigmoid(x . W_r^T); a per-expert bias is added for
+    selection only; the k selected scores, renormalised to sum to 1, are the
+    combine weights; ties in the biased score go to the lower expert index;
+  * SiTU-GLU(g, v) = silu(cap(g)) * cap(v) with cap(u) = c * tanh(u / c),
+    c = 100 by default;
+  * RMSNorm n = gamma * c / sqrt(mean(c^2) + eps) with eps = 1e-6;
+  * shared experts run at full width on x, use the same SiTU-GLU, have
+    weight 1 and are added after the up-projection;
+  * no capacity limit (no token is dropped), no biases in the linears, and
+    the residual add is outside the layer.
+
+Parity pins: every function here is pinned by tests/test_oracle.py against
+library routines (torch/scipy), closed forms, invariants or brute force; the
+chosen readings above are conventions and are pinned only through those
+properties.
+"""
+
+import numpy as np
+
+F8_BLOCK = 128
+
+
+# ----------------------------------------------------------------------------
+# Storage decoding (exact)
+# ----------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits):
+    """bf16 bit patterns (uint16) -> float64.  A bf16 value is the upper half
+    of the fp32 with the same bits, so widening is exact."""
+    b = np.asarray(bits, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):  # NaN payloads widen to NaN
+        return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _e4m3fn_table():
+    """Value of every OCP e4m3fn code: 1 sign bit, 4 exponent bits (bias 7),
+    3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN;
+    there are no infinities, so the largest finite magnitude is 448."""
+    tab = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        s = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 0x7
+        if e == 0xF and m == 0x7:
+            tab[code] = np.nan
+        elif e == 0:
+            tab[code] = s * (m / 8.0) * 2.0 ** (1 - 7)
+        else:
+            tab[code] = s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return tab
+
+
+E4M3FN = _e4m3fn_table()
+
+
+def e4m3fn_to_f64(codes):
+    return E4M3FN[np.asarray(codes, dtype=np.uint8)]
+
+
+def decode(raw, tag):
+    """Raw storage -> float64.  tag: "f32" (float32 array), "bf16" (uint16
+    bits), "f8" (uint8 e4m3fn codes, unscaled), "f64" (already float)."""
+    if raw is None:
+        return None
+    if tag == "f32":
+        return np.asarray(raw, dtype=np.float32).astype(np.float64)
+    if tag == "bf16":
+        return bf16_bits_to_f64(raw)
+    if tag == "f8":
+        return e4m3fn_to_f64(raw)
+    if tag == "f64":
+        return np.asarray(raw, dtype=np.float64)
+    raise ValueError(f"unknown storage tag {tag!r}")
+
+
+def dequant_blocks(codes, scales):
+    """fp8 matrix [R, C] with one fp32 scale per 128x128 block: value = q*s."""
+    q = e4m3fn_to_f64(codes)
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    return q * np.repeat(np.repeat(s, F8_BLOCK, axis=0), F8_BLOCK, axis=1)
+
+
+def matrix(stack, scales, idx, tag):
+    """Decoded fp64 matrix idx of a stacked weight tensor (experts or shared
+    experts).  `stack` may be any indexable whose items are raw arrays."""
+    raw = stack[idx]
+    if tag == "f8":
+        return dequant_blocks(raw, scales[idx])
+    return decode(raw, tag)
+
+
+# ----------------------------------------------------------------------------
+# Elementwise pieces
+# ----------------------------------------------------------------------------
+
+def sigmoid(u):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-u))
+
+
+def silu(u):
+    """SiLU / swish: u * sigmoid(u)."""
+    return u * sigmoid(u)
+
+
+def cap(u, c):
+    """Smooth cap to about +-c (P2 stabilizer passage: gate and value are
+    bounded to roughly +-100 yet behave like SwiGLU near zero; P3 Stable
+    LatentMoE bullet: soft cap of SwiGLU outliers).  c = inf means no cap."""
+    if not np.isfinite(c):
+        return u
+    return c * np.tanh(u / c)
+
+
+def situ_glu(g, v, c):
+    """SiTU-GLU: SwiGLU applied to capped gate and value branches."""
+    return silu(cap(g, c)) * cap(v, c)
+
+
+# ----------------------------------------------------------------------------
+# Layer steps
+# ----------------------------------------------------------------------------
+
+def select_topk(biased, k):
+    """Per token, the k experts with the largest biased score, in descending
+    score order, equal scores ordered by ascending expert index (a library
+    sort on the key (-score, index)).  Also returns gap = k-th minus
+    (k+1)-th biased score (inf when k == E)."""
+    T, E = biased.shape
+    if T == 0:
+        return np.zeros((0, k), np.int64), np.zeros((0,), np.float64)
+    order = np.lexsort((np.broadcast_to(np.arange(E), (T, E)), -biased), axis=-1)
+    idx = order[:, :k]
+    rows = np.arange(T)
+    if k < E:
+        gap = biased[rows, order[:, k - 1]] - biased[rows, order[:, k]]
+    else:
+        gap = np.full(T, np.inf)
+    return idx, gap
+
+
+def route(x, w_router, b_router, k):
+    """Router (P1 Technical Details: a lightweight router picks 16 of 896 per
+    token; P2 MoE passage).  Scores s = sigmoid(x W_r^T); selection on s + b;
+    combine weights = selected s renormalised to sum 1."""
+    logits = x @ w_router.T
+    scores = sigmoid(logits)
+    biased = scores + b_router[None, :]
+    idx, gap = select_topk(biased, k)
+    w = combine_weights(scores, idx)
+    return dict(logits=logits, scores=scores, biased=biased, idx=idx, gap=gap, w=w)
+
+
+def combine_weights(scores, idx):
+    sel = np.take_along_axis(scores, idx, axis=1)
+    if sel.shape[0] == 0:
+        return sel
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
+def check_forced(biased, forced_idx, tol):
+    """A given selection is accepted if its k experts are distinct, in range,
+    and each has a biased score within tol of the k-th largest score."""
+    T, E = biased.shape
+    f = np.asarray(forced_idx, dtype=np.int64)
+    k = f.shape[1]
+    if f.shape[0] != T:
+        raise ValueError("forced_idx has the wrong number of tokens")
+    if T == 0:
+        return f
+    if f.min() < 0 or f.max() >= E:
+        raise ValueError("forced_idx holds an expert index out of range")
+    if any(len(set(r.tolist())) != k for r in f):
+        raise ValueError("forced_idx repeats an expert within a token")
+    kth = -np.sort(-biased, axis=1)[:, k - 1]
+    chosen = np.take_along_axis(biased, f, axis=1)
+    worst = (kth[:, None] - chosen).max()
+    if worst > tol:
+        raise ValueError(f"forced_idx is not a top-k selection: an expert lies {worst:.3g} below the k-th score")
+    return f
+
+
+def latent_down(x, w_down):
+    """Routed path only: x (hidden) -> z (latent), P2 Stable LatentMoE
+    passage; with no projection the latent is x itself."""
+    return x if w_down is None else x @ w_down.T
+
+
+def permute(idx, E):
+    """Group the T*k (token, slot) assignments a = t*k + j by expert with a
+    stable library sort on the expert id: within an expert, assignments keep
+    ascending a, i.e. ascending token.  offsets[e]..offsets[e+1] is expert
+    e's range of `sorted`; pos is the inverse permutation."""
+    flat = np.asarray(idx, dtype=np.int64).reshape(-1)
+    counts = np.bincount(flat, minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    sorted_ = np.argsort(flat, kind="stable").astype(np.int64)
+    pos = np.empty_like(sorted_)
+    pos[sorted_] = np.arange(flat.size)
+    return offsets, sorted_, pos
+
+
+def expert_ffn(zrows, wg, wv, wo, c):
+    """One routed expert on its latent rows: gated FFN with gate and value
+    branches (P2 stabilizer passage) and the SiTU-GLU activation."""
+    a = situ_glu(zrows @ wg.T, zrows @ wv.T, c)
+    return a, a @ wo.T
+
+
+def combine(O, pos, w):
+    """Weighted sum of each token's k expert outputs, slot j ascending (P2
+    Stable LatentMoE passage: the selected experts' outputs are combined)."""
+    T, k = w.shape
+    out = np.zeros((T, O.shape[1]))
+    for j in range(k):
+        out += w[:, j:j + 1] * O[pos.reshape(T, k)[:, j]]
+    return out
+
+
+def rmsnorm(c, gamma, eps):
+    """RMSNorm after aggregation, before the up-projection (P2 stabilizer
+    passage; P3 Stable LatentMoE bullet)."""
+    return gamma[None, :] * c / np.sqrt(np.mean(c * c, axis=1, keepdims=True) + eps)
+
+
+def shared_experts(x, ws_gate, ws_value, ws_out, ss, tag, S, c):
+    """Always-on shared experts (P1 Technical Details; P3 LatentMoE bullet)
+    at full width on x, weight 1, summed."""
+    y = np.zeros((x.shape[0], x.shape[1]))
+    for s in range(S):
+        wg = matrix(ws_gate, ss[0], s, tag)
+        wv = matrix(ws_value, ss[1], s, tag)
+        wo = matrix(ws_out, ss[2], s, tag)
+        y += situ_glu(x @ wg.T, x @ wv.T, c) @ wo.T
+    return y
+
+
+def forward(inp, spec, forced_idx=None, forced_tol=1e-3):
+    """Whole layer.  `inp` holds raw storage arrays under the keys x,
+    w_router, b_router, w_down, w_gate, w_value, w_out, s_gate, s_value,
+    s_out, gamma, w_up, ws_gate, ws_value, ws_out, ss_gate, ss_value, ss_out
+    (expert stacks may be any indexable over experts).  `spec` gives act,
+    w_expert, k, cap, eps.  Returns every intermediate as float64/int64.
+
+    Steps: route on x; z = latent down-projection of x; tokens grouped by
+    expert; each expert's SiTU-GLU FFN on its latent rows; weighted combine;
+    RMSNorm; up-projection to full width; plus the shared experts (P2 Stable
+    LatentMoE passage and stabilizer passage; P3 LatentMoE bullets)."""
+    act, wt = spec["act"], spec["w_expert"]
+    k, c, eps = int(spec["k"]), float(spec["cap"]), float(spec["eps"])
+    x = decode(inp["x"], act)
+    w_router = decode(inp["w_router"], act)
+    b = np.asarray(inp["b_router"], dtype=np.float32).astype(np.float64)
+    w_down = decode(inp.get("w_down"), act)
+    w_up = decode(inp.get("w_up"), act)
+    gamma = np.asarray(inp["gamma"], dtype=np.float32).astype(np.float64)
+    T, H = x.shape
+    E = w_router.shape[0]
+
+    r = route(x, w_router, b, k)
+    if forced_idx is not None:
+        r["idx"] = check_forced(r["biased"], forced_idx, forced_tol)
+        r["w"] = combine_weights(r["scores"], r["idx"])
+    idx, w = r["idx"], r["w"]
+
+    z = latent_down(x, w_down)
+    L = z.shape[1]
+    offsets, sorted_, pos = permute(idx, E)
+    I = None
+    A = None
+    O = np.zeros((T * k, L))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        toks = sorted_[lo:hi] // k
+        wg = matrix(inp["w_gate"], inp.get("s_gate"), e, wt)
+        wv = matrix(inp["w_value"], inp.get("s_value"), e, wt)
+        wo = matrix(inp["w_out"], inp.get("s_out"), e, wt)
+        a, o = expert_ffn(z[toks], wg, wv, wo, c)
+        if A is None:
+            I = a.shape[1]
+            A = np.zeros((T * k, I))
+        A[lo:hi] = a
+        O[lo:hi] = o
+    if A is None:
+        A = np.zeros((T * k, 0))
+
+    comb = combine(O, pos, w)
+    n = rmsnorm(comb, gamma, eps)
+    up = n if w_up is None else n @ w_up.T
+    S = 0 if inp.get("ws_gate") is None else len(inp["ws_gate"])
+    sh = shared_experts(x, inp.get("ws_gate"), inp.get("ws_value"), inp.get("ws_out"),
+                        (inp.get("ss_gate"), inp.get("ss_value"), inp.get("ss_out")), wt, S, c)
+    y = up + sh
+    out = dict(r)
+    out.update(z=z, offsets=offsets, sorted=sorted_, pos=pos, A=A, O=O, c=comb, n=n,
+               shared=sh, y=y)
+    return out
