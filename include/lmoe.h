@@ -1,0 +1,193 @@
+/*
+ * lmoe.h -- C ABI of the Stable Latent MoE layer forward pass on MI355X (gfx950).
+ *
+ * The layer (one MoE feed-forward block of a decoder) computes, per token:
+ *   1. router: scores s = sigmoid(x . W_r^T) over E routed experts; the k experts
+ *      with the largest s + b are selected (b: per-expert bias, used for the
+ *      selection only); their scores, renormalised to sum 1, are the combine
+ *      weights;
+ *   2. latent down-projection z = x . W_dn^T (hidden H -> latent L);
+ *   3. tokens grouped per expert; each selected expert runs a gated FFN on z with
+ *      the SiTU-GLU activation silu(cap(g)) * cap(v), cap(u) = c * tanh(u / c);
+ *   4. weighted combine of the k expert outputs, then RMSNorm with gain gamma;
+ *   5. up-projection back to H, plus S always-on shared experts (full width, on x).
+ * The residual add is left to the caller.
+ *
+ * Sources -- the pages describe the layer in prose only:
+ *   P1 aitrending.vip, "The 2.8-Trillion-Parameter Problem: Why Bigger Models
+ *      Break the Old Playbook", TL;DR and Technical Details bullets (896 routed
+ *      experts, 16 active, 2 shared; 7168 -> 3584 latent; SiTU-GLU caps gate and
+ *      value to about +-100; RMSNorm before the up-projection);
+ *   P2 wpnews.pro, same title (Part 1 of "Inside Kimi K3"): the MoE passage, the
+ *      Stable LatentMoE passage (compress before dispatch, experts work in the
+ *      latent, outputs combined then projected back; residual stays full width)
+ *      and the stabilizer passage (RMSNorm right before the up-projection;
+ *      SiTU-GLU bounds gate and value branches, SwiGLU-like near zero);
+ *   P3 daily-ai-frontier, "苏神复盘 Kimi K3：896 个专家背后，藏着哪些关键技术取舍？",
+ *      Merged summary, LatentMoE and Stable LatentMoE bullets (norm after expert
+ *      aggregation and before the up-projection; shared experts always on; soft
+ *      cap against BF16/FP8 range blow-up).
+ * Choices the pages leave open (scoring function, combine weights, tie order,
+ * SiTU-GLU formula, eps, expert width, shared width, fp8 layout) are fixed as
+ * stated at each declaration below.
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major [out, in] (weights) and [rows, cols] (activations).
+ *   - Every tensor pointer is a device pointer owned by the caller.  The library
+ *     never allocates or frees device memory; scratch comes from `ws`, a caller
+ *     buffer of at least lmoe_workspace_bytes(shape) bytes, 256-byte aligned.
+ *   - Inputs are read only.  Outputs must not alias inputs or each other.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
+ *     stream) and never synchronise with the host; no work depends on a
+ *     host-side copy of device data.
+ *   - The return value reports argument validation (LMOE_EINVAL, LMOE_EUNSUPPORTED
+ *     for a shape/dtype combination with no kernel -- there is no fallback,
+ *     LMOE_EWORKSPACE) and launch failures (LMOE_EHIP).  A fault inside a kernel
+ *     surfaces at the caller's next synchronisation.  lmoe_last_error() returns a
+ *     message for the calling thread's last failure.  No C++ exception crosses
+ *     the ABI.  The library holds no mutable global state: calls on different
+ *     streams are independent if their workspaces differ.
+ */
+#ifndef LMOE_H
+#define LMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LMOE_OK = 0,
+  LMOE_EINVAL = 1,        /* null pointer, negative or inconsistent sizes       */
+  LMOE_EUNSUPPORTED = 2,  /* valid layer, but no kernel for this shape / dtype  */
+  LMOE_EWORKSPACE = 3,    /* ws_bytes below lmoe_workspace_bytes(shape)         */
+  LMOE_EHIP = 4           /* a HIP launch or attribute call failed              */
+} lmoe_status;
+
+typedef enum {
+  LMOE_F32 = 0,           /* IEEE binary32                                       */
+  LMOE_BF16 = 1,          /* bfloat16                                           */
+  LMOE_F8E4M3 = 2         /* OCP e4m3fn (bias 7, max 448, no inf), weights only  */
+} lmoe_dtype;
+
+/* Layer shape.  act: dtype of x, y, the router / down / up weights and every
+ * activation the library writes (z, n, expert outputs): LMOE_F32 or LMOE_BF16.
+ * w_expert: dtype of the routed and shared expert FFN weights: LMOE_F32 with an
+ * F32 layer, LMOE_BF16 or LMOE_F8E4M3 with a BF16 layer.  cap: SiTU-GLU cap c
+ * (> 0; +inf turns the cap off, giving SwiGLU).  rms_eps: RMSNorm epsilon (>= 0).
+ * Supported sizes: H, L, I, Is multiples of 64 (of 128 with F8E4M3 weights),
+ * L <= 8192, 1 <= k <= min(E, 64), E <= 1024, 0 <= S <= 8, T * k < 2^31.        */
+typedef struct {
+  int64_t T;              /* tokens (0 is a valid, empty call)                  */
+  int32_t H;              /* hidden width                                        */
+  int32_t L;              /* latent width                                        */
+  int32_t E;              /* routed experts                                      */
+  int32_t k;              /* experts selected per token                          */
+  int32_t I;              /* routed expert intermediate width                    */
+  int32_t S;              /* shared experts                                      */
+  int32_t Is;             /* shared expert intermediate width                    */
+  int32_t act;            /* lmoe_dtype                                          */
+  int32_t w_expert;       /* lmoe_dtype                                          */
+  float cap;              /* SiTU-GLU cap, 100 in the K3 layer                   */
+  float rms_eps;          /* RMSNorm epsilon, 1e-6                               */
+} lmoe_shape;
+
+/* Weights.  Expert stacks are [E, I, L] (gate, value) and [E, L, I] (out);
+ * shared stacks [S, Is, H] (gate, value) and [S, H, Is] (out).  With F8E4M3
+ * expert weights every expert matrix carries one fp32 scale per 128x128 block,
+ * row-major over blocks: s_gate [E, I/128, L/128], s_value [E, I/128, L/128],
+ * s_out [E, L/128, I/128], ss_gate/ss_value [S, Is/128, H/128], ss_out
+ * [S, H/128, Is/128]; the weight value is code * scale.  Scale pointers are
+ * ignored for other dtypes.  w_down = NULL and w_up = NULL select identity
+ * projections (a MoE with no latent; needs L == H).                              */
+typedef struct {
+  const void *w_router;   /* [E, H]  act dtype                                  */
+  const float *b_router;  /* [E]     selection bias                             */
+  const void *w_down;     /* [L, H]  act dtype, or NULL                         */
+  const void *w_gate;     /* [E, I, L] w_expert dtype                            */
+  const void *w_value;    /* [E, I, L]                                          */
+  const void *w_out;      /* [E, L, I]                                          */
+  const float *s_gate, *s_value, *s_out;
+  const float *gamma;     /* [L]     RMSNorm gain                               */
+  const void *w_up;       /* [H, L]  act dtype, or NULL                         */
+  const void *ws_gate;    /* [S, Is, H] w_expert dtype (NULL when S == 0)        */
+  const void *ws_value;   /* [S, Is, H]                                         */
+  const void *ws_out;     /* [S, H, Is]                                         */
+  const float *ss_gate, *ss_value, *ss_out;
+} lmoe_weights;
+
+/* Host-only argument check (no GPU call): the checks every entry point runs
+ * first, for the whole layer.  ws_bytes is compared with the requirement.     */
+lmoe_status lmoe_validate(const lmoe_shape *shape, const lmoe_weights *w, size_t ws_bytes);
+
+/* Workspace bytes that suffice for every entry point below at this shape;
+ * 0 for an invalid shape.                                                      */
+size_t lmoe_workspace_bytes(const lmoe_shape *shape);
+
+/* Whole layer: y[T, H] (act dtype) = up(RMSNorm(combine(experts(z)))) + shared(x)
+ * for x[T, H] (P2 Stable LatentMoE and stabilizer passages; P3 Stable LatentMoE
+ * bullet).  topk_idx [T, k] int32 and topk_w [T, k] fp32 receive the selection
+ * and combine weights if not NULL.  stage_events: NULL, or an array of
+ * LMOE_NUM_STAGES + 1 hipEvent_t recorded on `stream` before the first stage
+ * and after each stage (route GEMM, top-k, permute, expert gate/value GEMM,
+ * expert down GEMM, combine + norm, up GEMM), for timing.                        */
+#define LMOE_NUM_STAGES 7
+lmoe_status lmoe_forward(const lmoe_shape *shape, const lmoe_weights *w, const void *x, void *y,
+                         int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+                         void *stream, void *const *stage_events);
+
+/* Router and latent down-projection (P1 Technical Details; P2 MoE and Stable
+ * LatentMoE passages).  One GEMM over x serves both: logits = x . W_r^T in fp32
+ * (products of act-dtype operands, fp32 accumulation), z = x . W_dn^T (act
+ * dtype; z = x when w_down is NULL, in which case z is not written and may be
+ * NULL).  Then per token: s = sigmoid(logit) in fp32, the k largest s + b in
+ * descending order, equal values ordered by ascending expert index, written to
+ * topk_idx [T, k]; topk_w [T, k] = selected s / their sum.                       */
+lmoe_status lmoe_route(const lmoe_shape *shape, const lmoe_weights *w, const void *x,
+                       int32_t *topk_idx, float *topk_w, void *z, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/* Group the T*k assignments a = t*k + j by expert with a stable counting sort:
+ * offsets [E+1] (offsets[e]..offsets[e+1] is expert e's range), sorted [T*k]
+ * (assignment ids, ascending token within an expert), pos [T*k] (inverse:
+ * sorted[pos[a]] == a).  An id outside [0, E), or a repeat of an id already
+ * listed earlier in the same token's row, is dropped: its pos is -1 and it is
+ * in no expert's range.                                                        */
+lmoe_status lmoe_permute(const lmoe_shape *shape, const int32_t *topk_idx, int32_t *offsets,
+                         int32_t *sorted, int32_t *pos, void *ws, size_t ws_bytes, void *stream);
+
+/* Routed experts on their latent rows (P2 stabilizer passage: gated FFN with
+ * gate and value branches, SiTU-GLU).  For each expert e and each assignment in
+ * its range, with t = sorted[i] / k: g = z[t] . W_g[e]^T, v = z[t] . W_v[e]^T,
+ * a = silu(cap(g)) * cap(v) (fp32, rounded to act dtype), expert_out[i] =
+ * a . W_o[e]^T (act dtype, [T*k, L], rows in sorted order).  z is [T, L]; pass
+ * x when w_down is NULL.  Only offsets[0..E] and sorted are read; the number of
+ * assignments handled is offsets[E].                                            */
+lmoe_status lmoe_expert_gemm(const lmoe_shape *shape, const lmoe_weights *w, const void *z,
+                             const int32_t *offsets, const int32_t *sorted, void *expert_out,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* Weighted combine and RMSNorm (P2 stabilizer passage; P3 Stable LatentMoE
+ * bullet): c = sum over j ascending of topk_w[t, j] * expert_out[pos[t*k + j]]
+ * (fp32; entries with pos < 0 skipped), n[t] = gamma * c / sqrt(mean(c^2) + eps)
+ * in act dtype, [T, L].                                                         */
+lmoe_status lmoe_combine_norm(const lmoe_shape *shape, const void *expert_out, const int32_t *pos,
+                              const float *topk_w, const float *gamma, void *n, void *stream);
+
+/* Up-projection and shared experts (P2 Stable LatentMoE passage; P1 Technical
+ * Details; P3 LatentMoE bullet): y = n . W_up^T + sum_s SiTU-GLU-FFN_s(x), with
+ * the shared experts at full width on x[T, H], weight 1; n is [T, L].           */
+lmoe_status lmoe_up(const lmoe_shape *shape, const lmoe_weights *w, const void *n, const void *x,
+                    void *y, void *ws, size_t ws_bytes, void *stream);
+
+/* Name of a status code; message of the calling thread's last failure.       */
+const char *lmoe_status_str(lmoe_status s);
+const char *lmoe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMOE_H */

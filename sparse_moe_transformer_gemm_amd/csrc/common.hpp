@@ -1,0 +1,92 @@
+// Shared device helpers for the Stable Latent MoE kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lmoe {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+enum Dtype : int { DT_F32 = 0, DT_BF16 = 1, DT_F8 = 2 };
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, WGs dealt round-robin
+
+__host__ __device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v);
+template <>
+__device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }  // RNE
+
+// SiTU-GLU: silu(cap(g)) * cap(v), cap(u) = c * tanh(u / c); an infinite cap
+// (inv_c == 0) leaves g and v unchanged (plain SwiGLU).
+__device__ __forceinline__ float situ_cap(float u, float c, float inv_c) {
+  return inv_c == 0.f ? u : c * tanhf(u * inv_c);
+}
+__device__ __forceinline__ float situ_glu(float g, float v, float c, float inv_c) {
+  const float gc = situ_cap(g, c, inv_c);
+  const float vc = situ_cap(v, c, inv_c);
+  return gc / (1.f + expf(-gc)) * vc;
+}
+
+// Work-group id -> logical index so that each XCD receives a contiguous range
+// of logical tiles (neighbouring tiles share operands in that XCD's L2).
+// `padded` is a multiple of kXcds and the grid size.
+__device__ __forceinline__ int xcd_remap(int bid, int padded) {
+  const int per = padded / kXcds;
+  return (bid % kXcds) * per + bid / kXcds;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Exclusive prefix sum over a block of NT threads (NT a multiple of 64, <= 1024).
+// `lds` holds NT/64 + 1 ints.  Returns the exclusive prefix; *total = block sum.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* lds, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) lds[wid] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < NT / 64; ++w) {
+      const int c = lds[w];
+      lds[w] = run;
+      run += c;
+    }
+    lds[NT / 64] = run;
+  }
+  __syncthreads();
+  const int ex = lds[wid] + inc - v;
+  *total = lds[NT / 64];
+  __syncthreads();
+  return ex;
+}
+
+}  // namespace lmoe

@@ -1,0 +1,583 @@
+// MFMA GEMM core for the Stable Latent MoE layer (gfx950).
+//
+// Every GEMM of the layer has the form  C[t, f] = sum_k X[t, k] * W[f, k]  with
+// both operands K-contiguous (activations [tokens, K], weights [features, K]).
+// A work-group owns a BF x BT tile (features x tokens).  Per k-tile (128 bytes
+// of K per row) the work-group stages the W and X rows into LDS (double
+// buffered through registers: the global loads of k-tile kt+1 are in flight
+// while the MFMAs of k-tile kt run), then each wave multiplies its
+// (BF/WF) x (BT/WT) sub-tile with 32x32 MFMA blocks: v_mfma_f32_32x32x16_bf16
+// for bf16 operands, v_mfma_f32_32x32x2_f32 for fp32.  The weight operand sits
+// in the MFMA's A slot, so each lane's accumulator holds 4 consecutive
+// features of one token: stores are 8/16-byte packets along the output row.
+//
+// e4m3 weights are widened in the LDS store path (two codes per
+// v_cvt_pk_f32_fp8, times the block scale, rounded to bf16), so the MFMA
+// always sees bf16.  A "problem" object supplies the tile coordinates, the row
+// addresses of both operands for each K-segment, and the epilogue.
+#pragma once
+
+#include "common.hpp"
+
+namespace lmoe {
+
+constexpr int kPitch = 144;  // LDS bytes per staged row: 128 data + 16 pad
+
+template <int BF_, int BT_, int WF_, int WT_>
+struct TileCfg {
+  static constexpr int BF = BF_, BT = BT_, WF = WF_, WT = WT_;
+  static constexpr int NT = WF * WT * kWave;
+  static constexpr int FW = BF / WF, TW = BT / WT;
+  static constexpr int FI = FW / 32, TI = TW / 32;
+  static constexpr int CW = BF * 8 / NT;  // 16-byte LDS chunks per thread, W tile
+  static constexpr int CX = BT * 8 / NT;  // same, X tile
+  static constexpr int LDS = 2 * (BF + BT) * kPitch;
+  static_assert(FW % 64 == 0, "a wave covers whole gate/value pairs");
+  static_assert(TW % 32 == 0 && CW >= 1 && CX >= 1, "tile shape");
+  static_assert((BF * 8) % NT == 0 && (BT * 8) % NT == 0, "chunk split");
+};
+
+// Big tiles for prefill-sized token counts, small ones for decode / sparse experts.
+typedef TileCfg<128, 128, 2, 2> CfgBig;
+typedef TileCfg<128, 32, 2, 1> CfgSmall;
+
+enum Epi : int { EPI_F32 = 0, EPI_STORE = 1, EPI_GLU = 2 };
+
+// ---------------------------------------------------------------------------
+// Stores of 4 consecutive outputs (features f..f+3 of one token row).
+// ---------------------------------------------------------------------------
+template <typename OT>
+__device__ __forceinline__ void store4(OT* row, int f, const float* v, int fvalid, bool vec) {
+  if (vec && f + 3 < fvalid) {
+    if constexpr (sizeof(OT) == 4) {
+      *reinterpret_cast<f32x4*>(row + f) = f32x4{v[0], v[1], v[2], v[3]};
+    } else {
+      bf16x4 p = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+      *reinterpret_cast<bf16x4*>(row + f) = p;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (f + j < fvalid) row[f + j] = from_f32<OT>(v[j]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Problem: x-GEMM (router logits, latent z, shared-expert gate/value) -- one
+// GEMM over x with the weight matrices concatenated along the features.
+// ---------------------------------------------------------------------------
+struct NSeg {
+  const char* w;      // [rows, K] (GLU: gate matrix)
+  const char* w2;     // GLU: value matrix
+  const float* sc;    // e4m3 block scales of w / w2, [rows/128, K/128]
+  const float* sc2;
+  char* out;          // output matrix
+  int64_t ldo;        // its leading dimension, elements
+  int col0;           // first output column
+  int rows;           // features (GLU: units)
+  int ft0;            // first feature tile of this segment
+  int kind;           // Epi
+  int f8;             // weights are e4m3 codes
+  int vec;            // output rows allow vector stores
+};
+
+template <class Cfg, typename CT>
+struct DenseXProb {
+  const char* x;
+  int64_t T;
+  int K;              // H
+  int nseg, nft, ntt, padded;
+  float cap, inv_cap;
+  NSeg seg[4];
+  // per work-group
+  int tt, si, f0;     // token tile, segment, first feature (GLU: unit) of the tile
+
+  __device__ bool setup(int bid) {
+    if (bid >= padded) return false;
+    const int lg = xcd_remap(bid, padded);
+    if (lg >= ntt * nft) return false;
+    // 8 token tiles per group, feature tiles run over the group: 8 neighbours
+    // share one weight tile, and an XCD's window covers a few weight tiles.
+    const int grp = lg / (8 * nft);
+    const int gsz = min(8, ntt - grp * 8);
+    const int within = lg - grp * 8 * nft;
+    const int ft = within / gsz;
+    tt = grp * 8 + within % gsz;
+    si = 0;
+    for (int s = 1; s < nseg; ++s)
+      if (ft >= seg[s].ft0) si = s;
+    const int per = seg[si].kind == EPI_GLU ? Cfg::BF / 2 : Cfg::BF;
+    f0 = (ft - seg[si].ft0) * per;
+    return true;
+  }
+  __device__ int num_ksegs() const { return 1; }
+  __device__ int seg_ktiles(int) const { return K * (int)sizeof(CT) / 128; }
+  __device__ bool seg_f8(int) const { return seg[si].f8; }
+  __device__ int tokens_valid() const { return (int)imin64(Cfg::BT, T - (int64_t)tt * Cfg::BT); }
+  __device__ int feats_valid() const {
+    // GLU tiles interleave gate/value blocks: missing units load as zeros.
+    const NSeg& s = seg[si];
+    return s.kind == EPI_GLU ? Cfg::BF : min(Cfg::BF, s.rows - f0);
+  }
+  __device__ const char* x_row(int, int r) const {
+    const int64_t t = (int64_t)tt * Cfg::BT + r;
+    return t < T ? x + t * K * (int64_t)sizeof(CT) : nullptr;
+  }
+  __device__ const char* w_row(int, int r, const float** scrow) const {
+    const NSeg& s = seg[si];
+    const int64_t wes = s.f8 ? 1 : sizeof(CT);
+    const char* base = s.w;
+    const float* sb = s.sc;
+    int u;
+    if (s.kind == EPI_GLU) {
+      const int m = r & 63;
+      u = f0 + (r >> 6) * 32 + (m & 31);
+      if (m >= 32) { base = s.w2; sb = s.sc2; }
+    } else {
+      u = f0 + r;
+    }
+    if (u >= s.rows) return nullptr;
+    if (s.f8) *scrow = sb + (int64_t)(u >> 7) * (K >> 7);
+    return base + (int64_t)u * K * wes;
+  }
+  template <class Acc>
+  __device__ void epilogue(const Acc& acc, int wf0, int wt0, int lane) const;
+};
+
+// ---------------------------------------------------------------------------
+// Problem: up-projection + shared-expert down-projection, one GEMM with the K
+// ranges concatenated: y = [n | hs] . [W_up | W_so[0] | ... ]^T (+ addend).
+// ---------------------------------------------------------------------------
+struct KSeg {
+  const char* x;      // activations of this K range, rows of ldx elements
+  int64_t ldx;
+  const char* w;      // weights [N, K_seg], rows of ldw elements
+  int64_t ldw;
+  const float* sc;    // e4m3 scales [N/128, ldw/128]
+  int nkt;            // k-tiles in this range
+  int f8;
+};
+
+template <class Cfg, typename CT>
+struct UpProb {
+  int64_t T;
+  int N;              // H
+  int nks, nft, ntt, padded;
+  char* y;
+  const char* addend; // [T, N] act dtype, or null (identity up-projection adds n)
+  int vec;
+  KSeg ks[9];
+  int tt, ft;
+
+  __device__ bool setup(int bid) {
+    if (bid >= padded) return false;
+    const int lg = xcd_remap(bid, padded);
+    if (lg >= ntt * nft) return false;
+    const int grp = lg / (8 * nft);
+    const int gsz = min(8, ntt - grp * 8);
+    const int within = lg - grp * 8 * nft;
+    ft = within / gsz;
+    tt = grp * 8 + within % gsz;
+    return true;
+  }
+  __device__ int num_ksegs() const { return nks; }
+  __device__ int seg_ktiles(int s) const { return ks[s].nkt; }
+  __device__ bool seg_f8(int s) const { return ks[s].f8; }
+  __device__ int tokens_valid() const { return (int)imin64(Cfg::BT, T - (int64_t)tt * Cfg::BT); }
+  __device__ int feats_valid() const { return min(Cfg::BF, N - ft * Cfg::BF); }
+  __device__ const char* x_row(int s, int r) const {
+    const int64_t t = (int64_t)tt * Cfg::BT + r;
+    return t < T ? ks[s].x + t * ks[s].ldx * (int64_t)sizeof(CT) : nullptr;
+  }
+  __device__ const char* w_row(int s, int r, const float** scrow) const {
+    const int f = ft * Cfg::BF + r;
+    if (f >= N) return nullptr;
+    const KSeg& q = ks[s];
+    if (q.f8) {
+      *scrow = q.sc + (int64_t)(f >> 7) * (q.ldw >> 7);
+      return q.w + (int64_t)f * q.ldw;
+    }
+    return q.w + (int64_t)f * q.ldw * (int64_t)sizeof(CT);
+  }
+  template <class Acc>
+  __device__ void epilogue(const Acc& acc, int wf0, int wt0, int lane) const;
+};
+
+// ---------------------------------------------------------------------------
+// Problems over the expert tile list.  Entry q of `tiles` = {e, first tile of
+// e, tiles of e, 0}; an expert's tiles are consecutive.  Logical work index
+// -> (expert, feature tile, token tile) with the token tiles innermost, so
+// work-groups that share one weight slab run next to each other on one XCD.
+// ---------------------------------------------------------------------------
+template <class Cfg>
+struct ExpertTiles {
+  const int* offsets;
+  const int4* tiles;
+  const int* tile_count;
+  int nft;
+  int e, ft, m0, rows;
+
+  __device__ bool locate(int bid) {
+    const int R = *tile_count * nft;
+    const int per = (R + kXcds - 1) / kXcds;
+    if (bid >= per * kXcds) return false;
+    const int lg = (bid % kXcds) * per + bid / kXcds;
+    if (lg >= R) return false;
+    const int4 te = tiles[lg / nft];
+    const int local = lg - te.y * nft;
+    ft = local / te.z;
+    const int mt = local - ft * te.z;
+    e = te.x;
+    const int beg = offsets[e];
+    m0 = beg + mt * Cfg::BT;
+    rows = min(Cfg::BT, offsets[e + 1] - m0);
+    return rows > 0;
+  }
+};
+
+template <class Cfg, typename CT>
+struct ExpertGVProb {
+  ExpertTiles<Cfg> et;
+  const char* z;      // [T, ldz]
+  int64_t ldz;
+  const int* sorted;
+  const char* wg;     // [E, I, L]
+  const char* wv;
+  const float* sg;    // [E, I/128, L/128]
+  const float* sv;
+  char* act;          // [T*k, I]
+  int I, L, k, f8;
+  float cap, inv_cap;
+
+  __device__ bool setup(int bid) { return et.locate(bid); }
+  __device__ int num_ksegs() const { return 1; }
+  __device__ int seg_ktiles(int) const { return L * (int)sizeof(CT) / 128; }
+  __device__ bool seg_f8(int) const { return f8; }
+  __device__ int tokens_valid() const { return et.rows; }
+  __device__ int feats_valid() const { return Cfg::BF; }
+  __device__ const char* x_row(int, int r) const {
+    if (r >= et.rows) return nullptr;
+    const int t = sorted[et.m0 + r] / k;
+    return z + (int64_t)t * ldz * (int64_t)sizeof(CT);
+  }
+  __device__ const char* w_row(int, int r, const float** scrow) const {
+    const int m = r & 63;
+    const int u = et.ft * (Cfg::BF / 2) + (r >> 6) * 32 + (m & 31);
+    const bool val = m >= 32;
+    const int64_t wes = f8 ? 1 : sizeof(CT);
+    const int64_t off = ((int64_t)et.e * I + u) * L * wes;
+    if (f8) *scrow = (val ? sv : sg) + ((int64_t)et.e * (I >> 7) + (u >> 7)) * (L >> 7);
+    return (val ? wv : wg) + off;
+  }
+  template <class Acc>
+  __device__ void epilogue(const Acc& acc, int wf0, int wt0, int lane) const;
+};
+
+template <class Cfg, typename CT>
+struct ExpertDownProb {
+  ExpertTiles<Cfg> et;
+  const char* act;    // [T*k, I]
+  const char* wo;     // [E, L, I]
+  const float* so;    // [E, L/128, I/128]
+  char* out;          // [T*k, L]
+  int I, L, f8;
+
+  __device__ bool setup(int bid) { return et.locate(bid); }
+  __device__ int num_ksegs() const { return 1; }
+  __device__ int seg_ktiles(int) const { return I * (int)sizeof(CT) / 128; }
+  __device__ bool seg_f8(int) const { return f8; }
+  __device__ int tokens_valid() const { return et.rows; }
+  __device__ int feats_valid() const { return min(Cfg::BF, L - et.ft * Cfg::BF); }
+  __device__ const char* x_row(int, int r) const {
+    if (r >= et.rows) return nullptr;
+    return act + (int64_t)(et.m0 + r) * I * (int64_t)sizeof(CT);
+  }
+  __device__ const char* w_row(int, int r, const float** scrow) const {
+    const int f = et.ft * Cfg::BF + r;
+    if (f >= L) return nullptr;
+    const int64_t wes = f8 ? 1 : sizeof(CT);
+    if (f8) *scrow = so + ((int64_t)et.e * (L >> 7) + (f >> 7)) * (I >> 7);
+    return wo + ((int64_t)et.e * L + f) * I * wes;
+  }
+  template <class Acc>
+  __device__ void epilogue(const Acc& acc, int wf0, int wt0, int lane) const;
+};
+
+// ---------------------------------------------------------------------------
+// The mainloop.
+// ---------------------------------------------------------------------------
+template <typename CT>
+struct Frag;
+template <>
+struct Frag<bf16> {
+  typedef bf16x8 type;  // 8 consecutive K values of one row
+  static constexpr int KPM = 16;
+  static constexpr int EPL = 8;
+};
+template <>
+struct Frag<float> {
+  typedef float type;
+  static constexpr int KPM = 2;
+  static constexpr int EPL = 1;
+};
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// 8 e4m3 codes -> 8 bf16 of code * scale.
+__device__ __forceinline__ uint4 widen_e4m3(uint2 q, float s) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, true);
+  bf16x8 o = {(bf16)(a.x * s), (bf16)(a.y * s), (bf16)(b.x * s), (bf16)(b.y * s),
+              (bf16)(c.x * s), (bf16)(c.y * s), (bf16)(d.x * s), (bf16)(d.y * s)};
+  return *reinterpret_cast<uint4*>(&o);
+}
+
+template <class Cfg, typename CT, class Prob>
+__global__ __launch_bounds__(Cfg::NT) void gemm_kernel(Prob prob) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  Prob p = prob;
+  if (!p.setup(blockIdx.x)) return;
+
+  constexpr int NT = Cfg::NT, FI = Cfg::FI, TI = Cfg::TI, CW = Cfg::CW, CX = Cfg::CX;
+  constexpr int ES = sizeof(CT);
+  constexpr int BK = 128 / ES;
+  constexpr int KPM = Frag<CT>::KPM, EPL = Frag<CT>::EPL;
+  typedef typename Frag<CT>::type FT;
+
+  char* const sW0 = smem;
+  char* const sX0 = smem + 2 * Cfg::BF * kPitch;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wf0 = (wid % Cfg::WF) * Cfg::FW;
+  const int wt0 = (wid / Cfg::WF) * Cfg::TW;
+
+  const int tvalid = p.tokens_valid();
+  const int fvalid = p.feats_valid();
+  bool tok[TI], fea[FI];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) tok[i] = wt0 + i * 32 < tvalid;
+#pragma unroll
+  for (int i = 0; i < FI; ++i) fea[i] = wf0 + i * 32 < fvalid;
+
+  f32x16 acc[FI][TI];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < TI; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nks = p.num_ksegs();
+  for (int s = 0; s < nks; ++s) {
+    const int nkt = p.seg_ktiles(s);
+    if (nkt <= 0) continue;
+    const bool f8 = (ES == 2) && p.seg_f8(s);
+
+    const char* wp[CW];
+    const float* wsc[CW];
+    const char* xp[CX];
+#pragma unroll
+    for (int i = 0; i < CW; ++i) {
+      const int c = tid + i * NT;
+      wsc[i] = nullptr;
+      const char* rp = p.w_row(s, c >> 3, &wsc[i]);
+      wp[i] = rp ? rp + (c & 7) * (f8 ? 8 : 16) : nullptr;
+    }
+#pragma unroll
+    for (int i = 0; i < CX; ++i) {
+      const int c = tid + i * NT;
+      const char* rp = p.x_row(s, c >> 3);
+      xp[i] = rp ? rp + (c & 7) * 16 : nullptr;
+    }
+
+    uint4 wr[CW], xr[CX];
+    float sc[CW];
+    auto gload = [&](int kt) {
+#pragma unroll
+      for (int i = 0; i < CW; ++i) {
+        if (wp[i]) {
+          if (f8) {
+            const uint2 q = *reinterpret_cast<const uint2*>(wp[i] + (int64_t)kt * 64);
+            wr[i] = uint4{q.x, q.y, 0u, 0u};
+            sc[i] = wsc[i][kt >> 1];
+          } else {
+            wr[i] = *reinterpret_cast<const uint4*>(wp[i] + (int64_t)kt * 128);
+          }
+        } else {
+          wr[i] = uint4{0u, 0u, 0u, 0u};
+          sc[i] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < CX; ++i)
+        xr[i] = xp[i] ? *reinterpret_cast<const uint4*>(xp[i] + (int64_t)kt * 128) : uint4{0u, 0u, 0u, 0u};
+    };
+    auto lstore = [&](int buf) {
+      char* sW = sW0 + buf * Cfg::BF * kPitch;
+      char* sX = sX0 + buf * Cfg::BT * kPitch;
+#pragma unroll
+      for (int i = 0; i < CW; ++i) {
+        const int c = tid + i * NT;
+        uint4 v = wr[i];
+        if constexpr (ES == 2) {
+          if (f8) v = widen_e4m3(uint2{wr[i].x, wr[i].y}, sc[i]);
+        }
+        *reinterpret_cast<uint4*>(sW + (c >> 3) * kPitch + (c & 7) * 16) = v;
+      }
+#pragma unroll
+      for (int i = 0; i < CX; ++i) {
+        const int c = tid + i * NT;
+        *reinterpret_cast<uint4*>(sX + (c >> 3) * kPitch + (c & 7) * 16) = xr[i];
+      }
+    };
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nkt) gload(kt + 1);
+      const char* sW = sW0 + cur * Cfg::BF * kPitch;
+      const char* sX = sX0 + cur * Cfg::BT * kPitch;
+#pragma unroll
+      for (int ks = 0; ks < BK / KPM; ++ks) {
+        const int kb = (ks * KPM + (lane >> 5) * EPL) * ES;
+        FT a[FI], b[TI];
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+          a[i] = *reinterpret_cast<const FT*>(sW + (wf0 + i * 32 + (lane & 31)) * kPitch + kb);
+#pragma unroll
+        for (int j = 0; j < TI; ++j)
+          b[j] = *reinterpret_cast<const FT*>(sX + (wt0 + j * 32 + (lane & 31)) * kPitch + kb);
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+          for (int j = 0; j < TI; ++j)
+            if (fea[i] && tok[j]) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+      }
+      if (kt + 1 < nkt) lstore(cur ^ 1);
+      __syncthreads();
+    }
+  }
+  p.epilogue(acc, wf0, wt0, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Epilogues.  Accumulator element r of lane l in MFMA block (i, j) holds
+// feature wf0 + 32i + 8(r/4) + 4(l/32) + r%4 of token wt0 + 32j + l%32.
+// ---------------------------------------------------------------------------
+template <class Cfg, class F>
+__device__ __forceinline__ void for_acc(int wf0, int wt0, int lane, F&& f) {
+#pragma unroll
+  for (int i = 0; i < Cfg::FI; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TI; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) f(i, j, g, wf0 + i * 32 + g * 8 + (lane >> 5) * 4, wt0 + j * 32 + (lane & 31));
+}
+
+// GLU pairs: blocks (2q, 2q+1) hold gate and value of the same 32 units.
+template <class Cfg, class F>
+__device__ __forceinline__ void for_glu(int wf0, int wt0, int lane, F&& f) {
+#pragma unroll
+  for (int i = 0; i < Cfg::FI; i += 2)
+#pragma unroll
+    for (int j = 0; j < Cfg::TI; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        f(i, j, g, (wf0 + i * 32) / 2 + g * 8 + (lane >> 5) * 4, wt0 + j * 32 + (lane & 31));
+}
+
+template <class Cfg, typename CT>
+template <class Acc>
+__device__ void DenseXProb<Cfg, CT>::epilogue(const Acc& acc, int wf0, int wt0, int lane) const {
+  const NSeg& s = seg[si];
+  const int tv = tokens_valid();
+  if (s.kind == EPI_GLU) {
+    for_glu<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int ul, int tl) {
+      if (tl < tv) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = situ_glu(acc[i][j][4 * g + r], acc[i + 1][j][4 * g + r], cap, inv_cap);
+        const int64_t t = (int64_t)tt * Cfg::BT + tl;
+        CT* row = reinterpret_cast<CT*>(s.out) + t * s.ldo + s.col0;
+        store4<CT>(row, f0 + ul, v, s.rows, s.vec);
+      }
+    });
+  } else {
+    for_acc<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int fl, int tl) {
+      if (tl < tv) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r];
+        const int64_t t = (int64_t)tt * Cfg::BT + tl;
+        if (s.kind == EPI_F32) {
+          float* row = reinterpret_cast<float*>(s.out) + t * s.ldo + s.col0;
+          store4<float>(row, f0 + fl, v, s.rows, s.vec);
+        } else {
+          CT* row = reinterpret_cast<CT*>(s.out) + t * s.ldo + s.col0;
+          store4<CT>(row, f0 + fl, v, s.rows, s.vec);
+        }
+      }
+    });
+  }
+}
+
+template <class Cfg, typename CT>
+template <class Acc>
+__device__ void UpProb<Cfg, CT>::epilogue(const Acc& acc, int wf0, int wt0, int lane) const {
+  const int tv = tokens_valid();
+  for_acc<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int fl, int tl) {
+    const int f = ft * Cfg::BF + fl;
+    if (tl < tv && f < N) {
+      const int64_t t = (int64_t)tt * Cfg::BT + tl;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r];
+      if (addend) {
+        const CT* ar = reinterpret_cast<const CT*>(addend) + t * N;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (f + r < N) v[r] += to_f32(ar[f + r]);
+      }
+      store4<CT>(reinterpret_cast<CT*>(y) + t * N, f, v, N, vec);
+    }
+  });
+}
+
+template <class Cfg, typename CT>
+template <class Acc>
+__device__ void ExpertGVProb<Cfg, CT>::epilogue(const Acc& acc, int wf0, int wt0, int lane) const {
+  for_glu<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int ul, int tl) {
+    if (tl < et.rows) {
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = situ_glu(acc[i][j][4 * g + r], acc[i + 1][j][4 * g + r], cap, inv_cap);
+      CT* row = reinterpret_cast<CT*>(act) + (int64_t)(et.m0 + tl) * I;
+      store4<CT>(row, et.ft * (Cfg::BF / 2) + ul, v, I, true);
+    }
+  });
+}
+
+template <class Cfg, typename CT>
+template <class Acc>
+__device__ void ExpertDownProb<Cfg, CT>::epilogue(const Acc& acc, int wf0, int wt0, int lane) const {
+  for_acc<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int fl, int tl) {
+    if (tl < et.rows) {
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r];
+      CT* row = reinterpret_cast<CT*>(out) + (int64_t)(et.m0 + tl) * L;
+      store4<CT>(row, et.ft * Cfg::BF + fl, v, L, true);
+    }
+  });
+}
+
+}  // namespace lmoe

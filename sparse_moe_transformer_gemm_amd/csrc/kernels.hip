@@ -1,0 +1,287 @@
+// Router top-k, counting-sort permute, expert tile list and combine + RMSNorm.
+//
+// Sources: P1 aitrending.vip "The 2.8-Trillion-Parameter Problem", Technical
+// Details (router keeps 16 of 896 experts; RMSNorm before the up-projection);
+// P2 wpnews.pro, same title, MoE, Stable LatentMoE and stabilizer passages
+// (selected experts' outputs are combined, then normalised, then projected
+// back); P3 daily-ai-frontier "苏神复盘 Kimi K3", Merged summary (norm after
+// expert aggregation).
+#include <float.h>
+#include <limits.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lmoe {
+
+// ---------------------------------------------------------------------------
+// Top-k: one wavefront per token.  Lane l holds experts l, l+64, ...; each of
+// the k rounds takes the lane-local best (largest s + b, lower index on equal
+// values), reduces it across the wave with the same order, and retires the
+// winner.  All selection state stays in registers.
+// ---------------------------------------------------------------------------
+template <int NPL>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
+                                                   int64_t T, int E, int k, int32_t* __restrict__ idx,
+                                                   float* __restrict__ wout) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + t * E;
+  float key[NPL], sc[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      const float s = 1.f / (1.f + expf(-row[e]));
+      float v = s + bias[e];
+      // NaN and -inf rank below every real expert but above padding / retired ones.
+      v = (v == v) ? fmaxf(v, -FLT_MAX) : -FLT_MAX;
+      key[i] = v;
+      sc[i] = s;
+    } else {
+      key[i] = -INFINITY;
+      sc[i] = 0.f;
+    }
+  }
+  int my_e = 0;
+  float my_s = 0.f, ssum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY, bs = 0.f;
+    int be = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (key[i] > bv) { bv = key[i]; be = lane + 64 * i; bs = sc[i]; }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oe = __shfl_xor(be, o);
+      const float os = __shfl_xor(bs, o);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; bs = os; }
+    }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (lane + 64 * i == be) key[i] = -INFINITY;
+    if (lane == j) { my_e = be; my_s = bs; }
+    ssum += bs;
+  }
+  if (lane < k) {
+    idx[t * k + lane] = my_e;
+    wout[t * k + lane] = my_s / ssum;
+  }
+}
+
+hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int k, int32_t* idx,
+                       float* w, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  const int npl = (E + 63) / 64;
+  if (npl <= 1) hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, st, logits, bias, T, E, k, idx, w);
+  else if (npl <= 2) hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, st, logits, bias, T, E, k, idx, w);
+  else if (npl <= 4) hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, st, logits, bias, T, E, k, idx, w);
+  else if (npl <= 8) hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, st, logits, bias, T, E, k, idx, w);
+  else hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, st, logits, bias, T, E, k, idx, w);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Permute: stable counting sort of the T*k assignments by expert.  A
+// work-group covers 256 tokens (one per thread, 4 waves) and marks, per expert,
+// the tokens that chose it in a 256-bit LDS mask (4 x 64 bits, one word per
+// wave).  The mask's population gives the group's count per expert; the
+// population of the lower bits gives a token's rank inside the group.  Group
+// counts are scanned across groups per expert (in token order, so the sort is
+// stable), then across experts for the offsets.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void perm_mark(const int32_t* __restrict__ idx, int64_t T, int E, int k,
+                                          unsigned long long* mask, uint64_t* dup) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * 4; i += kPermTokens) mask[i] = 0ull;
+  __syncthreads();
+  const int64_t t = (int64_t)blockIdx.x * kPermTokens + tid;
+  const unsigned long long bit = 1ull << (tid & 63);
+  const int w = tid >> 6;
+  uint64_t d = 0;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if (e < 0 || e >= E) { d |= 1ull << j; continue; }
+      const unsigned long long old = atomicOr(&mask[e * 4 + w], bit);
+      if (old & bit) d |= 1ull << j;  // repeat of an expert already listed for this token
+    }
+  }
+  *dup = d;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kPermTokens) void perm_count_kernel(const int32_t* __restrict__ idx, int64_t T, int E,
+                                                                 int k, int32_t* __restrict__ bcounts) {
+  extern __shared__ unsigned long long mask[];
+  uint64_t dup;
+  perm_mark(idx, T, E, k, mask, &dup);
+  for (int e = threadIdx.x; e < E; e += kPermTokens)
+    bcounts[(int64_t)blockIdx.x * E + e] = __popcll(mask[e * 4]) + __popcll(mask[e * 4 + 1]) +
+                                           __popcll(mask[e * 4 + 2]) + __popcll(mask[e * 4 + 3]);
+}
+
+// One work-group: per expert, exclusive scan of the group counts in place;
+// then exclusive scan of the expert totals into offsets.
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ bcounts, int nb, int E,
+                                                         int32_t* __restrict__ offsets) {
+  __shared__ int lds[1024 / 64 + 1];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) {
+      const int c = bcounts[(int64_t)b * E + e];
+      bcounts[(int64_t)b * E + e] = run;
+      run += c;
+    }
+  }
+  int total;
+  const int ex = block_exclusive_scan<1024>(e < E ? run : 0, lds, &total);
+  if (e < E) offsets[e] = ex;
+  if (e == 0) offsets[E] = total;
+}
+
+__global__ __launch_bounds__(kPermTokens) void perm_scatter_kernel(const int32_t* __restrict__ idx, int64_t T, int E,
+                                                                   int k, const int32_t* __restrict__ bprefix,
+                                                                   const int32_t* __restrict__ offsets,
+                                                                   int32_t* __restrict__ sorted,
+                                                                   int32_t* __restrict__ pos) {
+  extern __shared__ unsigned long long mask[];
+  uint64_t dup;
+  perm_mark(idx, T, E, k, mask, &dup);
+  const int tid = threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * kPermTokens + tid;
+  if (t >= T) return;
+  const int w = tid >> 6;
+  const unsigned long long below = (1ull << (tid & 63)) - 1ull;
+  for (int j = 0; j < k; ++j) {
+    const int64_t a = t * k + j;
+    if (dup >> j & 1ull) { pos[a] = -1; continue; }
+    const int e = idx[a];
+    int rank = __popcll(mask[e * 4 + w] & below);
+    for (int q = 0; q < w; ++q) rank += __popcll(mask[e * 4 + q]);
+    const int dst = offsets[e] + bprefix[(int64_t)blockIdx.x * E + e] + rank;
+    sorted[dst] = (int32_t)a;
+    pos[a] = dst;
+  }
+}
+
+hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int32_t* bcounts, int32_t* offsets,
+                          int32_t* sorted, int32_t* pos, hipStream_t st) {
+  const int nb = (int)((T + kPermTokens - 1) / kPermTokens);
+  const size_t lds = (size_t)E * 4 * sizeof(unsigned long long);
+  if (nb > 0) {
+    hipLaunchKernelGGL(perm_count_kernel, dim3(nb), dim3(kPermTokens), lds, st, idx, T, E, k, bcounts);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, bcounts, nb, E, offsets);
+  if (hipError_t e = hipGetLastError()) return e;
+  if (nb > 0)
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(kPermTokens), lds, st, idx, T, E, k, bcounts, offsets,
+                       sorted, pos);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Tile list: expert e with c_e rows gets ceil(c_e / bt) token tiles; entry q
+// = {e, first tile of e, tiles of e, 0}.  One work-group, one expert a thread.
+// ---------------------------------------------------------------------------
+__device__ void write_tiles(int e, int E, int c, int bt, int4* tiles, int32_t* cnt, int* lds) {
+  const int nt = (e < E) ? (c + bt - 1) / bt : 0;
+  int total;
+  const int tb = block_exclusive_scan<1024>(nt, lds, &total);
+  for (int q = 0; q < nt; ++q) tiles[tb + q] = int4{e, tb, nt, 0};
+  if (threadIdx.x == 0) *cnt = total;
+}
+
+__global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__ offsets, int E, int bt_a,
+                                                     int4* tiles_a, int32_t* cnt_a, int bt_b, int4* tiles_b,
+                                                     int32_t* cnt_b) {
+  __shared__ int lds[1024 / 64 + 1];
+  const int e = threadIdx.x;
+  const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+  write_tiles(e, E, c, bt_a, tiles_a, cnt_a, lds);
+  if (bt_b > 0) write_tiles(e, E, c, bt_b, tiles_b, cnt_b, lds);
+}
+
+hipError_t launch_tiles(const int32_t* offsets, int E, int bt_a, int4* tiles_a, int32_t* cnt_a, int bt_b,
+                        int4* tiles_b, int32_t* cnt_b, hipStream_t st) {
+  hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(1024), 0, st, offsets, E, bt_a, tiles_a, cnt_a, bt_b, tiles_b,
+                     cnt_b);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Combine + RMSNorm: one work-group per token.  Thread c accumulates 16-byte
+// chunks c, c+256, ... of the token's k expert rows (slot order j ascending)
+// in fp32, the block reduces the sum of squares, and the normalised row is
+// written in the activation dtype.
+// ---------------------------------------------------------------------------
+template <typename CT, int MAXC>
+__global__ __launch_bounds__(256) void combine_norm_kernel(const CT* __restrict__ O, const int32_t* __restrict__ pos,
+                                                           const float* __restrict__ w,
+                                                           const float* __restrict__ gamma, int L, int k, float eps,
+                                                           CT* __restrict__ out) {
+  constexpr int EPC = 16 / sizeof(CT);
+  typedef CT vec_t __attribute__((ext_vector_type(EPC)));
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nch = L / EPC;
+  float acc[MAXC][EPC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c)
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) acc[c][i] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int p = pos[t * k + j];
+    if (p < 0) continue;
+    const float wj = w[t * k + j];
+    const CT* row = O + (int64_t)p * L;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int ch = tid + c * 256;
+      if (ch < nch) {
+        const vec_t v = *reinterpret_cast<const vec_t*>(row + ch * EPC);
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) acc[c][i] += wj * to_f32(v[i]);
+      }
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c)
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) ss += acc[c][i] * acc[c][i];
+  ss = wave_sum_f(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float inv = 1.f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)L + eps);
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int ch = tid + c * 256;
+    if (ch < nch) {
+      vec_t o;
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) o[i] = from_f32<CT>(gamma[ch * EPC + i] * acc[c][i] * inv);
+      *reinterpret_cast<vec_t*>(out + t * L + ch * EPC) = o;
+    }
+  }
+}
+
+hipError_t launch_combine_norm(bool bf16_act, const void* O, const int32_t* pos, const float* w, const float* gamma,
+                               int64_t T, int L, int k, float eps, void* n, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (bf16_act)
+    hipLaunchKernelGGL((combine_norm_kernel<bf16, 4>), dim3((unsigned)T), dim3(256), 0, st, (const bf16*)O, pos, w,
+                       gamma, L, k, eps, (bf16*)n);
+  else
+    hipLaunchKernelGGL((combine_norm_kernel<float, 8>), dim3((unsigned)T), dim3(256), 0, st, (const float*)O, pos, w,
+                       gamma, L, k, eps, (float*)n);
+  return hipGetLastError();
+}
+
+}  // namespace lmoe

@@ -1,0 +1,25 @@
+// Launchers of the non-GEMM kernels (top-k, permute, tile list, combine+norm).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lmoe {
+
+// Tokens handled by one permute work-group (one per thread).
+constexpr int kPermTokens = 256;
+
+hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int k, int32_t* idx,
+                       float* w, hipStream_t st);
+
+hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int32_t* bcounts, int32_t* offsets,
+                          int32_t* sorted, int32_t* pos, hipStream_t st);
+
+// Tile lists of the expert GEMMs for token-tile heights bt_a and bt_b (0: skip b).
+hipError_t launch_tiles(const int32_t* offsets, int E, int bt_a, int4* tiles_a, int32_t* cnt_a, int bt_b,
+                        int4* tiles_b, int32_t* cnt_b, hipStream_t st);
+
+hipError_t launch_combine_norm(bool bf16, const void* O, const int32_t* pos, const float* w, const float* gamma,
+                               int64_t T, int L, int k, float eps, void* n, hipStream_t st);
+
+}  // namespace lmoe

@@ -1,0 +1,546 @@
+// C ABI of the Stable Latent MoE layer: argument checks, workspace plan and
+// the launch sequence of each entry point (declarations and contracts in
+// include/lmoe.h).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <mutex>
+
+#include "gemm.hpp"
+#include "kernels.hpp"
+#include "lmoe.h"
+
+namespace lmoe {
+namespace {
+
+thread_local char g_err[512] = "";
+
+lmoe_status fail(lmoe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+lmoe_status hip_fail(hipError_t e, const char* what) {
+  return fail(LMOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define LMOE_HIP(call, what)                        \
+  do {                                              \
+    hipError_t e_ = (call);                         \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------------------
+// Shape checks (host only).
+// ---------------------------------------------------------------------------
+lmoe_status check_shape(const lmoe_shape* sh) {
+  if (!sh) return fail(LMOE_EINVAL, "shape is NULL");
+  if (sh->T < 0) return fail(LMOE_EINVAL, "T = %lld < 0", (long long)sh->T);
+  if (sh->H <= 0 || sh->L <= 0 || sh->E <= 0 || sh->k <= 0 || sh->I <= 0 || sh->S < 0)
+    return fail(LMOE_EINVAL, "H, L, E, k, I must be > 0 and S >= 0");
+  if (sh->S > 0 && sh->Is <= 0) return fail(LMOE_EINVAL, "Is must be > 0 when S > 0");
+  if (sh->k > sh->E) return fail(LMOE_EINVAL, "k = %d > E = %d", sh->k, sh->E);
+  if (!(sh->cap > 0.f)) return fail(LMOE_EINVAL, "cap must be > 0 (inf disables it)");
+  if (!(sh->rms_eps >= 0.f) || isinf(sh->rms_eps)) return fail(LMOE_EINVAL, "rms_eps must be finite and >= 0");
+  if (sh->act != LMOE_F32 && sh->act != LMOE_BF16)
+    return fail(sh->act == LMOE_F8E4M3 ? LMOE_EUNSUPPORTED : LMOE_EINVAL, "act dtype %d not supported", sh->act);
+  if (sh->w_expert < LMOE_F32 || sh->w_expert > LMOE_F8E4M3)
+    return fail(LMOE_EINVAL, "w_expert dtype %d unknown", sh->w_expert);
+  if (sh->act == LMOE_F32 && sh->w_expert != LMOE_F32)
+    return fail(LMOE_EUNSUPPORTED, "an F32 layer needs F32 expert weights");
+  if (sh->act == LMOE_BF16 && sh->w_expert == LMOE_F32)
+    return fail(LMOE_EUNSUPPORTED, "a BF16 layer takes BF16 or F8E4M3 expert weights");
+  const int al = sh->w_expert == LMOE_F8E4M3 ? 128 : 64;
+  if (sh->H % al || sh->L % al || sh->I % al || (sh->S > 0 && sh->Is % al))
+    return fail(LMOE_EUNSUPPORTED, "H, L, I, Is must be multiples of %d", al);
+  if (sh->L > 8192) return fail(LMOE_EUNSUPPORTED, "L = %d > 8192", sh->L);
+  if (sh->E > 1024) return fail(LMOE_EUNSUPPORTED, "E = %d > 1024", sh->E);
+  if (sh->k > 64) return fail(LMOE_EUNSUPPORTED, "k = %d > 64", sh->k);
+  if (sh->S > 8) return fail(LMOE_EUNSUPPORTED, "S = %d > 8", sh->S);
+  if (sh->T * (int64_t)sh->k >= (int64_t(1) << 31)) return fail(LMOE_EUNSUPPORTED, "T*k must be < 2^31");
+  if (sh->T >= (int64_t(1) << 31)) return fail(LMOE_EUNSUPPORTED, "T must be < 2^31");
+  return LMOE_OK;
+}
+
+bool is_f8(const lmoe_shape* sh) { return sh->w_expert == LMOE_F8E4M3; }
+
+// Which weights an entry point reads.
+enum : unsigned { NEED_ROUTE = 1, NEED_EXPERT = 2, NEED_UP = 4, NEED_NORM = 8 };
+
+lmoe_status check_weights(const lmoe_shape* sh, const lmoe_weights* w, unsigned need) {
+  if (!w) return fail(LMOE_EINVAL, "weights is NULL");
+  const bool f8 = is_f8(sh);
+  if (need & NEED_ROUTE) {
+    if (!w->w_router || !w->b_router) return fail(LMOE_EINVAL, "w_router and b_router are required");
+    if (!w->w_down && sh->L != sh->H) return fail(LMOE_EINVAL, "w_down = NULL needs L == H");
+  }
+  if (need & NEED_EXPERT) {
+    if (!w->w_gate || !w->w_value || !w->w_out) return fail(LMOE_EINVAL, "expert weights are required");
+    if (f8 && (!w->s_gate || !w->s_value || !w->s_out)) return fail(LMOE_EINVAL, "e4m3 expert scales are required");
+  }
+  if (need & NEED_NORM) {
+    if (!w->gamma) return fail(LMOE_EINVAL, "gamma is required");
+  }
+  if (need & NEED_UP) {
+    if (!w->w_up && sh->L != sh->H) return fail(LMOE_EINVAL, "w_up = NULL needs L == H");
+    if (sh->S > 0) {
+      if (!w->ws_gate || !w->ws_value || !w->ws_out) return fail(LMOE_EINVAL, "shared expert weights are required");
+      if (f8 && (!w->ss_gate || !w->ss_value || !w->ss_out))
+        return fail(LMOE_EINVAL, "e4m3 shared expert scales are required");
+    }
+  }
+  return LMOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel choices and the workspace plan.
+// ---------------------------------------------------------------------------
+// Expert GEMMs use the small token tile when experts hold few rows on average
+// (decode, small batches), the big one otherwise; dense GEMMs switch on T.
+bool expert_small(const lmoe_shape* sh) { return sh->T * (int64_t)sh->k < 48 * (int64_t)sh->E; }
+bool dense_small(const lmoe_shape* sh) { return sh->T <= 256; }
+int expert_bt(const lmoe_shape* sh) { return expert_small(sh) ? CfgSmall::BT : CfgBig::BT; }
+
+// Upper bound of the number of token tiles over all experts.
+int64_t max_tiles(const lmoe_shape* sh, int bt) {
+  const int64_t tk = sh->T * sh->k;
+  const int64_t busy = tk < sh->E ? tk : sh->E;
+  return (tk + busy * (bt - 1)) / bt;
+}
+
+struct Plan {
+  size_t logits, z, hs, n, idx, w, bcounts, offsets, sorted, pos, tiles_a, tiles_b, tcount, act, out, total;
+};
+
+Plan plan(const lmoe_shape* sh) {
+  Plan p{};
+  const size_t es = sh->act == LMOE_BF16 ? 2 : 4;
+  const size_t T = (size_t)sh->T, tk = T * sh->k;
+  const size_t nb = (T + kPermTokens - 1) / kPermTokens;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  p.logits = take(T * sh->E * 4);
+  p.z = take(T * sh->L * es);
+  p.hs = take(T * (size_t)sh->S * (sh->S ? sh->Is : 0) * es);
+  p.n = take(T * sh->L * es);
+  p.idx = take(tk * 4);
+  p.w = take(tk * 4);
+  p.bcounts = take(nb * sh->E * 4);
+  p.offsets = take((size_t)(sh->E + 1) * 4);
+  p.sorted = take(tk * 4);
+  p.pos = take(tk * 4);
+  p.tiles_a = take((size_t)max_tiles(sh, expert_bt(sh)) * 16);
+  p.tiles_b = take(16);
+  p.tcount = take(8);
+  p.act = take(tk * sh->I * es);
+  p.out = take(tk * sh->L * es);
+  p.total = off;
+  return p;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+lmoe_status check_ws(const lmoe_shape* sh, const void* ws, size_t ws_bytes) {
+  const size_t need = plan(sh).total;
+  if (ws_bytes < need) return fail(LMOE_EWORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  if (!ws) return fail(LMOE_EINVAL, "ws is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(LMOE_EINVAL, "ws must be 256-byte aligned");
+  return LMOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// GEMM launches.
+// ---------------------------------------------------------------------------
+template <class Cfg, typename CT, class Prob>
+hipError_t launch_gemm(const Prob& p, int64_t grid, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  auto kern = gemm_kernel<Cfg, CT, Prob>;
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [&] {
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               Cfg::LDS);
+  });
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::LDS, st, p);
+  return hipGetLastError();
+}
+
+int64_t pad8(int64_t v) { return (v + kXcds - 1) / kXcds * kXcds; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Ctx {
+  const lmoe_shape* sh;
+  const lmoe_weights* w;
+  hipStream_t st;
+  size_t es() const { return sh->act == LMOE_BF16 ? 2 : 4; }
+  size_t wes() const { return sh->w_expert == LMOE_F8E4M3 ? 1 : es(); }
+  float inv_cap() const { return isinf(sh->cap) ? 0.f : 1.f / sh->cap; }
+};
+
+// x-GEMM: any of router logits (fp32 [T, E]), latent z ([T, L]) and the shared
+// experts' SiTU-GLU activations (hs [T, S*Is]) from one pass over x.
+template <class Cfg, typename CT>
+hipError_t xgemm(const Ctx& c, const void* x, float* logits, void* z, void* hs) {
+  const lmoe_shape* sh = c.sh;
+  DenseXProb<Cfg, CT> p{};
+  p.x = static_cast<const char*>(x);
+  p.T = sh->T;
+  p.K = sh->H;
+  p.cap = sh->cap;
+  p.inv_cap = c.inv_cap();
+  int ns = 0, ft = 0;
+  if (logits) {
+    NSeg& s = p.seg[ns++];
+    s = NSeg{};
+    s.w = static_cast<const char*>(c.w->w_router);
+    s.out = reinterpret_cast<char*>(logits);
+    s.ldo = sh->E;
+    s.rows = sh->E;
+    s.kind = EPI_F32;
+    s.vec = (sh->E % 4) == 0;
+    s.ft0 = ft;
+    ft += (int)cdiv(sh->E, Cfg::BF);
+  }
+  if (z) {
+    NSeg& s = p.seg[ns++];
+    s = NSeg{};
+    s.w = static_cast<const char*>(c.w->w_down);
+    s.out = static_cast<char*>(z);
+    s.ldo = sh->L;
+    s.rows = sh->L;
+    s.kind = EPI_STORE;
+    s.vec = 1;
+    s.ft0 = ft;
+    ft += (int)cdiv(sh->L, Cfg::BF);
+  }
+  if (hs) {
+    // The S shared experts' gate (value) matrices are consecutive: one GLU
+    // segment of S*Is units; hs column s*Is + i is unit i of expert s.
+    NSeg& s = p.seg[ns++];
+    s = NSeg{};
+    s.w = static_cast<const char*>(c.w->ws_gate);
+    s.w2 = static_cast<const char*>(c.w->ws_value);
+    s.sc = c.w->ss_gate;
+    s.sc2 = c.w->ss_value;
+    s.f8 = is_f8(sh);
+    s.out = static_cast<char*>(hs);
+    s.ldo = (int64_t)sh->S * sh->Is;
+    s.rows = sh->S * sh->Is;
+    s.kind = EPI_GLU;
+    s.vec = 1;
+    s.ft0 = ft;
+    ft += (int)cdiv((int64_t)sh->S * sh->Is, Cfg::BF / 2);
+  }
+  if (ns == 0 || sh->T == 0) return hipSuccess;
+  p.nseg = ns;
+  p.nft = ft;
+  p.ntt = (int)cdiv(sh->T, Cfg::BT);
+  p.padded = (int)pad8((int64_t)p.ntt * p.nft);
+  return launch_gemm<Cfg, CT>(p, p.padded, c.st);
+}
+
+// y = n . W_up^T + sum_s hs_s . W_so[s]^T  (n added directly when w_up is NULL).
+template <class Cfg, typename CT>
+hipError_t upgemm(const Ctx& c, const void* n, const void* hs, void* y) {
+  const lmoe_shape* sh = c.sh;
+  if (sh->T == 0) return hipSuccess;
+  UpProb<Cfg, CT> p{};
+  p.T = sh->T;
+  p.N = sh->H;
+  p.y = static_cast<char*>(y);
+  p.vec = 1;
+  int nk = 0;
+  if (c.w->w_up) {
+    KSeg& q = p.ks[nk++];
+    q.x = static_cast<const char*>(n);
+    q.ldx = sh->L;
+    q.w = static_cast<const char*>(c.w->w_up);
+    q.ldw = sh->L;
+    q.nkt = (int)(sh->L * c.es() / 128);
+  } else {
+    p.addend = static_cast<const char*>(n);
+  }
+  for (int s = 0; s < sh->S; ++s) {
+    KSeg& q = p.ks[nk++];
+    q.x = static_cast<const char*>(hs) + (size_t)s * sh->Is * c.es();
+    q.ldx = (int64_t)sh->S * sh->Is;
+    q.w = static_cast<const char*>(c.w->ws_out) + (size_t)s * sh->H * sh->Is * c.wes();
+    q.ldw = sh->Is;
+    q.f8 = is_f8(sh);
+    if (q.f8) q.sc = c.w->ss_out + (size_t)s * (sh->H / 128) * (sh->Is / 128);
+    q.nkt = (int)(sh->Is * c.es() / 128);
+  }
+  p.nks = nk;
+  p.nft = (int)cdiv(sh->H, Cfg::BF);
+  p.ntt = (int)cdiv(sh->T, Cfg::BT);
+  p.padded = (int)pad8((int64_t)p.ntt * p.nft);
+  return launch_gemm<Cfg, CT>(p, p.padded, c.st);
+}
+
+template <class Cfg, typename CT>
+hipError_t expert_gv(const Ctx& c, const void* z, const int32_t* offsets, const int32_t* sorted,
+                     const int4* tiles, const int32_t* tcount, void* act) {
+  const lmoe_shape* sh = c.sh;
+  ExpertGVProb<Cfg, CT> p{};
+  p.et.offsets = offsets;
+  p.et.tiles = tiles;
+  p.et.tile_count = tcount;
+  p.et.nft = (int)(sh->I / (Cfg::BF / 2));
+  p.z = static_cast<const char*>(z);
+  p.ldz = sh->L;
+  p.sorted = sorted;
+  p.wg = static_cast<const char*>(c.w->w_gate);
+  p.wv = static_cast<const char*>(c.w->w_value);
+  p.sg = c.w->s_gate;
+  p.sv = c.w->s_value;
+  p.act = static_cast<char*>(act);
+  p.I = sh->I;
+  p.L = sh->L;
+  p.k = sh->k;
+  p.f8 = is_f8(sh);
+  p.cap = sh->cap;
+  p.inv_cap = c.inv_cap();
+  return launch_gemm<Cfg, CT>(p, pad8(max_tiles(sh, Cfg::BT) * p.et.nft), c.st);
+}
+
+template <class Cfg, typename CT>
+hipError_t expert_down(const Ctx& c, const void* act, const int32_t* offsets, const int4* tiles,
+                       const int32_t* tcount, void* out) {
+  const lmoe_shape* sh = c.sh;
+  ExpertDownProb<Cfg, CT> p{};
+  p.et.offsets = offsets;
+  p.et.tiles = tiles;
+  p.et.tile_count = tcount;
+  p.et.nft = (int)cdiv(sh->L, Cfg::BF);
+  p.act = static_cast<const char*>(act);
+  p.wo = static_cast<const char*>(c.w->w_out);
+  p.so = c.w->s_out;
+  p.out = static_cast<char*>(out);
+  p.I = sh->I;
+  p.L = sh->L;
+  p.f8 = is_f8(sh);
+  return launch_gemm<Cfg, CT>(p, pad8(max_tiles(sh, Cfg::BT) * p.et.nft), c.st);
+}
+
+// Dispatch on (dense tile, activation dtype).
+template <typename CT>
+hipError_t xgemm_any(const Ctx& c, const void* x, float* logits, void* z, void* hs) {
+  return dense_small(c.sh) ? xgemm<CfgSmall, CT>(c, x, logits, z, hs) : xgemm<CfgBig, CT>(c, x, logits, z, hs);
+}
+template <typename CT>
+hipError_t upgemm_any(const Ctx& c, const void* n, const void* hs, void* y) {
+  return dense_small(c.sh) ? upgemm<CfgSmall, CT>(c, n, hs, y) : upgemm<CfgBig, CT>(c, n, hs, y);
+}
+
+// Both expert GEMMs plus the tile list they share.
+template <typename CT>
+hipError_t experts_any(const Ctx& c, const void* z, const int32_t* offsets, const int32_t* sorted, void* act,
+                       void* out, int4* tiles, int32_t* tcount) {
+  const lmoe_shape* sh = c.sh;
+  hipError_t e = launch_tiles(offsets, sh->E, expert_bt(sh), tiles, tcount, 0, nullptr, nullptr, c.st);
+  if (e != hipSuccess) return e;
+  if (expert_small(sh)) {
+    if ((e = expert_gv<CfgSmall, CT>(c, z, offsets, sorted, tiles, tcount, act)) != hipSuccess) return e;
+    return expert_down<CfgSmall, CT>(c, act, offsets, tiles, tcount, out);
+  }
+  if ((e = expert_gv<CfgBig, CT>(c, z, offsets, sorted, tiles, tcount, act)) != hipSuccess) return e;
+  return expert_down<CfgBig, CT>(c, act, offsets, tiles, tcount, out);
+}
+
+bool bf16_act(const lmoe_shape* sh) { return sh->act == LMOE_BF16; }
+
+lmoe_status record(void* const* ev, int i, hipStream_t st) {
+  if (ev && ev[i]) LMOE_HIP(hipEventRecord(static_cast<hipEvent_t>(ev[i]), st), "hipEventRecord");
+  return LMOE_OK;
+}
+
+}  // namespace
+}  // namespace lmoe
+
+using namespace lmoe;
+
+extern "C" {
+
+const char* lmoe_status_str(lmoe_status s) {
+  switch (s) {
+    case LMOE_OK: return "LMOE_OK";
+    case LMOE_EINVAL: return "LMOE_EINVAL";
+    case LMOE_EUNSUPPORTED: return "LMOE_EUNSUPPORTED";
+    case LMOE_EWORKSPACE: return "LMOE_EWORKSPACE";
+    case LMOE_EHIP: return "LMOE_EHIP";
+  }
+  return "unknown lmoe_status";
+}
+
+const char* lmoe_last_error(void) { return g_err; }
+
+size_t lmoe_workspace_bytes(const lmoe_shape* sh) {
+  if (check_shape(sh) != LMOE_OK) return 0;
+  return plan(sh).total;
+}
+
+lmoe_status lmoe_validate(const lmoe_shape* sh, const lmoe_weights* w, size_t ws_bytes) {
+  g_err[0] = 0;
+  if (lmoe_status s = check_shape(sh)) return s;
+  if (lmoe_status s = check_weights(sh, w, NEED_ROUTE | NEED_EXPERT | NEED_UP | NEED_NORM)) return s;
+  const size_t need = plan(sh).total;
+  if (ws_bytes < need) return fail(LMOE_EWORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_route(const lmoe_shape* sh, const lmoe_weights* w, const void* x, int32_t* topk_idx,
+                       float* topk_w, void* z, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (lmoe_status s = check_shape(sh)) return s;
+  if (lmoe_status s = check_weights(sh, w, NEED_ROUTE)) return s;
+  if (lmoe_status s = check_ws(sh, ws, ws_bytes)) return s;
+  if (sh->T == 0) return LMOE_OK;
+  if (!x || !topk_idx || !topk_w || (w->w_down && !z)) return fail(LMOE_EINVAL, "x, topk_idx, topk_w, z are required");
+  const Ctx c{sh, w, static_cast<hipStream_t>(stream)};
+  const Plan pl = plan(sh);
+  float* logits = at<float>(ws, pl.logits);
+  void* zz = w->w_down ? z : nullptr;
+  LMOE_HIP(bf16_act(sh) ? xgemm_any<bf16>(c, x, logits, zz, nullptr) : xgemm_any<float>(c, x, logits, zz, nullptr),
+           "router / down GEMM");
+  LMOE_HIP(launch_topk(logits, w->b_router, sh->T, sh->E, sh->k, topk_idx, topk_w, c.st), "top-k");
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_permute(const lmoe_shape* sh, const int32_t* topk_idx, int32_t* offsets, int32_t* sorted,
+                         int32_t* pos, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (lmoe_status s = check_shape(sh)) return s;
+  if (lmoe_status s = check_ws(sh, ws, ws_bytes)) return s;
+  if (!offsets) return fail(LMOE_EINVAL, "offsets is required");
+  if (sh->T > 0 && (!topk_idx || !sorted || !pos)) return fail(LMOE_EINVAL, "topk_idx, sorted, pos are required");
+  const Plan pl = plan(sh);
+  LMOE_HIP(launch_permute(topk_idx, sh->T, sh->E, sh->k, at<int32_t>(ws, pl.bcounts), offsets, sorted, pos,
+                          static_cast<hipStream_t>(stream)),
+           "permute");
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_expert_gemm(const lmoe_shape* sh, const lmoe_weights* w, const void* z, const int32_t* offsets,
+                             const int32_t* sorted, void* expert_out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (lmoe_status s = check_shape(sh)) return s;
+  if (lmoe_status s = check_weights(sh, w, NEED_EXPERT)) return s;
+  if (lmoe_status s = check_ws(sh, ws, ws_bytes)) return s;
+  if (sh->T == 0) return LMOE_OK;
+  if (!z || !offsets || !sorted || !expert_out) return fail(LMOE_EINVAL, "z, offsets, sorted, expert_out are required");
+  const Ctx c{sh, w, static_cast<hipStream_t>(stream)};
+  const Plan pl = plan(sh);
+  void* act = at<void>(ws, pl.act);
+  int4* tiles = at<int4>(ws, pl.tiles_a);
+  int32_t* tc = at<int32_t>(ws, pl.tcount);
+  LMOE_HIP(bf16_act(sh) ? experts_any<bf16>(c, z, offsets, sorted, act, expert_out, tiles, tc)
+                        : experts_any<float>(c, z, offsets, sorted, act, expert_out, tiles, tc),
+           "expert GEMMs");
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_combine_norm(const lmoe_shape* sh, const void* expert_out, const int32_t* pos, const float* topk_w,
+                              const float* gamma, void* n, void* stream) {
+  g_err[0] = 0;
+  if (lmoe_status s = check_shape(sh)) return s;
+  if (sh->T == 0) return LMOE_OK;
+  if (!expert_out || !pos || !topk_w || !gamma || !n) return fail(LMOE_EINVAL, "null argument");
+  LMOE_HIP(launch_combine_norm(bf16_act(sh), expert_out, pos, topk_w, gamma, sh->T, sh->L, sh->k, sh->rms_eps, n,
+                               static_cast<hipStream_t>(stream)),
+           "combine + norm");
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_up(const lmoe_shape* sh, const lmoe_weights* w, const void* n, const void* x, void* y, void* ws,
+                    size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (lmoe_status s = check_shape(sh)) return s;
+  if (lmoe_status s = check_weights(sh, w, NEED_UP)) return s;
+  if (lmoe_status s = check_ws(sh, ws, ws_bytes)) return s;
+  if (sh->T == 0) return LMOE_OK;
+  if (!n || !y || (sh->S > 0 && !x)) return fail(LMOE_EINVAL, "n, x, y are required");
+  const Ctx c{sh, w, static_cast<hipStream_t>(stream)};
+  void* hs = at<void>(ws, plan(sh).hs);
+  if (sh->S > 0)
+    LMOE_HIP(bf16_act(sh) ? xgemm_any<bf16>(c, x, nullptr, nullptr, hs) : xgemm_any<float>(c, x, nullptr, nullptr, hs),
+             "shared gate/value GEMM");
+  LMOE_HIP(bf16_act(sh) ? upgemm_any<bf16>(c, n, hs, y) : upgemm_any<float>(c, n, hs, y), "up GEMM");
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_forward(const lmoe_shape* sh, const lmoe_weights* w, const void* x, void* y, int32_t* topk_idx,
+                         float* topk_w, void* ws, size_t ws_bytes, void* stream, void* const* ev) {
+  g_err[0] = 0;
+  if (lmoe_status s = lmoe_validate(sh, w, ws_bytes)) return s;
+  if (lmoe_status s = check_ws(sh, ws, ws_bytes)) return s;
+  if (sh->T == 0) return LMOE_OK;
+  if (!x || !y) return fail(LMOE_EINVAL, "x and y are required");
+  const Ctx c{sh, w, static_cast<hipStream_t>(stream)};
+  const Plan pl = plan(sh);
+  const bool bf = bf16_act(sh);
+  float* logits = at<float>(ws, pl.logits);
+  void* z = w->w_down ? at<void>(ws, pl.z) : nullptr;
+  void* hs = sh->S > 0 ? at<void>(ws, pl.hs) : nullptr;
+  void* n = at<void>(ws, pl.n);
+  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, pl.idx);
+  float* tw = topk_w ? topk_w : at<float>(ws, pl.w);
+  int32_t* offsets = at<int32_t>(ws, pl.offsets);
+  int32_t* sorted = at<int32_t>(ws, pl.sorted);
+  int32_t* pos = at<int32_t>(ws, pl.pos);
+  void* act = at<void>(ws, pl.act);
+  void* out = at<void>(ws, pl.out);
+
+  if (lmoe_status s = record(ev, 0, c.st)) return s;
+  LMOE_HIP(bf ? xgemm_any<bf16>(c, x, logits, z, hs) : xgemm_any<float>(c, x, logits, z, hs), "route GEMM");
+  if (lmoe_status s = record(ev, 1, c.st)) return s;
+  LMOE_HIP(launch_topk(logits, w->b_router, sh->T, sh->E, sh->k, idx, tw, c.st), "top-k");
+  if (lmoe_status s = record(ev, 2, c.st)) return s;
+  LMOE_HIP(launch_permute(idx, sh->T, sh->E, sh->k, at<int32_t>(ws, pl.bcounts), offsets, sorted, pos, c.st),
+           "permute");
+  LMOE_HIP(launch_tiles(offsets, sh->E, expert_bt(sh), at<int4>(ws, pl.tiles_a), at<int32_t>(ws, pl.tcount), 0,
+                        nullptr, nullptr, c.st),
+           "tile list");
+  if (lmoe_status s = record(ev, 3, c.st)) return s;
+  const void* zin = z ? z : x;
+  const int4* tiles = at<int4>(ws, pl.tiles_a);
+  const int32_t* tc = at<int32_t>(ws, pl.tcount);
+  hipError_t e;
+  if (expert_small(sh))
+    e = bf ? expert_gv<CfgSmall, bf16>(c, zin, offsets, sorted, tiles, tc, act)
+           : expert_gv<CfgSmall, float>(c, zin, offsets, sorted, tiles, tc, act);
+  else
+    e = bf ? expert_gv<CfgBig, bf16>(c, zin, offsets, sorted, tiles, tc, act)
+           : expert_gv<CfgBig, float>(c, zin, offsets, sorted, tiles, tc, act);
+  LMOE_HIP(e, "expert gate/value GEMM");
+  if (lmoe_status s = record(ev, 4, c.st)) return s;
+  if (expert_small(sh))
+    e = bf ? expert_down<CfgSmall, bf16>(c, act, offsets, tiles, tc, out)
+           : expert_down<CfgSmall, float>(c, act, offsets, tiles, tc, out);
+  else
+    e = bf ? expert_down<CfgBig, bf16>(c, act, offsets, tiles, tc, out)
+           : expert_down<CfgBig, float>(c, act, offsets, tiles, tc, out);
+  LMOE_HIP(e, "expert down GEMM");
+  if (lmoe_status s = record(ev, 5, c.st)) return s;
+  LMOE_HIP(launch_combine_norm(bf, out, pos, tw, w->gamma, sh->T, sh->L, sh->k, sh->rms_eps, n, c.st),
+           "combine + norm");
+  if (lmoe_status s = record(ev, 6, c.st)) return s;
+  LMOE_HIP(bf ? upgemm_any<bf16>(c, n, hs, y) : upgemm_any<float>(c, n, hs, y), "up GEMM");
+  if (lmoe_status s = record(ev, 7, c.st)) return s;
+  return LMOE_OK;
+}
+
+}  // extern "C"

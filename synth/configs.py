@@ -58,6 +58,9 @@ _LIST = [
                 act="bf16", w_expert="f8", seed=4),
     LayerConfig("small_identity_bf16", T=130, H=256, L=256, E=12, k=3, S=1, I=128,
                 Is=128, act="bf16", w_expert="bf16", seed=5, identity_proj=True),
+    # Every expert selected (k == E) and no shared expert.
+    LayerConfig("small_full_k", T=77, H=256, L=128, E=8, k=8, S=0, I=128, Is=0,
+                act="bf16", w_expert="bf16", seed=6),
     # K3-shape layers.
     LayerConfig("k3_prefill_t2048", T=2048, act="bf16", w_expert="bf16", seed=1, **K3),
     LayerConfig("k3_t8192", T=8192, act="bf16", w_expert="bf16", seed=1, **K3),

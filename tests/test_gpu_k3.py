@@ -1,0 +1,102 @@
+"""GPU parity at the K3 layer shape (hidden 7168, latent 3584, 896 experts,
+top-16, 2 shared experts, intermediate 1024): the whole batch runs on the GPU
+in the launch configuration the benchmark times; the oracle checks the
+selection of every token and the outputs of a seeded sample of rows (each
+output row depends only on its own token)."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import lmoe_oracle as O
+from synth import get_config, make_inputs, raw_numpy
+from synth.inputs import make_router_bias, make_x
+
+from gpu_common import check_selection, lazy_inputs, note, rowwise_rel_err, spec_of, to_f64, tol_of
+
+pytestmark = pytest.mark.gpu
+
+lmoe = pytest.importorskip("sparse_moe_transformer_gemm_amd.lmoe")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available()
+    lmoe.load_library()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def k3w(dev):
+    """K3 bf16 weights (seed 1), generated on the device once for the module."""
+    note("[k3] generating bf16 weights on the device")
+    g = make_inputs(get_config("k3_t8192"), device=dev, with_x=False)
+    torch.cuda.synchronize()
+    yield g
+    g.clear()
+    torch.cuda.empty_cache()
+
+
+def _route_all(g, x, cfg):
+    """Oracle routing of every token (cheap next to the experts)."""
+    x64 = O.decode(raw_numpy(x), cfg.act)
+    return O.route(x64, O.decode(raw_numpy(g["w_router"]), cfg.act),
+                   raw_numpy(g["b_router"]).astype(np.float64), cfg.k)
+
+
+def _run(cfg, g, dev, sample=8, x=None):
+    note(f"[k3] {cfg.name}: T={cfg.T} E={cfg.E} k={cfg.k} L={cfg.L} {cfg.act}/{cfg.w_expert} bias={cfg.bias}")
+    x = make_x(cfg, dev) if x is None else x
+    sh = lmoe.shape_of(cfg)
+    w = lmoe.make_weights(sh, g)
+    y, idx, tw = lmoe.forward(sh, w, x)
+    torch.cuda.synchronize()
+    r = _route_all(g, x, cfg)
+    idx_h = idx.cpu().numpy()
+    mism, n = check_selection(idx_h, tw.cpu().numpy(), r)
+    note(f"    selection: {mism}/{n} tokens differ from the oracle (all within the near-tie rule)")
+    rows = np.sort(np.random.default_rng(cfg.T).choice(cfg.T, size=min(sample, cfg.T), replace=False))
+    inp = lazy_inputs(g, None)
+    inp["x"] = raw_numpy(x[torch.as_tensor(rows, device=dev)])
+    ref = O.forward(inp, spec_of(cfg), forced_idx=idx_h[rows].astype(np.int64), forced_tol=1e-5)
+    err = rowwise_rel_err(to_f64(y[torch.as_tensor(rows, device=dev)]), ref["y"])
+    note(f"    sampled rows {rows.tolist()}: max row rel err {err:.3e} (tol {tol_of(cfg)})")
+    assert err <= tol_of(cfg)
+    return y, idx
+
+
+def test_k3_t8192(dev, k3w):
+    _run(get_config("k3_t8192"), k3w, dev)
+
+
+def test_k3_prefill_and_decode_batch_invariant(dev, k3w):
+    cfg = get_config("k3_prefill_t2048")
+    y, idx = _run(cfg, k3w, dev, sample=6)
+    dcfg = get_config("k3_decode_t64")
+    xd = make_x(dcfg, dev)
+    assert torch.equal(xd, make_x(cfg, dev)[:64])  # the decode batch is the first 64 prefill tokens
+    yd, idd = _run(dcfg, k3w, dev, sample=6, x=xd)
+    assert torch.equal(idd, idx[:64])
+    assert torch.equal(yd, y[:64])
+
+
+def test_k3_zipf_t16384(dev, k3w):
+    cfg = get_config("k3_zipf_t16384")
+    g = dict(k3w)
+    g["b_router"] = make_router_bias(cfg, dev)
+    y, idx = _run(cfg, g, dev, sample=6)
+    counts = torch.bincount(idx.flatten().long(), minlength=cfg.E)
+    note(f"    tokens per expert: max {int(counts.max())}, min {int(counts.min())}")
+    assert int(counts.max()) == cfg.T  # the most favoured expert is in every token's top-16
+
+
+@pytest.mark.parametrize("name", ["k3_fp8_t8192", "fp8_448x8_l7168_t8192"])
+def test_fp8_layers(dev, k3w, name):
+    cfg = get_config(name)
+    note(f"[k3] generating {name} weights on the device")
+    g = make_inputs(cfg, device=dev, with_x=False)
+    try:
+        _run(cfg, g, dev, sample=6)
+    finally:
+        g.clear()
+        torch.cuda.empty_cache()
