@@ -177,6 +177,9 @@ def forward(sh: Shape, w: Weights, x, y=None, topk_idx=None, topk_w=None, ws=Non
     if events is not None:
         if len(events) != NUM_STAGES + 1:
             raise ValueError(f"events must hold {NUM_STAGES + 1} torch.cuda.Event objects")
+        for e in events:
+            if not e.cuda_event:
+                e.record()  # torch creates the HIP event on first use
         ev = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
     _check(lib.lmoe_forward(ctypes.byref(sh), ctypes.byref(w), _ptr(x, _act_dtype(sh), "x"),
                             _ptr(y, _act_dtype(sh), "y"), _ptr(topk_idx, torch.int32, "topk_idx"),
