@@ -32,6 +32,7 @@ struct TileCfg {
   static constexpr int CW = BF * 8 / NT;  // 16-byte LDS chunks per thread, W tile
   static constexpr int CX = BT * 8 / NT;  // same, X tile
   static constexpr int LDS = 2 * (BF + BT) * kPitch;
+  static constexpr bool kDma = false;
   static_assert(FW % 64 == 0, "a wave covers whole gate/value pairs");
   static_assert(TW % 32 == 0 && CW >= 1 && CX >= 1, "tile shape");
   static_assert((BF * 8) % NT == 0 && (BT * 8) % NT == 0, "chunk split");
@@ -88,11 +89,14 @@ struct DenseXProb {
   int K;              // H
   int nseg, nft, ntt, padded;
   float cap, inv_cap;
-  NSeg seg[4];
-  // per work-group
-  int tt, si, f0;     // token tile, segment, first feature (GLU: unit) of the tile
+  NSeg seg[3];
 
-  __device__ bool setup(int bid) {
+  struct State {
+    int tt, f0;       // token tile, first feature (GLU: unit) of the tile
+    NSeg s;           // its feature segment
+  };
+
+  __device__ bool setup(int bid, State& st) const {
     if (bid >= padded) return false;
     const int lg = xcd_remap(bid, padded);
     if (lg >= ntt * nft) return false;
@@ -102,46 +106,47 @@ struct DenseXProb {
     const int gsz = min(8, ntt - grp * 8);
     const int within = lg - grp * 8 * nft;
     const int ft = within / gsz;
-    tt = grp * 8 + within % gsz;
-    si = 0;
-    for (int s = 1; s < nseg; ++s)
-      if (ft >= seg[s].ft0) si = s;
-    const int per = seg[si].kind == EPI_GLU ? Cfg::BF / 2 : Cfg::BF;
-    f0 = (ft - seg[si].ft0) * per;
+    st.tt = grp * 8 + within % gsz;
+    // constant indices only: the argument block stays in kernarg memory
+    st.s = seg[0];
+    if (nseg > 1 && ft >= seg[1].ft0) st.s = seg[1];
+    if (nseg > 2 && ft >= seg[2].ft0) st.s = seg[2];
+    const int per = st.s.kind == EPI_GLU ? Cfg::BF / 2 : Cfg::BF;
+    st.f0 = (ft - st.s.ft0) * per;
     return true;
   }
   __device__ int num_ksegs() const { return 1; }
   __device__ int seg_ktiles(int) const { return K * (int)sizeof(CT) / 128; }
-  __device__ bool seg_f8(int) const { return seg[si].f8; }
-  __device__ int tokens_valid() const { return (int)imin64(Cfg::BT, T - (int64_t)tt * Cfg::BT); }
-  __device__ int feats_valid() const {
+  __device__ bool seg_f8(const State& st, int) const { return st.s.f8; }
+  __device__ int tokens_valid(const State& st) const { return (int)imin64(Cfg::BT, T - (int64_t)st.tt * Cfg::BT); }
+  __device__ int feats_valid(const State& st) const {
     // GLU tiles interleave gate/value blocks: missing units load as zeros.
-    const NSeg& s = seg[si];
-    return s.kind == EPI_GLU ? Cfg::BF : min(Cfg::BF, s.rows - f0);
+    const NSeg& s = st.s;
+    return s.kind == EPI_GLU ? Cfg::BF : min(Cfg::BF, s.rows - st.f0);
   }
-  __device__ const char* x_row(int, int r) const {
-    const int64_t t = (int64_t)tt * Cfg::BT + r;
+  __device__ const char* x_row(const State& st, int, int r) const {
+    const int64_t t = (int64_t)st.tt * Cfg::BT + r;
     return t < T ? x + t * K * (int64_t)sizeof(CT) : nullptr;
   }
-  __device__ const char* w_row(int, int r, const float** scrow) const {
-    const NSeg& s = seg[si];
+  __device__ const char* w_row(const State& st, int, int r, const float** scrow) const {
+    const NSeg& s = st.s;
     const int64_t wes = s.f8 ? 1 : sizeof(CT);
     const char* base = s.w;
     const float* sb = s.sc;
     int u;
     if (s.kind == EPI_GLU) {
       const int m = r & 63;
-      u = f0 + (r >> 6) * 32 + (m & 31);
+      u = st.f0 + (r >> 6) * 32 + (m & 31);
       if (m >= 32) { base = s.w2; sb = s.sc2; }
     } else {
-      u = f0 + r;
+      u = st.f0 + r;
     }
     if (u >= s.rows) return nullptr;
     if (s.f8) *scrow = sb + (int64_t)(u >> 7) * (K >> 7);
     return base + (int64_t)u * K * wes;
   }
   template <class Acc>
-  __device__ void epilogue(const Acc& acc, int wf0, int wt0, int lane) const;
+  __device__ __forceinline__ void epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const;
 };
 
 // ---------------------------------------------------------------------------
@@ -167,30 +172,33 @@ struct UpProb {
   const char* addend; // [T, N] act dtype, or null (identity up-projection adds n)
   int vec;
   KSeg ks[9];
-  int tt, ft;
 
-  __device__ bool setup(int bid) {
+  struct State {
+    int tt, ft;
+  };
+
+  __device__ bool setup(int bid, State& st) const {
     if (bid >= padded) return false;
     const int lg = xcd_remap(bid, padded);
     if (lg >= ntt * nft) return false;
     const int grp = lg / (8 * nft);
     const int gsz = min(8, ntt - grp * 8);
     const int within = lg - grp * 8 * nft;
-    ft = within / gsz;
-    tt = grp * 8 + within % gsz;
+    st.ft = within / gsz;
+    st.tt = grp * 8 + within % gsz;
     return true;
   }
   __device__ int num_ksegs() const { return nks; }
   __device__ int seg_ktiles(int s) const { return ks[s].nkt; }
-  __device__ bool seg_f8(int s) const { return ks[s].f8; }
-  __device__ int tokens_valid() const { return (int)imin64(Cfg::BT, T - (int64_t)tt * Cfg::BT); }
-  __device__ int feats_valid() const { return min(Cfg::BF, N - ft * Cfg::BF); }
-  __device__ const char* x_row(int s, int r) const {
-    const int64_t t = (int64_t)tt * Cfg::BT + r;
+  __device__ bool seg_f8(const State&, int s) const { return ks[s].f8; }
+  __device__ int tokens_valid(const State& st) const { return (int)imin64(Cfg::BT, T - (int64_t)st.tt * Cfg::BT); }
+  __device__ int feats_valid(const State& st) const { return min(Cfg::BF, N - st.ft * Cfg::BF); }
+  __device__ const char* x_row(const State& st, int s, int r) const {
+    const int64_t t = (int64_t)st.tt * Cfg::BT + r;
     return t < T ? ks[s].x + t * ks[s].ldx * (int64_t)sizeof(CT) : nullptr;
   }
-  __device__ const char* w_row(int s, int r, const float** scrow) const {
-    const int f = ft * Cfg::BF + r;
+  __device__ const char* w_row(const State& st, int s, int r, const float** scrow) const {
+    const int f = st.ft * Cfg::BF + r;
     if (f >= N) return nullptr;
     const KSeg& q = ks[s];
     if (q.f8) {
@@ -200,7 +208,7 @@ struct UpProb {
     return q.w + (int64_t)f * q.ldw * (int64_t)sizeof(CT);
   }
   template <class Acc>
-  __device__ void epilogue(const Acc& acc, int wf0, int wt0, int lane) const;
+  __device__ __forceinline__ void epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const;
 };
 
 // ---------------------------------------------------------------------------
@@ -209,15 +217,18 @@ struct UpProb {
 // -> (expert, feature tile, token tile) with the token tiles innermost, so
 // work-groups that share one weight slab run next to each other on one XCD.
 // ---------------------------------------------------------------------------
+struct ExpertState {
+  int e, ft, m0, rows;
+};
+
 template <class Cfg>
 struct ExpertTiles {
   const int* offsets;
   const int4* tiles;
   const int* tile_count;
   int nft;
-  int e, ft, m0, rows;
 
-  __device__ bool locate(int bid) {
+  __device__ bool locate(int bid, ExpertState& st) const {
     const int R = *tile_count * nft;
     const int per = (R + kXcds - 1) / kXcds;
     if (bid >= per * kXcds) return false;
@@ -225,13 +236,13 @@ struct ExpertTiles {
     if (lg >= R) return false;
     const int4 te = tiles[lg / nft];
     const int local = lg - te.y * nft;
-    ft = local / te.z;
-    const int mt = local - ft * te.z;
-    e = te.x;
-    const int beg = offsets[e];
-    m0 = beg + mt * Cfg::BT;
-    rows = min(Cfg::BT, offsets[e + 1] - m0);
-    return rows > 0;
+    st.ft = local / te.z;
+    const int mt = local - st.ft * te.z;
+    st.e = te.x;
+    const int beg = offsets[st.e];
+    st.m0 = beg + mt * Cfg::BT;
+    st.rows = min(Cfg::BT, offsets[st.e + 1] - st.m0);
+    return st.rows > 0;
   }
 };
 
@@ -249,28 +260,30 @@ struct ExpertGVProb {
   int I, L, k, f8;
   float cap, inv_cap;
 
-  __device__ bool setup(int bid) { return et.locate(bid); }
+  typedef ExpertState State;
+  __device__ bool setup(int bid, State& st) const { return et.locate(bid, st); }
   __device__ int num_ksegs() const { return 1; }
   __device__ int seg_ktiles(int) const { return L * (int)sizeof(CT) / 128; }
-  __device__ bool seg_f8(int) const { return f8; }
-  __device__ int tokens_valid() const { return et.rows; }
-  __device__ int feats_valid() const { return Cfg::BF; }
-  __device__ const char* x_row(int, int r) const {
-    if (r >= et.rows) return nullptr;
-    const int t = sorted[et.m0 + r] / k;
+  __device__ bool seg_f8(const State&, int) const { return f8; }
+  __device__ int tokens_valid(const State& st) const { return st.rows; }
+  __device__ int feats_valid(const State&) const { return Cfg::BF; }
+  __device__ const char* x_row(const State& st, int, int r) const {
+    if (r >= st.rows) return nullptr;
+    const int t = sorted[st.m0 + r] / k;
     return z + (int64_t)t * ldz * (int64_t)sizeof(CT);
   }
-  __device__ const char* w_row(int, int r, const float** scrow) const {
+  __device__ const char* w_row(const State& st, int, int r, const float** scrow) const {
     const int m = r & 63;
-    const int u = et.ft * (Cfg::BF / 2) + (r >> 6) * 32 + (m & 31);
+    const int u = st.ft * (Cfg::BF / 2) + (r >> 6) * 32 + (m & 31);
+    if (u >= I) return nullptr;  // last tile of an I that is not a multiple of BF/2
     const bool val = m >= 32;
     const int64_t wes = f8 ? 1 : sizeof(CT);
-    const int64_t off = ((int64_t)et.e * I + u) * L * wes;
-    if (f8) *scrow = (val ? sv : sg) + ((int64_t)et.e * (I >> 7) + (u >> 7)) * (L >> 7);
+    const int64_t off = ((int64_t)st.e * I + u) * L * wes;
+    if (f8) *scrow = (val ? sv : sg) + ((int64_t)st.e * (I >> 7) + (u >> 7)) * (L >> 7);
     return (val ? wv : wg) + off;
   }
   template <class Acc>
-  __device__ void epilogue(const Acc& acc, int wf0, int wt0, int lane) const;
+  __device__ __forceinline__ void epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const;
 };
 
 template <class Cfg, typename CT>
@@ -282,25 +295,26 @@ struct ExpertDownProb {
   char* out;          // [T*k, L]
   int I, L, f8;
 
-  __device__ bool setup(int bid) { return et.locate(bid); }
+  typedef ExpertState State;
+  __device__ bool setup(int bid, State& st) const { return et.locate(bid, st); }
   __device__ int num_ksegs() const { return 1; }
   __device__ int seg_ktiles(int) const { return I * (int)sizeof(CT) / 128; }
-  __device__ bool seg_f8(int) const { return f8; }
-  __device__ int tokens_valid() const { return et.rows; }
-  __device__ int feats_valid() const { return min(Cfg::BF, L - et.ft * Cfg::BF); }
-  __device__ const char* x_row(int, int r) const {
-    if (r >= et.rows) return nullptr;
-    return act + (int64_t)(et.m0 + r) * I * (int64_t)sizeof(CT);
+  __device__ bool seg_f8(const State&, int) const { return f8; }
+  __device__ int tokens_valid(const State& st) const { return st.rows; }
+  __device__ int feats_valid(const State& st) const { return min(Cfg::BF, L - st.ft * Cfg::BF); }
+  __device__ const char* x_row(const State& st, int, int r) const {
+    if (r >= st.rows) return nullptr;
+    return act + (int64_t)(st.m0 + r) * I * (int64_t)sizeof(CT);
   }
-  __device__ const char* w_row(int, int r, const float** scrow) const {
-    const int f = et.ft * Cfg::BF + r;
+  __device__ const char* w_row(const State& st, int, int r, const float** scrow) const {
+    const int f = st.ft * Cfg::BF + r;
     if (f >= L) return nullptr;
     const int64_t wes = f8 ? 1 : sizeof(CT);
-    if (f8) *scrow = so + ((int64_t)et.e * (L >> 7) + (f >> 7)) * (I >> 7);
-    return wo + ((int64_t)et.e * L + f) * I * wes;
+    if (f8) *scrow = so + ((int64_t)st.e * (L >> 7) + (f >> 7)) * (I >> 7);
+    return wo + ((int64_t)st.e * L + f) * I * wes;
   }
   template <class Acc>
-  __device__ void epilogue(const Acc& acc, int wf0, int wt0, int lane) const;
+  __device__ __forceinline__ void epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const;
 };
 
 // ---------------------------------------------------------------------------
@@ -340,10 +354,10 @@ __device__ __forceinline__ uint4 widen_e4m3(uint2 q, float s) {
 }
 
 template <class Cfg, typename CT, class Prob>
-__global__ __launch_bounds__(Cfg::NT) void gemm_kernel(Prob prob) {
+__global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const Prob p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  Prob p = prob;
-  if (!p.setup(blockIdx.x)) return;
+  typename Prob::State st;
+  if (!p.setup(blockIdx.x, st)) return;
 
   constexpr int NT = Cfg::NT, FI = Cfg::FI, TI = Cfg::TI, CW = Cfg::CW, CX = Cfg::CX;
   constexpr int ES = sizeof(CT);
@@ -358,8 +372,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(Prob prob) {
   const int wf0 = (wid % Cfg::WF) * Cfg::FW;
   const int wt0 = (wid / Cfg::WF) * Cfg::TW;
 
-  const int tvalid = p.tokens_valid();
-  const int fvalid = p.feats_valid();
+  const int tvalid = p.tokens_valid(st);
+  const int fvalid = p.feats_valid(st);
   bool tok[TI], fea[FI];
 #pragma unroll
   for (int i = 0; i < TI; ++i) tok[i] = wt0 + i * 32 < tvalid;
@@ -378,7 +392,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(Prob prob) {
   for (int s = 0; s < nks; ++s) {
     const int nkt = p.seg_ktiles(s);
     if (nkt <= 0) continue;
-    const bool f8 = (ES == 2) && p.seg_f8(s);
+    const bool f8 = (ES == 2) && p.seg_f8(st, s);
 
     const char* wp[CW];
     const float* wsc[CW];
@@ -387,13 +401,13 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(Prob prob) {
     for (int i = 0; i < CW; ++i) {
       const int c = tid + i * NT;
       wsc[i] = nullptr;
-      const char* rp = p.w_row(s, c >> 3, &wsc[i]);
+      const char* rp = p.w_row(st, s, c >> 3, &wsc[i]);
       wp[i] = rp ? rp + (c & 7) * (f8 ? 8 : 16) : nullptr;
     }
 #pragma unroll
     for (int i = 0; i < CX; ++i) {
       const int c = tid + i * NT;
-      const char* rp = p.x_row(s, c >> 3);
+      const char* rp = p.x_row(st, s, c >> 3);
       xp[i] = rp ? rp + (c & 7) * 16 : nullptr;
     }
 
@@ -466,7 +480,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(Prob prob) {
       __syncthreads();
     }
   }
-  p.epilogue(acc, wf0, wt0, lane);
+  p.epilogue(st, acc, wf0, wt0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -497,11 +511,12 @@ __device__ __forceinline__ void for_glu(int wf0, int wt0, int lane, F&& f) {
 
 template <class Cfg, typename CT>
 template <class Acc>
-__device__ void DenseXProb<Cfg, CT>::epilogue(const Acc& acc, int wf0, int wt0, int lane) const {
-  const NSeg& s = seg[si];
-  const int tv = tokens_valid();
+__device__ __forceinline__ void DenseXProb<Cfg, CT>::epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const {
+  const NSeg& s = st.s;
+  const int tv = tokens_valid(st);
+  const int tt = st.tt, f0 = st.f0;
   if (s.kind == EPI_GLU) {
-    for_glu<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int ul, int tl) {
+    for_glu<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int ul, int tl) __attribute__((always_inline)) {
       if (tl < tv) {
         float v[4];
 #pragma unroll
@@ -512,7 +527,7 @@ __device__ void DenseXProb<Cfg, CT>::epilogue(const Acc& acc, int wf0, int wt0, 
       }
     });
   } else {
-    for_acc<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int fl, int tl) {
+    for_acc<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int fl, int tl) __attribute__((always_inline)) {
       if (tl < tv) {
         float v[4];
 #pragma unroll
@@ -532,9 +547,10 @@ __device__ void DenseXProb<Cfg, CT>::epilogue(const Acc& acc, int wf0, int wt0, 
 
 template <class Cfg, typename CT>
 template <class Acc>
-__device__ void UpProb<Cfg, CT>::epilogue(const Acc& acc, int wf0, int wt0, int lane) const {
-  const int tv = tokens_valid();
-  for_acc<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int fl, int tl) {
+__device__ __forceinline__ void UpProb<Cfg, CT>::epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const {
+  const int tv = tokens_valid(st);
+  const int tt = st.tt, ft = st.ft;
+  for_acc<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int fl, int tl) __attribute__((always_inline)) {
     const int f = ft * Cfg::BF + fl;
     if (tl < tv && f < N) {
       const int64_t t = (int64_t)tt * Cfg::BT + tl;
@@ -554,28 +570,28 @@ __device__ void UpProb<Cfg, CT>::epilogue(const Acc& acc, int wf0, int wt0, int 
 
 template <class Cfg, typename CT>
 template <class Acc>
-__device__ void ExpertGVProb<Cfg, CT>::epilogue(const Acc& acc, int wf0, int wt0, int lane) const {
-  for_glu<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int ul, int tl) {
-    if (tl < et.rows) {
+__device__ __forceinline__ void ExpertGVProb<Cfg, CT>::epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const {
+  for_glu<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int ul, int tl) __attribute__((always_inline)) {
+    if (tl < st.rows) {
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = situ_glu(acc[i][j][4 * g + r], acc[i + 1][j][4 * g + r], cap, inv_cap);
-      CT* row = reinterpret_cast<CT*>(act) + (int64_t)(et.m0 + tl) * I;
-      store4<CT>(row, et.ft * (Cfg::BF / 2) + ul, v, I, true);
+      CT* row = reinterpret_cast<CT*>(act) + (int64_t)(st.m0 + tl) * I;
+      store4<CT>(row, st.ft * (Cfg::BF / 2) + ul, v, I, true);
     }
   });
 }
 
 template <class Cfg, typename CT>
 template <class Acc>
-__device__ void ExpertDownProb<Cfg, CT>::epilogue(const Acc& acc, int wf0, int wt0, int lane) const {
-  for_acc<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int fl, int tl) {
-    if (tl < et.rows) {
+__device__ __forceinline__ void ExpertDownProb<Cfg, CT>::epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const {
+  for_acc<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int fl, int tl) __attribute__((always_inline)) {
+    if (tl < st.rows) {
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r];
-      CT* row = reinterpret_cast<CT*>(out) + (int64_t)(et.m0 + tl) * L;
-      store4<CT>(row, et.ft * Cfg::BF + fl, v, L, true);
+      CT* row = reinterpret_cast<CT*>(out) + (int64_t)(st.m0 + tl) * L;
+      store4<CT>(row, st.ft * Cfg::BF + fl, v, L, true);
     }
   });
 }

@@ -7,7 +7,7 @@
 
 #include <mutex>
 
-#include "gemm.hpp"
+#include "gemm2.hpp"
 #include "kernels.hpp"
 #include "lmoe.h"
 
@@ -101,11 +101,28 @@ lmoe_status check_weights(const lmoe_shape* sh, const lmoe_weights* w, unsigned 
 // ---------------------------------------------------------------------------
 // Kernel choices and the workspace plan.
 // ---------------------------------------------------------------------------
-// Expert GEMMs use the small token tile when experts hold few rows on average
-// (decode, small batches), the big one otherwise; dense GEMMs switch on T.
-bool expert_small(const lmoe_shape* sh) { return sh->T * (int64_t)sh->k < 48 * (int64_t)sh->E; }
+// Kernel choice.  bf16 layers with bf16 expert weights run the LDS-DMA
+// pipeline (gemm2.hpp); fp32 layers and e4m3 weights run the register-staged
+// mainloop (gemm.hpp), which widens e4m3 codes on the way into LDS.
+bool use_dma(const lmoe_shape* sh) { return sh->act == LMOE_BF16 && sh->w_expert == LMOE_BF16; }
+
+// Experts: token tile by the mean rows per expert (T*k/E).
+enum ExpertTile { ET_SMALL, ET_MID, ET_BIG };
+ExpertTile expert_tile(const lmoe_shape* sh) {
+  const int64_t tk = sh->T * (int64_t)sh->k;
+  if (use_dma(sh)) {
+    if (tk < 16 * (int64_t)sh->E) return ET_SMALL;
+    if (tk < 96 * (int64_t)sh->E) return ET_MID;
+    return ET_BIG;
+  }
+  return tk < 48 * (int64_t)sh->E ? ET_SMALL : ET_BIG;
+}
+int expert_bt(const lmoe_shape* sh) {
+  const ExpertTile t = expert_tile(sh);
+  if (use_dma(sh)) return t == ET_SMALL ? T2Small::BT : t == ET_MID ? T2Mid::BT : T2Expert::BT;
+  return t == ET_SMALL ? CfgSmall::BT : CfgBig::BT;
+}
 bool dense_small(const lmoe_shape* sh) { return sh->T <= 256; }
-int expert_bt(const lmoe_shape* sh) { return expert_small(sh) ? CfgSmall::BT : CfgBig::BT; }
 
 // Upper bound of the number of token tiles over all experts.
 int64_t max_tiles(const lmoe_shape* sh, int bt) {
@@ -167,7 +184,9 @@ lmoe_status check_ws(const lmoe_shape* sh, const void* ws, size_t ws_bytes) {
 template <class Cfg, typename CT, class Prob>
 hipError_t launch_gemm(const Prob& p, int64_t grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  auto kern = gemm_kernel<Cfg, CT, Prob>;
+  void (*kern)(const Prob);
+  if constexpr (Cfg::kDma) kern = gemm2_kernel<Cfg, Prob>;
+  else kern = gemm_kernel<Cfg, CT, Prob>;
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [&] {
@@ -299,7 +318,7 @@ hipError_t expert_gv(const Ctx& c, const void* z, const int32_t* offsets, const 
   p.et.offsets = offsets;
   p.et.tiles = tiles;
   p.et.tile_count = tcount;
-  p.et.nft = (int)(sh->I / (Cfg::BF / 2));
+  p.et.nft = (int)cdiv(sh->I, Cfg::BF / 2);
   p.z = static_cast<const char*>(z);
   p.ldz = sh->L;
   p.sorted = sorted;
@@ -336,29 +355,61 @@ hipError_t expert_down(const Ctx& c, const void* act, const int32_t* offsets, co
   return launch_gemm<Cfg, CT>(p, pad8(max_tiles(sh, Cfg::BT) * p.et.nft), c.st);
 }
 
-// Dispatch on (dense tile, activation dtype).
+// Dispatch on (dtype, tile).
 template <typename CT>
 hipError_t xgemm_any(const Ctx& c, const void* x, float* logits, void* z, void* hs) {
+  if constexpr (sizeof(CT) == 2) {
+    if (!(hs && is_f8(c.sh)))
+      return dense_small(c.sh) ? xgemm<T2Thin, CT>(c, x, logits, z, hs) : xgemm<T2Dense, CT>(c, x, logits, z, hs);
+  }
   return dense_small(c.sh) ? xgemm<CfgSmall, CT>(c, x, logits, z, hs) : xgemm<CfgBig, CT>(c, x, logits, z, hs);
 }
 template <typename CT>
 hipError_t upgemm_any(const Ctx& c, const void* n, const void* hs, void* y) {
+  if constexpr (sizeof(CT) == 2) {
+    if (!(c.sh->S > 0 && is_f8(c.sh)))
+      return dense_small(c.sh) ? upgemm<T2Thin, CT>(c, n, hs, y) : upgemm<T2Dense, CT>(c, n, hs, y);
+  }
   return dense_small(c.sh) ? upgemm<CfgSmall, CT>(c, n, hs, y) : upgemm<CfgBig, CT>(c, n, hs, y);
+}
+
+template <typename CT>
+hipError_t expert_gv_any(const Ctx& c, const void* z, const int32_t* offsets, const int32_t* sorted,
+                         const int4* tiles, const int32_t* tcount, void* act) {
+  const ExpertTile t = expert_tile(c.sh);
+  if constexpr (sizeof(CT) == 2) {
+    if (use_dma(c.sh)) {
+      if (t == ET_SMALL) return expert_gv<T2Small, CT>(c, z, offsets, sorted, tiles, tcount, act);
+      if (t == ET_MID) return expert_gv<T2Mid, CT>(c, z, offsets, sorted, tiles, tcount, act);
+      return expert_gv<T2Expert, CT>(c, z, offsets, sorted, tiles, tcount, act);
+    }
+  }
+  return t == ET_SMALL ? expert_gv<CfgSmall, CT>(c, z, offsets, sorted, tiles, tcount, act)
+                       : expert_gv<CfgBig, CT>(c, z, offsets, sorted, tiles, tcount, act);
+}
+template <typename CT>
+hipError_t expert_down_any(const Ctx& c, const void* act, const int32_t* offsets, const int4* tiles,
+                           const int32_t* tcount, void* out) {
+  const ExpertTile t = expert_tile(c.sh);
+  if constexpr (sizeof(CT) == 2) {
+    if (use_dma(c.sh)) {
+      if (t == ET_SMALL) return expert_down<T2Small, CT>(c, act, offsets, tiles, tcount, out);
+      if (t == ET_MID) return expert_down<T2Mid, CT>(c, act, offsets, tiles, tcount, out);
+      return expert_down<T2Expert, CT>(c, act, offsets, tiles, tcount, out);
+    }
+  }
+  return t == ET_SMALL ? expert_down<CfgSmall, CT>(c, act, offsets, tiles, tcount, out)
+                       : expert_down<CfgBig, CT>(c, act, offsets, tiles, tcount, out);
 }
 
 // Both expert GEMMs plus the tile list they share.
 template <typename CT>
 hipError_t experts_any(const Ctx& c, const void* z, const int32_t* offsets, const int32_t* sorted, void* act,
                        void* out, int4* tiles, int32_t* tcount) {
-  const lmoe_shape* sh = c.sh;
-  hipError_t e = launch_tiles(offsets, sh->E, expert_bt(sh), tiles, tcount, 0, nullptr, nullptr, c.st);
+  hipError_t e = launch_tiles(offsets, c.sh->E, expert_bt(c.sh), tiles, tcount, 0, nullptr, nullptr, c.st);
   if (e != hipSuccess) return e;
-  if (expert_small(sh)) {
-    if ((e = expert_gv<CfgSmall, CT>(c, z, offsets, sorted, tiles, tcount, act)) != hipSuccess) return e;
-    return expert_down<CfgSmall, CT>(c, act, offsets, tiles, tcount, out);
-  }
-  if ((e = expert_gv<CfgBig, CT>(c, z, offsets, sorted, tiles, tcount, act)) != hipSuccess) return e;
-  return expert_down<CfgBig, CT>(c, act, offsets, tiles, tcount, out);
+  if ((e = expert_gv_any<CT>(c, z, offsets, sorted, tiles, tcount, act)) != hipSuccess) return e;
+  return expert_down_any<CT>(c, act, offsets, tiles, tcount, out);
 }
 
 bool bf16_act(const lmoe_shape* sh) { return sh->act == LMOE_BF16; }
@@ -518,21 +569,12 @@ lmoe_status lmoe_forward(const lmoe_shape* sh, const lmoe_weights* w, const void
   const void* zin = z ? z : x;
   const int4* tiles = at<int4>(ws, pl.tiles_a);
   const int32_t* tc = at<int32_t>(ws, pl.tcount);
-  hipError_t e;
-  if (expert_small(sh))
-    e = bf ? expert_gv<CfgSmall, bf16>(c, zin, offsets, sorted, tiles, tc, act)
-           : expert_gv<CfgSmall, float>(c, zin, offsets, sorted, tiles, tc, act);
-  else
-    e = bf ? expert_gv<CfgBig, bf16>(c, zin, offsets, sorted, tiles, tc, act)
-           : expert_gv<CfgBig, float>(c, zin, offsets, sorted, tiles, tc, act);
-  LMOE_HIP(e, "expert gate/value GEMM");
+  LMOE_HIP(bf ? expert_gv_any<bf16>(c, zin, offsets, sorted, tiles, tc, act)
+              : expert_gv_any<float>(c, zin, offsets, sorted, tiles, tc, act),
+           "expert gate/value GEMM");
   if (lmoe_status s = record(ev, 4, c.st)) return s;
-  if (expert_small(sh))
-    e = bf ? expert_down<CfgSmall, bf16>(c, act, offsets, tiles, tc, out)
-           : expert_down<CfgSmall, float>(c, act, offsets, tiles, tc, out);
-  else
-    e = bf ? expert_down<CfgBig, bf16>(c, act, offsets, tiles, tc, out)
-           : expert_down<CfgBig, float>(c, act, offsets, tiles, tc, out);
+  hipError_t e = bf ? expert_down_any<bf16>(c, act, offsets, tiles, tc, out)
+                    : expert_down_any<float>(c, act, offsets, tiles, tc, out);
   LMOE_HIP(e, "expert down GEMM");
   if (lmoe_status s = record(ev, 5, c.st)) return s;
   LMOE_HIP(launch_combine_norm(bf, out, pos, tw, w->gamma, sh->T, sh->L, sh->k, sh->rms_eps, n, c.st),

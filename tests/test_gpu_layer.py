@@ -55,6 +55,25 @@ def test_forward_small(dev, name):
         assert np.abs(forced["z"] @ O.decode(inp["w_gate"][0], "f32").T).max() > 300
 
 
+@pytest.mark.parametrize("T", [20, 300, 700, 2000])
+def test_forward_tile_variants(dev, T):
+    """Token counts that select each kernel tile: thin / dense x- and up-GEMMs,
+    small / mid / big expert token tiles (experts with 1-3, ~50, ~330 rows)."""
+    cfg = replace(get_config("small_bf16"), T=T, name=f"small_bf16_T{T}")
+    note(f"[forward] {cfg.name}")
+    t, g = make_case(cfg, dev)
+    sh, w = _weights(cfg, g)
+    y, idx, tw = lmoe.forward(sh, w, g["x"])
+    torch.cuda.synchronize()
+    inp = host_inputs(t)
+    ref = O.forward(inp, spec_of(cfg))
+    check_selection(idx.cpu().numpy(), tw.cpu().numpy(), ref)
+    forced = O.forward(inp, spec_of(cfg), forced_idx=idx.cpu().numpy().astype(np.int64), forced_tol=1e-5)
+    err = rowwise_rel_err(to_f64(y), forced["y"])
+    note(f"    max row rel err {err:.3e}")
+    assert err <= tol_of(cfg)
+
+
 @pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "small_fp8", "small_identity_bf16"])
 def test_route(dev, name):
     cfg = get_config(name)
