@@ -51,25 +51,27 @@ def _run(cmd, verbose):
     return r.stdout
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link liblmoe.so; returns its path."""
+def build(verbose: bool = False, defines=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every HIP source for gfx950 and link liblmoe.so; returns its
+    path.  `defines` (NAME=VALUE strings) and `out` build a variant elsewhere."""
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
+    flags = FLAGS + [f"-D{d}" for d in defines]
     objs = []
     jobs = []
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         for s in SOURCES:
-            o = os.path.join(BUILD, os.path.splitext(s)[0] + ".o")
+            o = os.path.join(build_dir, os.path.splitext(s)[0] + ".o")
             objs.append(o)
-            jobs.append(ex.submit(_run, [hipcc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o], verbose))
+            jobs.append(ex.submit(_run, [hipcc, *flags, "-c", os.path.join(CSRC, s), "-o", o], verbose))
         for j in jobs:
-            out = j.result()
-            if verbose and out.strip():
-                print(out)
-    tmp = LIB + ".tmp"
+            log = j.result()
+            if verbose and log.strip():
+                print(log)
+    tmp = out + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

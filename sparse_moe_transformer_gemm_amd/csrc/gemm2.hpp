@@ -28,9 +28,10 @@ namespace lmoe {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int BF_, int BT_, int WF_, int WT_, int STAGES_>
+template <int BF_, int BT_, int WF_, int WT_, int STAGES_, int WAUX_ = 0>
 struct Tile2 {
   static constexpr int BF = BF_, BT = BT_, WF = WF_, WT = WT_, STAGES = STAGES_;
+  static constexpr int WAUX = WAUX_;  // cache policy of the weight loads
   static constexpr int NT = WF * WT * kWave, NW = WF * WT;
   static constexpr int FW = BF / WF, TW = BT / WT;
   static constexpr int FI = FW / 32, TI = TW / 32;
@@ -39,6 +40,7 @@ struct Tile2 {
   static constexpr int STAGE_BYTES = (BF + BT) * 128;
   static constexpr int LDS = STAGES * STAGE_BYTES;
   static constexpr bool kDma = true;
+  static constexpr bool kSplit = false;
   static_assert(FW % 64 == 0 && TW % 32 == 0, "wave tile");
   static_assert((QW + QX) % NW == 0, "DMA instructions split evenly over the waves");
   static_assert(STAGES >= 2 && NQ * (STAGES - 2) <= 63, "vmcnt range");
@@ -47,19 +49,77 @@ struct Tile2 {
 
 // Dense GEMMs over many tokens / few tokens (weight streaming); experts
 // holding many rows, a few dozen rows, or one or two rows (decode).
-typedef Tile2<256, 128, 2, 2, 3> T2Dense;
-typedef Tile2<64, 32, 1, 1, 4> T2Thin;
-typedef Tile2<128, 256, 2, 2, 3> T2Expert;
-typedef Tile2<256, 64, 4, 1, 3> T2Mid;
-typedef Tile2<256, 32, 4, 1, 4> T2Small;
+// Split-ring tile (gemm3_kernel below): weights three stages deep, tokens two.
+template <int BF_, int BT_, int WF_, int WT_, int WAUX_>
+struct Tile3 {
+  static constexpr int BF = BF_, BT = BT_, WF = WF_, WT = WT_, WAUX = WAUX_;
+  static constexpr int NT = WF * WT * kWave, NW = WF * WT;
+  static constexpr int FW = BF / WF, TW = BT / WT;
+  static constexpr int FI = FW / 32, TI = TW / 32;
+  static constexpr int QW = BF / 8, QX = BT / 8;
+  static constexpr int NQW = QW / NW, NQX = QX / NW;
+  static constexpr int SW = 3, SX = 2;
+  static constexpr int X_OFF = SW * BF * 128;
+  static constexpr int LDS = SW * BF * 128 + SX * BT * 128;
+  static constexpr bool kDma = true;
+  static constexpr bool kSplit = true;
+  static_assert(FW % 64 == 0 && TW % 32 == 0, "wave tile");
+  static_assert(QW % NW == 0 && QX % NW == 0, "DMA instructions split evenly over the waves");
+  static_assert(NQW <= 63, "vmcnt range");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+// Tile shapes: features x tokens, waves along features x tokens, pipeline
+// stages, weight-load cache policy (gfx950 CPol bits: 1 = sc0, 2 = nt,
+// 16 = sc1).  Expert gate/value and down GEMMs of one size class share the
+// token tile (and so the expert tile list).
+#ifndef LMOE_T2DENSE
+#define LMOE_T2DENSE 256, 256, 2, 4
+#endif
+#ifndef LMOE_T2THIN
+#define LMOE_T2THIN 64, 32, 1, 1, 4
+#endif
+#ifndef LMOE_T2EXPERT_GV
+#define LMOE_T2EXPERT_GV 256, 256, 2, 4
+#endif
+#ifndef LMOE_T2EXPERT_DN
+#define LMOE_T2EXPERT_DN 256, 256, 2, 4
+#endif
+#ifndef LMOE_T2MID_GV
+#define LMOE_T2MID_GV 256, 64, 4, 1, 3
+#endif
+#ifndef LMOE_T2MID_DN
+#define LMOE_T2MID_DN 256, 64, 4, 1, 3
+#endif
+#ifndef LMOE_T2SMALL_GV
+#define LMOE_T2SMALL_GV 256, 32, 4, 1, 4, 2
+#endif
+#ifndef LMOE_T2SMALL_DN
+#define LMOE_T2SMALL_DN 256, 32, 4, 1, 4, 2
+#endif
+typedef Tile3<LMOE_T2DENSE, 0> T2Dense;
+typedef Tile2<LMOE_T2THIN> T2Thin;
+typedef Tile3<LMOE_T2EXPERT_GV, 0> T2ExpertGV;
+typedef Tile3<LMOE_T2EXPERT_DN, 0> T2ExpertDn;
+typedef Tile2<LMOE_T2MID_GV> T2MidGV;
+typedef Tile2<LMOE_T2MID_DN> T2MidDn;
+typedef Tile2<LMOE_T2SMALL_GV> T2SmallGV;
+typedef Tile2<LMOE_T2SMALL_DN> T2SmallDn;
+static_assert(T2ExpertGV::BT == T2ExpertDn::BT && T2MidGV::BT == T2MidDn::BT && T2SmallGV::BT == T2SmallDn::BT,
+              "expert GEMMs of one size class share the token tile");
+
+#ifndef LMOE_X_AUX
+#define LMOE_X_AUX 0
+#endif
 
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 // 16 bytes per lane from `g` into LDS at `lds` + 16 * lane (lds wave-uniform).
 // A __device__ function, not a lambda: lambdas are also compiled for the host,
 // where the builtin does not exist.
+template <int AUX>
 __device__ __forceinline__ void dma16(const char* g, char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, AUX);
 }
 
 template <int N>
@@ -130,7 +190,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm2_kernel(const Prob p) {
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int q = wid + NW * i;
-      dma16(src[i] + (int64_t)ik * 128, base + q * 1024);
+      if (q < Cfg::QW) dma16<Cfg::WAUX>(src[i] + (int64_t)ik * 128, base + q * 1024);
+      else dma16<LMOE_X_AUX>(src[i] + (int64_t)ik * 128, base + q * 1024);
     }
     if (++ik == p.seg_ktiles(is)) {
       ik = 0;
@@ -177,6 +238,132 @@ __global__ __launch_bounds__(Cfg::NT) void gemm2_kernel(const Prob p) {
     }
     if (kt + S - 1 < nkt) issue((kt + S - 1) % S);
     compute(kt % S);
+  }
+  p.epilogue(st, acc, wf0, wt0, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Split rings: the weight operand (streamed from HBM) gets three LDS stages
+// and runs two k-tiles ahead; the token operand (re-read by neighbouring
+// tiles, mostly from L2) gets two stages and runs one k-tile ahead.  Issue
+// order: X(0) W(0) W(1) before the loop, then X(kt+1) W(kt+2) in iteration
+// kt.  At the top of iteration kt the only DMA issued after the newest
+// operand that iteration kt needs (X(kt), or W(0) when kt = 0) is W(kt+1), so
+// the wait is vmcnt(NQW) while W(kt+1) exists and vmcnt(0) after.
+// ---------------------------------------------------------------------------
+template <class Cfg, class Prob>
+__global__ __launch_bounds__(Cfg::NT) void gemm3_kernel(const Prob p) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  typename Prob::State st;
+  if (!p.setup(blockIdx.x, st)) return;
+
+  constexpr int FI = Cfg::FI, TI = Cfg::TI, NQW = Cfg::NQW, NQX = Cfg::NQX, NW = Cfg::NW;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wf0 = (wid % Cfg::WF) * Cfg::FW;
+  const int wt0 = (wid / Cfg::WF) * Cfg::TW;
+
+  const int tvalid = p.tokens_valid(st);
+  const int fvalid = p.feats_valid(st);
+  bool tok[TI], fea[FI];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) tok[i] = wt0 + i * 32 < tvalid;
+#pragma unroll
+  for (int i = 0; i < FI; ++i) fea[i] = wf0 + i * 32 < fvalid;
+
+  f32x16 acc[FI][TI];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < TI; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nks = p.num_ksegs();
+  int nkt = 0;
+  for (int s = 0; s < nks; ++s) nkt += p.seg_ktiles(s);
+
+  // issue cursors (segment, k-tile within it) and source pointers per operand
+  int wsg = 0, wk = 0, xsg = 0, xk = 0;
+  while (wsg < nks && p.seg_ktiles(wsg) == 0) ++wsg;
+  xsg = wsg;
+  const char* srcW[NQW];
+  const char* srcX[NQX];
+  auto set_w = [&](int s) {
+    const float* dummy = nullptr;
+    const char* w0 = p.w_row(st, s, 0, &dummy);
+#pragma unroll
+    for (int i = 0; i < NQW; ++i) {
+      const int row = (wid + NW * i) * 8 + (lane >> 3);
+      const char* rp = p.w_row(st, s, row, &dummy);
+      srcW[i] = (rp ? rp : w0) + (((lane & 7) ^ swz(row)) << 4);
+    }
+  };
+  auto set_x = [&](int s) {
+    const char* x0 = p.x_row(st, s, 0);
+#pragma unroll
+    for (int i = 0; i < NQX; ++i) {
+      const int row = (wid + NW * i) * 8 + (lane >> 3);
+      const char* rp = p.x_row(st, s, row);
+      srcX[i] = (rp ? rp : x0) + (((lane & 7) ^ swz(row)) << 4);
+    }
+  };
+  if (wsg < nks) {
+    set_w(wsg);
+    set_x(xsg);
+  }
+  auto issue_w = [&](int buf) {
+    char* base = smem + buf * Cfg::BF * 128;
+#pragma unroll
+    for (int i = 0; i < NQW; ++i) dma16<Cfg::WAUX>(srcW[i] + (int64_t)wk * 128, base + (wid + NW * i) * 1024);
+    if (++wk == p.seg_ktiles(wsg)) {
+      wk = 0;
+      do { ++wsg; } while (wsg < nks && p.seg_ktiles(wsg) == 0);
+      if (wsg < nks) set_w(wsg);
+    }
+  };
+  auto issue_x = [&](int buf) {
+    char* base = smem + Cfg::X_OFF + buf * Cfg::BT * 128;
+#pragma unroll
+    for (int i = 0; i < NQX; ++i) dma16<LMOE_X_AUX>(srcX[i] + (int64_t)xk * 128, base + (wid + NW * i) * 1024);
+    if (++xk == p.seg_ktiles(xsg)) {
+      xk = 0;
+      do { ++xsg; } while (xsg < nks && p.seg_ktiles(xsg) == 0);
+      if (xsg < nks) set_x(xsg);
+    }
+  };
+
+  const int lr = lane & 31;
+  const int sw = swz(lr);
+  auto compute = [&](int wbuf, int xbuf) {
+    const char* sW = smem + wbuf * Cfg::BF * 128;
+    const char* sX = smem + Cfg::X_OFF + xbuf * Cfg::BT * 128;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ch = ((2 * ks + (lane >> 5)) ^ sw) << 4;
+      bf16x8 a[FI], b[TI];
+#pragma unroll
+      for (int i = 0; i < FI; ++i) a[i] = *reinterpret_cast<const bf16x8*>(sW + (wf0 + i * 32 + lr) * 128 + ch);
+#pragma unroll
+      for (int j = 0; j < TI; ++j) b[j] = *reinterpret_cast<const bf16x8*>(sX + (wt0 + j * 32 + lr) * 128 + ch);
+#pragma unroll
+      for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < TI; ++j)
+          if (fea[i] && tok[j]) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+    }
+  };
+
+  if (nkt > 0) {
+    issue_x(0);
+    issue_w(0);
+    if (nkt > 1) issue_w(1);
+  }
+  for (int kt = 0; kt < nkt; ++kt) {
+    if (kt + 1 < nkt) wait_vmcnt_barrier<NQW>();
+    else wait_vmcnt_barrier<0>();
+    if (kt + 1 < nkt) issue_x((kt + 1) & 1);
+    if (kt + 2 < nkt) issue_w((kt + 2) % 3);
+    compute(kt % 3, kt & 1);
   }
   p.epilogue(st, acc, wf0, wt0, lane);
 }

@@ -119,7 +119,7 @@ ExpertTile expert_tile(const lmoe_shape* sh) {
 }
 int expert_bt(const lmoe_shape* sh) {
   const ExpertTile t = expert_tile(sh);
-  if (use_dma(sh)) return t == ET_SMALL ? T2Small::BT : t == ET_MID ? T2Mid::BT : T2Expert::BT;
+  if (use_dma(sh)) return t == ET_SMALL ? T2SmallGV::BT : t == ET_MID ? T2MidGV::BT : T2ExpertGV::BT;
   return t == ET_SMALL ? CfgSmall::BT : CfgBig::BT;
 }
 bool dense_small(const lmoe_shape* sh) { return sh->T <= 256; }
@@ -185,8 +185,12 @@ template <class Cfg, typename CT, class Prob>
 hipError_t launch_gemm(const Prob& p, int64_t grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   void (*kern)(const Prob);
-  if constexpr (Cfg::kDma) kern = gemm2_kernel<Cfg, Prob>;
-  else kern = gemm_kernel<Cfg, CT, Prob>;
+  if constexpr (Cfg::kDma) {
+    if constexpr (Cfg::kSplit) kern = gemm3_kernel<Cfg, Prob>;
+    else kern = gemm2_kernel<Cfg, Prob>;
+  } else {
+    kern = gemm_kernel<Cfg, CT, Prob>;
+  }
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [&] {
@@ -379,9 +383,9 @@ hipError_t expert_gv_any(const Ctx& c, const void* z, const int32_t* offsets, co
   const ExpertTile t = expert_tile(c.sh);
   if constexpr (sizeof(CT) == 2) {
     if (use_dma(c.sh)) {
-      if (t == ET_SMALL) return expert_gv<T2Small, CT>(c, z, offsets, sorted, tiles, tcount, act);
-      if (t == ET_MID) return expert_gv<T2Mid, CT>(c, z, offsets, sorted, tiles, tcount, act);
-      return expert_gv<T2Expert, CT>(c, z, offsets, sorted, tiles, tcount, act);
+      if (t == ET_SMALL) return expert_gv<T2SmallGV, CT>(c, z, offsets, sorted, tiles, tcount, act);
+      if (t == ET_MID) return expert_gv<T2MidGV, CT>(c, z, offsets, sorted, tiles, tcount, act);
+      return expert_gv<T2ExpertGV, CT>(c, z, offsets, sorted, tiles, tcount, act);
     }
   }
   return t == ET_SMALL ? expert_gv<CfgSmall, CT>(c, z, offsets, sorted, tiles, tcount, act)
@@ -393,9 +397,9 @@ hipError_t expert_down_any(const Ctx& c, const void* act, const int32_t* offsets
   const ExpertTile t = expert_tile(c.sh);
   if constexpr (sizeof(CT) == 2) {
     if (use_dma(c.sh)) {
-      if (t == ET_SMALL) return expert_down<T2Small, CT>(c, act, offsets, tiles, tcount, out);
-      if (t == ET_MID) return expert_down<T2Mid, CT>(c, act, offsets, tiles, tcount, out);
-      return expert_down<T2Expert, CT>(c, act, offsets, tiles, tcount, out);
+      if (t == ET_SMALL) return expert_down<T2SmallDn, CT>(c, act, offsets, tiles, tcount, out);
+      if (t == ET_MID) return expert_down<T2MidDn, CT>(c, act, offsets, tiles, tcount, out);
+      return expert_down<T2ExpertDn, CT>(c, act, offsets, tiles, tcount, out);
     }
   }
   return t == ET_SMALL ? expert_down<CfgSmall, CT>(c, act, offsets, tiles, tcount, out)
