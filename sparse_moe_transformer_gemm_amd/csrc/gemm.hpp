@@ -33,7 +33,7 @@ struct TileCfg {
   static constexpr int CX = BT * 8 / NT;  // same, X tile
   static constexpr int LDS = 2 * (BF + BT) * kPitch;
   static constexpr bool kDma = false;
-  static constexpr bool kSplit = false;
+  static constexpr int kKind = 1;
   static_assert(FW % 64 == 0, "a wave covers whole gate/value pairs");
   static_assert(TW % 32 == 0 && CW >= 1 && CX >= 1, "tile shape");
   static_assert((BF * 8) % NT == 0 && (BT * 8) % NT == 0, "chunk split");

@@ -40,7 +40,7 @@ struct Tile2 {
   static constexpr int STAGE_BYTES = (BF + BT) * 128;
   static constexpr int LDS = STAGES * STAGE_BYTES;
   static constexpr bool kDma = true;
-  static constexpr bool kSplit = false;
+  static constexpr int kKind = 2;
   static_assert(FW % 64 == 0 && TW % 32 == 0, "wave tile");
   static_assert((QW + QX) % NW == 0, "DMA instructions split evenly over the waves");
   static_assert(STAGES >= 2 && NQ * (STAGES - 2) <= 63, "vmcnt range");
@@ -62,49 +62,49 @@ struct Tile3 {
   static constexpr int X_OFF = SW * BF * 128;
   static constexpr int LDS = SW * BF * 128 + SX * BT * 128;
   static constexpr bool kDma = true;
-  static constexpr bool kSplit = true;
+  static constexpr int kKind = 3;
   static_assert(FW % 64 == 0 && TW % 32 == 0, "wave tile");
   static_assert(QW % NW == 0 && QX % NW == 0, "DMA instructions split evenly over the waves");
   static_assert(NQW <= 63, "vmcnt range");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-// Tile shapes: features x tokens, waves along features x tokens, pipeline
-// stages, weight-load cache policy (gfx950 CPol bits: 1 = sc0, 2 = nt,
-// 16 = sc1).  Expert gate/value and down GEMMs of one size class share the
-// token tile (and so the expert tile list).
-#ifndef LMOE_T2DENSE
-#define LMOE_T2DENSE 256, 256, 2, 4
+// Tile configurations (full types, overridable at build time for tuning
+// sweeps).  Tile2: one ring for both operands; Tile3: weight ring 3 deep,
+// token ring 2 deep.  Expert gate/value and down GEMMs of one size class
+// share the token tile (and so the expert tile list).
+#ifndef LMOE_T_DENSE
+#define LMOE_T_DENSE Tile3<256, 256, 4, 4, 0>
 #endif
-#ifndef LMOE_T2THIN
-#define LMOE_T2THIN 64, 32, 1, 1, 4
+#ifndef LMOE_T_THIN
+#define LMOE_T_THIN Tile2<64, 32, 1, 1, 4, 0>
 #endif
-#ifndef LMOE_T2EXPERT_GV
-#define LMOE_T2EXPERT_GV 256, 256, 2, 4
+#ifndef LMOE_T_EXPERT_GV
+#define LMOE_T_EXPERT_GV Tile3<256, 256, 4, 4, 0>
 #endif
-#ifndef LMOE_T2EXPERT_DN
-#define LMOE_T2EXPERT_DN 256, 256, 2, 4
+#ifndef LMOE_T_EXPERT_DN
+#define LMOE_T_EXPERT_DN Tile3<256, 256, 4, 4, 0>
 #endif
-#ifndef LMOE_T2MID_GV
-#define LMOE_T2MID_GV 256, 64, 4, 1, 3
+#ifndef LMOE_T_MID_GV
+#define LMOE_T_MID_GV Tile2<256, 64, 4, 1, 3, 0>
 #endif
-#ifndef LMOE_T2MID_DN
-#define LMOE_T2MID_DN 256, 64, 4, 1, 3
+#ifndef LMOE_T_MID_DN
+#define LMOE_T_MID_DN Tile2<256, 64, 4, 1, 3, 0>
 #endif
-#ifndef LMOE_T2SMALL_GV
-#define LMOE_T2SMALL_GV 256, 32, 4, 1, 4, 2
+#ifndef LMOE_T_SMALL_GV
+#define LMOE_T_SMALL_GV Tile2<256, 32, 4, 1, 4, 2>
 #endif
-#ifndef LMOE_T2SMALL_DN
-#define LMOE_T2SMALL_DN 256, 32, 4, 1, 4, 2
+#ifndef LMOE_T_SMALL_DN
+#define LMOE_T_SMALL_DN Tile2<256, 32, 4, 1, 4, 2>
 #endif
-typedef Tile3<LMOE_T2DENSE, 0> T2Dense;
-typedef Tile2<LMOE_T2THIN> T2Thin;
-typedef Tile3<LMOE_T2EXPERT_GV, 0> T2ExpertGV;
-typedef Tile3<LMOE_T2EXPERT_DN, 0> T2ExpertDn;
-typedef Tile2<LMOE_T2MID_GV> T2MidGV;
-typedef Tile2<LMOE_T2MID_DN> T2MidDn;
-typedef Tile2<LMOE_T2SMALL_GV> T2SmallGV;
-typedef Tile2<LMOE_T2SMALL_DN> T2SmallDn;
+typedef LMOE_T_DENSE T2Dense;
+typedef LMOE_T_THIN T2Thin;
+typedef LMOE_T_EXPERT_GV T2ExpertGV;
+typedef LMOE_T_EXPERT_DN T2ExpertDn;
+typedef LMOE_T_MID_GV T2MidGV;
+typedef LMOE_T_MID_DN T2MidDn;
+typedef LMOE_T_SMALL_GV T2SmallGV;
+typedef LMOE_T_SMALL_DN T2SmallDn;
 static_assert(T2ExpertGV::BT == T2ExpertDn::BT && T2MidGV::BT == T2MidDn::BT && T2SmallGV::BT == T2SmallDn::BT,
               "expert GEMMs of one size class share the token tile");
 
@@ -112,7 +112,13 @@ static_assert(T2ExpertGV::BT == T2ExpertDn::BT && T2MidGV::BT == T2MidDn::BT && 
 #define LMOE_X_AUX 0
 #endif
 
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// XOR swizzle of the 16-byte chunks of an LDS row (0: none, 1: (r >> 1) & 7,
+// 2: r & 7).  DMA writes are contiguous whatever the choice; it only moves
+// the fragment reads between banks.
+#ifndef LMOE_SWZ
+#define LMOE_SWZ 1
+#endif
+__device__ __forceinline__ int swz(int r) { return LMOE_SWZ == 1 ? ((r >> 1) & 7) : LMOE_SWZ == 2 ? (r & 7) : 0; }
 
 // 16 bytes per lane from `g` into LDS at `lds` + 16 * lane (lds wave-uniform).
 // A __device__ function, not a lambda: lambdas are also compiled for the host,
@@ -127,6 +133,37 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// One k-tile (64 bf16 of K) of a wave's FI x TI block of 32x32 MFMAs, from
+// the swizzled LDS stage (W rows at sW, token rows at sX).  Fragments are
+// double-buffered across the four 16-wide k-steps so the LDS reads of step
+// ks+1 overlap the MFMAs of step ks; no per-block predicates, so the MFMA
+// sequence is straight-line code.
+template <int FI, int TI>
+__device__ __forceinline__ void mma_ktile(f32x16 (&acc)[FI][TI], const char* sW, const char* sX, int wf0, int wt0,
+                                          int lane) {
+  const int lr = lane & 31;
+  const int sw = swz(lr);  // fragment row offsets are multiples of 32
+  const char* pw = sW + (wf0 + lr) * 128;
+  const char* px = sX + (wt0 + lr) * 128;
+  bf16x8 a[2][FI], b[2][TI];
+  auto load = [&](int ks, int buf) {
+    const int ch = ((2 * ks + (lane >> 5)) ^ sw) << 4;
+#pragma unroll
+    for (int i = 0; i < FI; ++i) a[buf][i] = *reinterpret_cast<const bf16x8*>(pw + i * 32 * 128 + ch);
+#pragma unroll
+    for (int j = 0; j < TI; ++j) b[buf][j] = *reinterpret_cast<const bf16x8*>(px + j * 32 * 128 + ch);
+  };
+  load(0, 0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks + 1 < 4) load(ks + 1, (ks + 1) & 1);
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < TI; ++j) acc[i][j] = mfma32(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
+  }
+}
+
 template <class Cfg, class Prob>
 __global__ __launch_bounds__(Cfg::NT) void gemm2_kernel(const Prob p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -134,17 +171,13 @@ __global__ __launch_bounds__(Cfg::NT) void gemm2_kernel(const Prob p) {
   if (!p.setup(blockIdx.x, st)) return;
 
   constexpr int FI = Cfg::FI, TI = Cfg::TI, NQ = Cfg::NQ, S = Cfg::STAGES, NW = Cfg::NW;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wf0 = (wid % Cfg::WF) * Cfg::FW;
   const int wt0 = (wid / Cfg::WF) * Cfg::TW;
 
-  const int tvalid = p.tokens_valid(st);
-  const int fvalid = p.feats_valid(st);
-  bool tok[TI], fea[FI];
-#pragma unroll
-  for (int i = 0; i < TI; ++i) tok[i] = wt0 + i * 32 < tvalid;
-#pragma unroll
-  for (int i = 0; i < FI; ++i) fea[i] = wf0 + i * 32 < fvalid;
+  // a wave whose token or feature slab lies wholly past the end skips its MFMAs
+  const bool active = wt0 < p.tokens_valid(st) && wf0 < p.feats_valid(st);
 
   f32x16 acc[FI][TI];
 #pragma unroll
@@ -201,25 +234,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm2_kernel(const Prob p) {
   };
 
   // ---- compute side ----
-  const int lr = lane & 31;
-  const int sw = swz(lr);  // row offsets of fragments are multiples of 32
   auto compute = [&](int buf) {
     const char* sW = smem + buf * Cfg::STAGE_BYTES;
-    const char* sX = sW + Cfg::BF * 128;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int ch = ((2 * ks + (lane >> 5)) ^ sw) << 4;
-      bf16x8 a[FI], b[TI];
-#pragma unroll
-      for (int i = 0; i < FI; ++i) a[i] = *reinterpret_cast<const bf16x8*>(sW + (wf0 + i * 32 + lr) * 128 + ch);
-#pragma unroll
-      for (int j = 0; j < TI; ++j) b[j] = *reinterpret_cast<const bf16x8*>(sX + (wt0 + j * 32 + lr) * 128 + ch);
-#pragma unroll
-      for (int i = 0; i < FI; ++i)
-#pragma unroll
-        for (int j = 0; j < TI; ++j)
-          if (fea[i] && tok[j]) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
-    }
+    if (active) mma_ktile<FI, TI>(acc, sW, sW + Cfg::BF * 128, wf0, wt0, lane);
   };
 
 #pragma unroll
@@ -258,17 +275,13 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3_kernel(const Prob p) {
   if (!p.setup(blockIdx.x, st)) return;
 
   constexpr int FI = Cfg::FI, TI = Cfg::TI, NQW = Cfg::NQW, NQX = Cfg::NQX, NW = Cfg::NW;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wf0 = (wid % Cfg::WF) * Cfg::FW;
   const int wt0 = (wid / Cfg::WF) * Cfg::TW;
 
-  const int tvalid = p.tokens_valid(st);
-  const int fvalid = p.feats_valid(st);
-  bool tok[TI], fea[FI];
-#pragma unroll
-  for (int i = 0; i < TI; ++i) tok[i] = wt0 + i * 32 < tvalid;
-#pragma unroll
-  for (int i = 0; i < FI; ++i) fea[i] = wf0 + i * 32 < fvalid;
+  // a wave whose token or feature slab lies wholly past the end skips its MFMAs
+  const bool active = wt0 < p.tokens_valid(st) && wf0 < p.feats_valid(st);
 
   f32x16 acc[FI][TI];
 #pragma unroll
@@ -332,25 +345,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3_kernel(const Prob p) {
     }
   };
 
-  const int lr = lane & 31;
-  const int sw = swz(lr);
   auto compute = [&](int wbuf, int xbuf) {
-    const char* sW = smem + wbuf * Cfg::BF * 128;
-    const char* sX = smem + Cfg::X_OFF + xbuf * Cfg::BT * 128;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int ch = ((2 * ks + (lane >> 5)) ^ sw) << 4;
-      bf16x8 a[FI], b[TI];
-#pragma unroll
-      for (int i = 0; i < FI; ++i) a[i] = *reinterpret_cast<const bf16x8*>(sW + (wf0 + i * 32 + lr) * 128 + ch);
-#pragma unroll
-      for (int j = 0; j < TI; ++j) b[j] = *reinterpret_cast<const bf16x8*>(sX + (wt0 + j * 32 + lr) * 128 + ch);
-#pragma unroll
-      for (int i = 0; i < FI; ++i)
-#pragma unroll
-        for (int j = 0; j < TI; ++j)
-          if (fea[i] && tok[j]) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
-    }
+    if (active)
+      mma_ktile<FI, TI>(acc, smem + wbuf * Cfg::BF * 128, smem + Cfg::X_OFF + xbuf * Cfg::BT * 128, wf0, wt0, lane);
   };
 
   if (nkt > 0) {

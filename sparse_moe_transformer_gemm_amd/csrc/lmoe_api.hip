@@ -185,12 +185,9 @@ template <class Cfg, typename CT, class Prob>
 hipError_t launch_gemm(const Prob& p, int64_t grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   void (*kern)(const Prob);
-  if constexpr (Cfg::kDma) {
-    if constexpr (Cfg::kSplit) kern = gemm3_kernel<Cfg, Prob>;
-    else kern = gemm2_kernel<Cfg, Prob>;
-  } else {
-    kern = gemm_kernel<Cfg, CT, Prob>;
-  }
+  if constexpr (Cfg::kKind == 3) kern = gemm3_kernel<Cfg, Prob>;
+  else if constexpr (Cfg::kKind == 2) kern = gemm2_kernel<Cfg, Prob>;
+  else kern = gemm_kernel<Cfg, CT, Prob>;
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [&] {
