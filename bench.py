@@ -13,6 +13,9 @@ oracle timed on a bounded sample of the same workload.
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -24,6 +27,19 @@ sys.path.insert(0, ROOT)
 METRIC = "latent-MoE layer tokens/s at T=8192 bf16 (% MFMA peak); T=64 decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (about 2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+CSRC = os.path.join(ROOT, "sparse_moe_transformer_gemm_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+GV_KERNEL = "ExpertGVProb"  # substring of the expert gate/value GEMM kernel name
+
+
+def source_hash():
+    """Hash of the kernel sources: counter-based traffic figures are only
+    reported while the kernels they were taken on are unchanged."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -36,7 +52,70 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--cpu-sample", type=int, default=48, help="tokens the oracle runs for cpu_baseline (0: skip)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run one device-to-device copy of BYTES (PMC calibration) and exit")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs of the layer and of the copy "
+                         "calibration into profiles/traffic_<workload>.json, then exit")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     return ap.parse_args()
+
+
+def calibrate_copy(nbytes):
+    """One elementwise kernel that reads and writes `nbytes` each (fp32
+    negation), so the HBM counters can be scaled to bytes."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def _counter_means(path):
+    """{kernel name: {counter: mean over dispatches}} from a counter_collection.csv."""
+    acc = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            d = acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], [])
+            d.append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def summarize_pmc(a):
+    fetch, write, cfetch, cwrite = (_counter_means(p) for p in a.summarize_pmc)
+    # the calibration run holds one copy kernel (the largest dispatch)
+    cf = max(v.get("FETCH_SIZE", 0) for v in cfetch.values())
+    cw = max(v.get("WRITE_SIZE", 0) for v in cwrite.values())
+    f_scale, w_scale = a.copy_bytes / cf, a.copy_bytes / cw
+    out = {"workload": a.workload, "source_hash": source_hash(),
+           "copy_calibration": {"bytes": a.copy_bytes, "FETCH_SIZE": cf, "WRITE_SIZE": cw,
+                                "bytes_per_fetch_unit": f_scale, "bytes_per_write_unit": w_scale},
+           "kernels": {}}
+    for name, tag in (("expert_gate_value", "ExpertGVProb"), ("expert_down", "ExpertDownProb"),
+                      ("route_gemm", "DenseXProb"), ("up", "UpProb"), ("combine_norm", "combine_norm")):
+        fk = [v["FETCH_SIZE"] for k, v in fetch.items() if tag in k and "FETCH_SIZE" in v]
+        wk = [v["WRITE_SIZE"] for k, v in write.items() if tag in k and "WRITE_SIZE" in v]
+        if fk and wk:
+            out["kernels"][name] = {"fetch_bytes": max(fk) * f_scale, "write_bytes": max(wk) * w_scale,
+                                    "FETCH_SIZE": max(fk), "WRITE_SIZE": max(wk)}
+    path = os.path.join(PROFILES, f"traffic_{a.workload}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(path)
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when absent or taken on other kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != source_hash() or kernel not in t.get("kernels", {}):
+        return None
+    k = t["kernels"][kernel]
+    return k["fetch_bytes"] + k["write_bytes"]
 
 
 def timed_loop(lmoe, sh, w, x, y, idx, tw, ws, steps, warmup, per_stage):
@@ -63,6 +142,9 @@ def timed_loop(lmoe, sh, w, x, y, idx, tw, ws, steps, warmup, per_stage):
 
 def main():
     a = parse()
+    if a.summarize_pmc:
+        summarize_pmc(a)
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): the layer is measured on a single "
               f"MI355X; multi-GPU sharding is not built.", file=sys.stderr)
@@ -78,6 +160,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if a.calibrate_copy:
+        calibrate_copy(a.calibrate_copy)
+        return
     lmoe.load_library()
     dev = torch.device("cuda:0")
     cfg = get_config(a.workload)
@@ -141,7 +226,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(gv_gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(cfg.name, "expert_gate_value"),
             "bytes_per_launch": gv_bytes,
             "avg_ms": round(gv_ms, 4),
         },
