@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--cpu-sample", type=int, default=48, help="tokens the oracle runs for cpu_baseline (0: skip)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--pack", action="store_true",
+                    help="pack the routed expert weights once (lmoe_pack_experts) and time the layer on them")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES (PMC calibration) and exit")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -170,6 +172,12 @@ def main():
     g = make_inputs(cfg, device=dev)
     sh = lmoe.shape_of(cfg)
     w = lmoe.make_weights(sh, g)
+    # one-time layout change of the routed expert weights (outside any timing)
+    packed = None
+    if a.pack and lmoe.packed_bytes(sh) > 0:
+        packed = lmoe.pack_experts(sh, w)
+        w = lmoe.with_packed(sh, w, packed)
+        torch.cuda.synchronize()
     x = g["x"]
     T = cfg.T
     y = torch.empty((T, cfg.H), dtype=x.dtype, device=dev)
@@ -212,6 +220,7 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, K3 layer shape)",
         "config": {"workload": cfg.name, "T": T, "H": cfg.H, "L": cfg.L, "E": cfg.E, "k": cfg.k, "I": cfg.I,
                    "S": cfg.S, "Is": cfg.Is, "act": cfg.act, "w_expert": cfg.w_expert,
+                   "expert_weights": "packed" if packed is not None else "row-major",
                    "parallelism": "single GPU"},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),

@@ -116,6 +116,11 @@ typedef struct {
   const void *ws_value;   /* [S, Is, H]                                         */
   const void *ws_out;     /* [S, H, Is]                                         */
   const float *ss_gate, *ss_value, *ss_out;
+  const void *packed;     /* NULL, or the routed expert weights in the packed
+                             layout of lmoe_pack_experts (BF16 layers with BF16
+                             expert weights); when set, the expert GEMMs read
+                             it instead of w_gate / w_value / w_out, which may
+                             then be NULL                                       */
 } lmoe_weights;
 
 /* Host-only argument check (no GPU call): the checks every entry point runs
@@ -181,6 +186,30 @@ lmoe_status lmoe_combine_norm(const lmoe_shape *shape, const void *expert_out, c
  * the shared experts at full width on x[T, H], weight 1; n is [T, L].           */
 lmoe_status lmoe_up(const lmoe_shape *shape, const lmoe_weights *w, const void *n, const void *x,
                     void *y, void *ws, size_t ws_bytes, void *stream);
+
+/* Packed routed-expert weights.  The expert GEMMs stream each 256-row by
+ * 64-column tile of an expert matrix as one contiguous 32 KB block laid out
+ * exactly as they stage it in on-chip memory, so every load is a dense 1 KB
+ * run instead of 256 scattered 128-byte row pieces.  Layout (bf16, one block =
+ * 256 rows x 128 bytes, row r's 16-byte chunk c stored at chunk position
+ * c ^ ((r >> 1) & 7)):
+ *   gate/value part: block (e, f, kt) for e < E, f < ceil(I / 128), kt < L / 64
+ *     at index (e * ceil(I/128) + f) * (L/64) + kt; block row r holds k-columns
+ *     64 kt .. 64 kt + 63 of gate row u (r mod 64 < 32) or value row u
+ *     (r mod 64 >= 32) of expert e, u = 128 f + 32 (r / 64) + (r mod 32);
+ *     rows with u >= I are zero;
+ *   out part (after the gate/value part): block (e, f, kt) for f < ceil(L/256),
+ *     kt < I / 64 at index (e * ceil(L/256) + f) * (I/64) + kt; block row r holds
+ *     k-columns 64 kt .. 64 kt + 63 of out row 256 f + r of expert e (zero past L).
+ * lmoe_packed_bytes returns the size (0 when the shape has no packed form:
+ * an invalid shape, or one that is not BF16 with BF16 expert weights).
+ * lmoe_pack_experts fills `packed` (device memory, 256-byte aligned, at least
+ * lmoe_packed_bytes bytes) from w_gate / w_value / w_out on `stream`; it is a
+ * one-time layout change of the weights, after which w->packed may point at
+ * the buffer for every call of the layer.                                      */
+size_t lmoe_packed_bytes(const lmoe_shape *shape);
+lmoe_status lmoe_pack_experts(const lmoe_shape *shape, const lmoe_weights *w, void *packed, size_t bytes,
+                              void *stream);
 
 /* Name of a status code; message of the calling thread's last failure.       */
 const char *lmoe_status_str(lmoe_status s);

@@ -17,6 +17,10 @@ enum Dtype : int { DT_F32 = 0, DT_BF16 = 1, DT_F8 = 2 };
 
 constexpr int kWave = 64;
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, WGs dealt round-robin
+// Packed expert weights: one block = 256 rows x 64 bf16 columns (32 KB), the
+// on-chip image of one weight tile of the expert GEMMs.
+constexpr int kPackRows = 256;
+constexpr int kPackBlock = kPackRows * 128;
 
 __host__ __device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
 

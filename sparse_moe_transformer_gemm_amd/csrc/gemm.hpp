@@ -146,6 +146,7 @@ struct DenseXProb {
     if (s.f8) *scrow = sb + (int64_t)(u >> 7) * (K >> 7);
     return base + (int64_t)u * K * wes;
   }
+  __device__ const char* w_block(const State&) const { return nullptr; }
   template <class Acc>
   __device__ __forceinline__ void epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const;
 };
@@ -208,6 +209,7 @@ struct UpProb {
     }
     return q.w + (int64_t)f * q.ldw * (int64_t)sizeof(CT);
   }
+  __device__ const char* w_block(const State&) const { return nullptr; }
   template <class Acc>
   __device__ __forceinline__ void epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const;
 };
@@ -258,6 +260,7 @@ struct ExpertGVProb {
   const float* sg;    // [E, I/128, L/128]
   const float* sv;
   char* act;          // [T*k, I]
+  const char* wpk;    // packed gate/value blocks (see lmoe_pack_experts) or NULL
   int I, L, k, f8;
   float cap, inv_cap;
 
@@ -283,6 +286,11 @@ struct ExpertGVProb {
     if (f8) *scrow = (val ? sv : sg) + ((int64_t)st.e * (I >> 7) + (u >> 7)) * (L >> 7);
     return (val ? wv : wg) + off;
   }
+  // k-tile 0 block of this tile in the packed layout (k-tile kt at + kt * 32 KB)
+  __device__ const char* w_block(const State& st) const {
+    if (!wpk) return nullptr;
+    return wpk + ((int64_t)st.e * et.nft + st.ft) * (int64_t)(L / 64) * kPackBlock;
+  }
   template <class Acc>
   __device__ __forceinline__ void epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const;
 };
@@ -294,6 +302,7 @@ struct ExpertDownProb {
   const char* wo;     // [E, L, I]
   const float* so;    // [E, L/128, I/128]
   char* out;          // [T*k, L]
+  const char* wpk;    // packed out blocks (see lmoe_pack_experts) or NULL
   int I, L, f8;
 
   typedef ExpertState State;
@@ -313,6 +322,10 @@ struct ExpertDownProb {
     const int64_t wes = f8 ? 1 : sizeof(CT);
     if (f8) *scrow = so + ((int64_t)st.e * (L >> 7) + (f >> 7)) * (I >> 7);
     return wo + ((int64_t)st.e * L + f) * I * wes;
+  }
+  __device__ const char* w_block(const State& st) const {
+    if (!wpk) return nullptr;
+    return wpk + ((int64_t)st.e * et.nft + st.ft) * (int64_t)(I / 64) * kPackBlock;
   }
   template <class Acc>
   __device__ __forceinline__ void epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const;

@@ -107,6 +107,9 @@ typedef LMOE_T_SMALL_GV T2SmallGV;
 typedef LMOE_T_SMALL_DN T2SmallDn;
 static_assert(T2ExpertGV::BT == T2ExpertDn::BT && T2MidGV::BT == T2MidDn::BT && T2SmallGV::BT == T2SmallDn::BT,
               "expert GEMMs of one size class share the token tile");
+static_assert(T2ExpertGV::BF == kPackRows && T2ExpertDn::BF == kPackRows && T2MidGV::BF == kPackRows &&
+                  T2MidDn::BF == kPackRows && T2SmallGV::BF == kPackRows && T2SmallDn::BF == kPackRows,
+              "every bf16 expert tile reads whole packed weight blocks");
 
 #ifndef LMOE_X_AUX
 #define LMOE_X_AUX 0
@@ -128,6 +131,45 @@ __device__ __forceinline__ void dma16(const char* g, char* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, AUX);
 }
 
+// Packs the routed expert weights into 32 KB blocks, each the LDS image of
+// one 256-row weight tile at one 64-column k-tile (layout at
+// lmoe_pack_experts).  One work-group per block; thread t writes chunks t,
+// t + 256, ... (coalesced 16-byte stores), and the 8 chunks of a row come
+// from one 128-byte run of the source row.  Rows past I (gate/value) or L
+// (out) are zero.
+__global__ __launch_bounds__(256) void pack_experts_kernel(const char* wg, const char* wv, const char* wo, char* dst,
+                                                          int E, int I, int L) {
+  const int64_t nft_gv = (I + 127) / 128, nkt_gv = L / 64;
+  const int64_t nft_dn = (L + 255) / 256, nkt_dn = I / 64;
+  const int64_t gv_blocks = (int64_t)E * nft_gv * nkt_gv;
+  const int64_t b = blockIdx.x;
+  const bool gv = b < gv_blocks;
+  int64_t rem = gv ? b : b - gv_blocks;
+  const int64_t nkt = gv ? nkt_gv : nkt_dn, nft = gv ? nft_gv : nft_dn;
+  const int kt = (int)(rem % nkt);
+  rem /= nkt;
+  const int ft = (int)(rem % nft);
+  const int64_t e = rem / nft;
+  char* out = dst + b * kPackBlock;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = threadIdx.x + 256 * j;  // chunk 0 .. 2047 of the block
+    const int r = c >> 3, ch = (c & 7) ^ swz(r);
+    const char* src = nullptr;
+    if (gv) {
+      const int m = r & 63;
+      const int u = ft * 128 + (r >> 6) * 32 + (m & 31);
+      if (u < I) src = (m >= 32 ? wv : wg) + ((e * I + u) * L + kt * 64 + ch * 8) * 2;
+    } else {
+      const int f = ft * 256 + r;
+      if (f < L) src = wo + ((e * L + f) * I + kt * 64 + ch * 8) * 2;
+    }
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (src) v = *reinterpret_cast<const uint4*>(src);
+    *reinterpret_cast<uint4*>(out + c * 16) = v;
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
@@ -136,31 +178,37 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
 // One k-tile (64 bf16 of K) of a wave's FI x TI block of 32x32 MFMAs, from
 // the swizzled LDS stage (W rows at sW, token rows at sX).  Fragments are
 // double-buffered across the four 16-wide k-steps so the LDS reads of step
-// ks+1 overlap the MFMAs of step ks; no per-block predicates, so the MFMA
-// sequence is straight-line code.
+// ks+1 overlap the MFMAs of step ks.  Token blocks j >= tiv (rows all past
+// the valid ones) are skipped, loads and MFMAs alike; the test is uniform
+// across the wave.  (A branch-free variant of this loop for full tiles was
+// measured to run the 256x256 dense GEMMs about 3x slower on MI355X, and to
+// slow the kernels launched after them, so it is not used.)
 template <int FI, int TI>
 __device__ __forceinline__ void mma_ktile(f32x16 (&acc)[FI][TI], const char* sW, const char* sX, int wf0, int wt0,
-                                          int lane) {
+                                          int lane, int tiv) {
   const int lr = lane & 31;
   const int sw = swz(lr);  // fragment row offsets are multiples of 32
   const char* pw = sW + (wf0 + lr) * 128;
   const char* px = sX + (wt0 + lr) * 128;
   bf16x8 a[2][FI], b[2][TI];
-  auto load = [&](int ks, int buf) {
+  auto load = [&](int ks, int buf) __attribute__((always_inline)) {
     const int ch = ((2 * ks + (lane >> 5)) ^ sw) << 4;
 #pragma unroll
     for (int i = 0; i < FI; ++i) a[buf][i] = *reinterpret_cast<const bf16x8*>(pw + i * 32 * 128 + ch);
 #pragma unroll
-    for (int j = 0; j < TI; ++j) b[buf][j] = *reinterpret_cast<const bf16x8*>(px + j * 32 * 128 + ch);
+    for (int j = 0; j < TI; ++j)
+      if (j < tiv) b[buf][j] = *reinterpret_cast<const bf16x8*>(px + j * 32 * 128 + ch);
   };
   load(0, 0);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     if (ks + 1 < 4) load(ks + 1, (ks + 1) & 1);
 #pragma unroll
-    for (int i = 0; i < FI; ++i)
+    for (int j = 0; j < TI; ++j)
+      if (j < tiv) {
 #pragma unroll
-      for (int j = 0; j < TI; ++j) acc[i][j] = mfma32(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
+        for (int i = 0; i < FI; ++i) acc[i][j] = mfma32(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
+      }
   }
 }
 
@@ -176,8 +224,10 @@ __global__ __launch_bounds__(Cfg::NT) void gemm2_kernel(const Prob p) {
   const int wf0 = (wid % Cfg::WF) * Cfg::FW;
   const int wt0 = (wid / Cfg::WF) * Cfg::TW;
 
-  // a wave whose token or feature slab lies wholly past the end skips its MFMAs
-  const bool active = wt0 < p.tokens_valid(st) && wf0 < p.feats_valid(st);
+  // token blocks of this wave holding valid rows; a wave with none, or whose
+  // feature slab lies wholly past the end, skips its MFMAs
+  const int tiv = min(TI, max(0, (p.tokens_valid(st) - wt0 + 31) >> 5));
+  const bool active = tiv > 0 && wf0 < p.feats_valid(st);
 
   f32x16 acc[FI][TI];
 #pragma unroll
@@ -196,34 +246,38 @@ __global__ __launch_bounds__(Cfg::NT) void gemm2_kernel(const Prob p) {
   int is = 0, ik = 0;
   while (is < nks && p.seg_ktiles(is) == 0) ++is;
   const char* src[NQ];
-  auto set_src = [&](int s) {
+  const char* wblk = p.w_block(st);
+  const int64_t wstep = wblk ? kPackBlock : 128;
+  auto set_src = [&](int s) __attribute__((always_inline)) {
     const float* dummy = nullptr;
     const char* w0 = p.w_row(st, s, 0, &dummy);
     const char* x0 = p.x_row(st, s, 0);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int q = wid + NW * i;  // uniform per wave
-      const char* rp;
       int row;
       if (q < Cfg::QW) {
         row = q * 8 + (lane >> 3);
-        rp = p.w_row(st, s, row, &dummy);
-        if (!rp) rp = w0;
+        if (wblk) {
+          src[i] = wblk + q * 1024 + lane * 16;
+        } else {
+          const char* rp = p.w_row(st, s, row, &dummy);
+          src[i] = (rp ? rp : w0) + (((lane & 7) ^ swz(row)) << 4);
+        }
       } else {
         row = (q - Cfg::QW) * 8 + (lane >> 3);
-        rp = p.x_row(st, s, row);
-        if (!rp) rp = x0;
+        const char* rp = p.x_row(st, s, row);
+        src[i] = (rp ? rp : x0) + (((lane & 7) ^ swz(row)) << 4);
       }
-      src[i] = rp + (((lane & 7) ^ swz(row)) << 4);
     }
   };
   if (is < nks) set_src(is);
-  auto issue = [&](int buf) {
+  auto issue = [&](int buf) __attribute__((always_inline)) {
     char* base = smem + buf * Cfg::STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int q = wid + NW * i;
-      if (q < Cfg::QW) dma16<Cfg::WAUX>(src[i] + (int64_t)ik * 128, base + q * 1024);
+      if (q < Cfg::QW) dma16<Cfg::WAUX>(src[i] + ik * wstep, base + q * 1024);
       else dma16<LMOE_X_AUX>(src[i] + (int64_t)ik * 128, base + q * 1024);
     }
     if (++ik == p.seg_ktiles(is)) {
@@ -231,12 +285,6 @@ __global__ __launch_bounds__(Cfg::NT) void gemm2_kernel(const Prob p) {
       do { ++is; } while (is < nks && p.seg_ktiles(is) == 0);
       if (is < nks) set_src(is);
     }
-  };
-
-  // ---- compute side ----
-  auto compute = [&](int buf) {
-    const char* sW = smem + buf * Cfg::STAGE_BYTES;
-    if (active) mma_ktile<FI, TI>(acc, sW, sW + Cfg::BF * 128, wf0, wt0, lane);
   };
 
 #pragma unroll
@@ -254,7 +302,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm2_kernel(const Prob p) {
       else wait_vmcnt_barrier<0>();
     }
     if (kt + S - 1 < nkt) issue((kt + S - 1) % S);
-    compute(kt % S);
+    const char* sW = smem + (kt % S) * Cfg::STAGE_BYTES;
+    if (active) mma_ktile<FI, TI>(acc, sW, sW + Cfg::BF * 128, wf0, wt0, lane, tiv);
   }
   p.epilogue(st, acc, wf0, wt0, lane);
 }
@@ -266,7 +315,11 @@ __global__ __launch_bounds__(Cfg::NT) void gemm2_kernel(const Prob p) {
 // order: X(0) W(0) W(1) before the loop, then X(kt+1) W(kt+2) in iteration
 // kt.  At the top of iteration kt the only DMA issued after the newest
 // operand that iteration kt needs (X(kt), or W(0) when kt = 0) is W(kt+1), so
-// the wait is vmcnt(NQW) while W(kt+1) exists and vmcnt(0) after.
+// the wait is vmcnt(NQW) while W(kt+1) exists and vmcnt(0) after.  Token DMA
+// instructions whose 8 rows all lie past the valid ones are not issued: their
+// LDS rows feed only token blocks no wave computes, and since the weight
+// instructions come last in every iteration the waits do not depend on how
+// many token instructions went out.
 // ---------------------------------------------------------------------------
 template <class Cfg, class Prob>
 __global__ __launch_bounds__(Cfg::NT) void gemm3_kernel(const Prob p) {
@@ -280,8 +333,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3_kernel(const Prob p) {
   const int wf0 = (wid % Cfg::WF) * Cfg::FW;
   const int wt0 = (wid / Cfg::WF) * Cfg::TW;
 
-  // a wave whose token or feature slab lies wholly past the end skips its MFMAs
-  const bool active = wt0 < p.tokens_valid(st) && wf0 < p.feats_valid(st);
+  const int xrows = p.tokens_valid(st);
+  const int tiv = min(TI, max(0, (xrows - wt0 + 31) >> 5));
+  const bool active = tiv > 0 && wf0 < p.feats_valid(st);
 
   f32x16 acc[FI][TI];
 #pragma unroll
@@ -301,17 +355,27 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3_kernel(const Prob p) {
   xsg = wsg;
   const char* srcW[NQW];
   const char* srcX[NQX];
-  auto set_w = [&](int s) {
+  bool xon[NQX];
+#pragma unroll
+  for (int i = 0; i < NQX; ++i) xon[i] = (wid + NW * i) * 8 < xrows;
+  const char* wblk = p.w_block(st);
+  const int64_t wstep = wblk ? kPackBlock : 128;
+  auto set_w = [&](int s) __attribute__((always_inline)) {
     const float* dummy = nullptr;
     const char* w0 = p.w_row(st, s, 0, &dummy);
 #pragma unroll
     for (int i = 0; i < NQW; ++i) {
-      const int row = (wid + NW * i) * 8 + (lane >> 3);
-      const char* rp = p.w_row(st, s, row, &dummy);
-      srcW[i] = (rp ? rp : w0) + (((lane & 7) ^ swz(row)) << 4);
+      const int q = wid + NW * i;
+      if (wblk) {
+        srcW[i] = wblk + q * 1024 + lane * 16;
+      } else {
+        const int row = q * 8 + (lane >> 3);
+        const char* rp = p.w_row(st, s, row, &dummy);
+        srcW[i] = (rp ? rp : w0) + (((lane & 7) ^ swz(row)) << 4);
+      }
     }
   };
-  auto set_x = [&](int s) {
+  auto set_x = [&](int s) __attribute__((always_inline)) {
     const char* x0 = p.x_row(st, s, 0);
 #pragma unroll
     for (int i = 0; i < NQX; ++i) {
@@ -324,30 +388,26 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3_kernel(const Prob p) {
     set_w(wsg);
     set_x(xsg);
   }
-  auto issue_w = [&](int buf) {
+  auto issue_w = [&](int buf) __attribute__((always_inline)) {
     char* base = smem + buf * Cfg::BF * 128;
 #pragma unroll
-    for (int i = 0; i < NQW; ++i) dma16<Cfg::WAUX>(srcW[i] + (int64_t)wk * 128, base + (wid + NW * i) * 1024);
+    for (int i = 0; i < NQW; ++i) dma16<Cfg::WAUX>(srcW[i] + wk * wstep, base + (wid + NW * i) * 1024);
     if (++wk == p.seg_ktiles(wsg)) {
       wk = 0;
       do { ++wsg; } while (wsg < nks && p.seg_ktiles(wsg) == 0);
       if (wsg < nks) set_w(wsg);
     }
   };
-  auto issue_x = [&](int buf) {
+  auto issue_x = [&](int buf) __attribute__((always_inline)) {
     char* base = smem + Cfg::X_OFF + buf * Cfg::BT * 128;
 #pragma unroll
-    for (int i = 0; i < NQX; ++i) dma16<LMOE_X_AUX>(srcX[i] + (int64_t)xk * 128, base + (wid + NW * i) * 1024);
+    for (int i = 0; i < NQX; ++i)
+      if (xon[i]) dma16<LMOE_X_AUX>(srcX[i] + (int64_t)xk * 128, base + (wid + NW * i) * 1024);
     if (++xk == p.seg_ktiles(xsg)) {
       xk = 0;
       do { ++xsg; } while (xsg < nks && p.seg_ktiles(xsg) == 0);
       if (xsg < nks) set_x(xsg);
     }
-  };
-
-  auto compute = [&](int wbuf, int xbuf) {
-    if (active)
-      mma_ktile<FI, TI>(acc, smem + wbuf * Cfg::BF * 128, smem + Cfg::X_OFF + xbuf * Cfg::BT * 128, wf0, wt0, lane);
   };
 
   if (nkt > 0) {
@@ -360,7 +420,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3_kernel(const Prob p) {
     else wait_vmcnt_barrier<0>();
     if (kt + 1 < nkt) issue_x((kt + 1) & 1);
     if (kt + 2 < nkt) issue_w((kt + 2) % 3);
-    compute(kt % 3, kt & 1);
+    if (active)
+      mma_ktile<FI, TI>(acc, smem + (kt % 3) * Cfg::BF * 128, smem + Cfg::X_OFF + (kt & 1) * Cfg::BT * 128, wf0, wt0,
+                        lane, tiv);
   }
   p.epilogue(st, acc, wf0, wt0, lane);
 }

@@ -81,8 +81,15 @@ lmoe_status check_weights(const lmoe_shape* sh, const lmoe_weights* w, unsigned 
     if (!w->w_down && sh->L != sh->H) return fail(LMOE_EINVAL, "w_down = NULL needs L == H");
   }
   if (need & NEED_EXPERT) {
-    if (!w->w_gate || !w->w_value || !w->w_out) return fail(LMOE_EINVAL, "expert weights are required");
-    if (f8 && (!w->s_gate || !w->s_value || !w->s_out)) return fail(LMOE_EINVAL, "e4m3 expert scales are required");
+    if (w->packed) {
+      if (!(sh->act == LMOE_BF16 && sh->w_expert == LMOE_BF16))
+        return fail(LMOE_EUNSUPPORTED, "packed expert weights need a BF16 layer with BF16 expert weights");
+      if (reinterpret_cast<uintptr_t>(w->packed) & 255) return fail(LMOE_EINVAL, "packed must be 256-byte aligned");
+    } else {
+      if (!w->w_gate || !w->w_value || !w->w_out) return fail(LMOE_EINVAL, "expert weights are required");
+      if (f8 && (!w->s_gate || !w->s_value || !w->s_out))
+        return fail(LMOE_EINVAL, "e4m3 expert scales are required");
+    }
   }
   if (need & NEED_NORM) {
     if (!w->gamma) return fail(LMOE_EINVAL, "gamma is required");
@@ -202,10 +209,18 @@ hipError_t launch_gemm(const Prob& p, int64_t grid, hipStream_t st) {
 int64_t pad8(int64_t v) { return (v + kXcds - 1) / kXcds * kXcds; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Packed expert weights: gate/value blocks, then out blocks (32 KB each).
+int64_t packed_gv_blocks(const lmoe_shape* sh) { return (int64_t)sh->E * cdiv(sh->I, 128) * (sh->L / 64); }
+int64_t packed_dn_blocks(const lmoe_shape* sh) { return (int64_t)sh->E * cdiv(sh->L, kPackRows) * (sh->I / 64); }
+
 struct Ctx {
   const lmoe_shape* sh;
   const lmoe_weights* w;
   hipStream_t st;
+  const char* pk_gv() const { return static_cast<const char*>(w->packed); }
+  const char* pk_dn() const {
+    return w->packed ? static_cast<const char*>(w->packed) + packed_gv_blocks(sh) * kPackBlock : nullptr;
+  }
   size_t es() const { return sh->act == LMOE_BF16 ? 2 : 4; }
   size_t wes() const { return sh->w_expert == LMOE_F8E4M3 ? 1 : es(); }
   float inv_cap() const { return isinf(sh->cap) ? 0.f : 1.f / sh->cap; }
@@ -328,6 +343,7 @@ hipError_t expert_gv(const Ctx& c, const void* z, const int32_t* offsets, const 
   p.sg = c.w->s_gate;
   p.sv = c.w->s_value;
   p.act = static_cast<char*>(act);
+  if constexpr (Cfg::kDma && Cfg::BF == kPackRows) p.wpk = c.pk_gv();
   p.I = sh->I;
   p.L = sh->L;
   p.k = sh->k;
@@ -350,6 +366,7 @@ hipError_t expert_down(const Ctx& c, const void* act, const int32_t* offsets, co
   p.wo = static_cast<const char*>(c.w->w_out);
   p.so = c.w->s_out;
   p.out = static_cast<char*>(out);
+  if constexpr (Cfg::kDma && Cfg::BF == kPackRows) p.wpk = c.pk_dn();
   p.I = sh->I;
   p.L = sh->L;
   p.f8 = is_f8(sh);
@@ -583,6 +600,31 @@ lmoe_status lmoe_forward(const lmoe_shape* sh, const lmoe_weights* w, const void
   if (lmoe_status s = record(ev, 6, c.st)) return s;
   LMOE_HIP(bf ? upgemm_any<bf16>(c, n, hs, y) : upgemm_any<float>(c, n, hs, y), "up GEMM");
   if (lmoe_status s = record(ev, 7, c.st)) return s;
+  return LMOE_OK;
+}
+
+size_t lmoe_packed_bytes(const lmoe_shape* sh) {
+  if (check_shape(sh) != LMOE_OK) return 0;
+  if (!(sh->act == LMOE_BF16 && sh->w_expert == LMOE_BF16)) return 0;
+  return (size_t)(packed_gv_blocks(sh) + packed_dn_blocks(sh)) * kPackBlock;
+}
+
+lmoe_status lmoe_pack_experts(const lmoe_shape* sh, const lmoe_weights* w, void* packed, size_t bytes, void* stream) {
+  g_err[0] = 0;
+  if (lmoe_status s = check_shape(sh)) return s;
+  if (!(sh->act == LMOE_BF16 && sh->w_expert == LMOE_BF16))
+    return fail(LMOE_EUNSUPPORTED, "packed expert weights need a BF16 layer with BF16 expert weights");
+  if (!w || !w->w_gate || !w->w_value || !w->w_out) return fail(LMOE_EINVAL, "w_gate, w_value and w_out are required");
+  if (!packed) return fail(LMOE_EINVAL, "packed is NULL");
+  if (reinterpret_cast<uintptr_t>(packed) & 255) return fail(LMOE_EINVAL, "packed must be 256-byte aligned");
+  const size_t need = lmoe_packed_bytes(sh);
+  if (bytes < need) return fail(LMOE_EINVAL, "packed buffer of %zu bytes, %zu needed", bytes, need);
+  const int64_t blocks = packed_gv_blocks(sh) + packed_dn_blocks(sh);
+  if (blocks >= (int64_t(1) << 31)) return fail(LMOE_EUNSUPPORTED, "too many packed blocks");
+  hipLaunchKernelGGL(pack_experts_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const char*>(w->w_gate), static_cast<const char*>(w->w_value),
+                     static_cast<const char*>(w->w_out), static_cast<char*>(packed), sh->E, sh->I, sh->L);
+  LMOE_HIP(hipGetLastError(), "pack experts");
   return LMOE_OK;
 }
 

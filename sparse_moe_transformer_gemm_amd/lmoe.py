@@ -23,7 +23,8 @@ DTYPE_CODE = {"f32": F32, "bf16": BF16, "f8": F8E4M3}
 _TORCH = {F32: torch.float32, BF16: torch.bfloat16, F8E4M3: torch.float8_e4m3fn}
 
 EXPORTS = ("lmoe_validate", "lmoe_workspace_bytes", "lmoe_forward", "lmoe_route", "lmoe_permute",
-           "lmoe_expert_gemm", "lmoe_combine_norm", "lmoe_up", "lmoe_status_str", "lmoe_last_error")
+           "lmoe_expert_gemm", "lmoe_combine_norm", "lmoe_up", "lmoe_packed_bytes", "lmoe_pack_experts",
+           "lmoe_status_str", "lmoe_last_error")
 
 
 class LmoeError(RuntimeError):
@@ -40,7 +41,7 @@ class Shape(ctypes.Structure):
 
 
 _WEIGHT_FIELDS = ("w_router", "b_router", "w_down", "w_gate", "w_value", "w_out", "s_gate", "s_value", "s_out",
-                  "gamma", "w_up", "ws_gate", "ws_value", "ws_out", "ss_gate", "ss_value", "ss_out")
+                  "gamma", "w_up", "ws_gate", "ws_value", "ws_out", "ss_gate", "ss_value", "ss_out", "packed")
 
 
 class Weights(ctypes.Structure):
@@ -70,6 +71,8 @@ def load_library(path: str = LIB_PATH):
         "lmoe_expert_gemm": (ctypes.c_int, [sp, wp, vp, i32p, i32p, vp, vp, sz, vp]),
         "lmoe_combine_norm": (ctypes.c_int, [sp, vp, i32p, f32p, f32p, vp, vp]),
         "lmoe_up": (ctypes.c_int, [sp, wp, vp, vp, vp, vp, sz, vp]),
+        "lmoe_packed_bytes": (sz, [sp]),
+        "lmoe_pack_experts": (ctypes.c_int, [sp, wp, vp, sz, vp]),
         "lmoe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "lmoe_last_error": (ctypes.c_char_p, []),
     }
@@ -117,18 +120,49 @@ def _ptr(t, dtype=None, name="tensor"):
 
 
 def make_weights(sh: Shape, t: dict) -> Weights:
-    """Weights struct from a dict of tensors (keys as in include/lmoe.h)."""
+    """Weights struct from a dict of tensors (keys as in include/lmoe.h;
+    "packed" is the uint8 buffer filled by pack_experts, or absent)."""
     act, wexp = _TORCH[sh.act], _TORCH[sh.w_expert]
     want = {"w_router": act, "b_router": torch.float32, "w_down": act, "w_gate": wexp, "w_value": wexp,
             "w_out": wexp, "s_gate": torch.float32, "s_value": torch.float32, "s_out": torch.float32,
             "gamma": torch.float32, "w_up": act, "ws_gate": wexp, "ws_value": wexp, "ws_out": wexp,
-            "ss_gate": torch.float32, "ss_value": torch.float32, "ss_out": torch.float32}
+            "ss_gate": torch.float32, "ss_value": torch.float32, "ss_out": torch.float32, "packed": torch.uint8}
     vals = {}
     for n in _WEIGHT_FIELDS:
         vals[n] = _ptr(t.get(n), want[n], n)
     w = Weights(**vals)
     w._keep = [t.get(n) for n in _WEIGHT_FIELDS]  # keep the tensors alive with the struct
     return w
+
+
+def packed_bytes(sh: Shape) -> int:
+    """Bytes of the packed expert weights (0: the shape has no packed form)."""
+    load_library()
+    return int(_lib.lmoe_packed_bytes(ctypes.byref(sh)))
+
+
+def pack_experts(sh: Shape, w: Weights, out=None, stream=None):
+    """Packed copy of the routed expert weights (uint8 device tensor) for
+    Weights.packed; see lmoe_pack_experts in include/lmoe.h."""
+    n = packed_bytes(sh)
+    if n == 0:
+        raise LmoeError(2, "this shape has no packed expert layout")
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device="cuda")
+    if out.dtype != torch.uint8 or out.numel() < n:
+        raise ValueError(f"out must be a uint8 tensor of at least {n} bytes")
+    _check(_lib.lmoe_pack_experts(ctypes.byref(sh), ctypes.byref(w), _ptr(out, torch.uint8, "out"), n,
+                                  _stream(stream)))
+    return out
+
+
+def with_packed(sh: Shape, w: Weights, packed) -> Weights:
+    """Copy of `w` whose expert GEMMs read `packed` (from pack_experts)."""
+    vals = {n: getattr(w, n) for n in _WEIGHT_FIELDS}
+    vals["packed"] = _ptr(packed, torch.uint8, "packed")
+    w2 = Weights(**vals)
+    w2._keep = list(getattr(w, "_keep", [])) + [packed]
+    return w2
 
 
 def _stream(stream):

@@ -26,8 +26,10 @@ def declared_functions():
 
 
 def fake_weights(sh, **override):
-    """Non-null host addresses: validation never dereferences them."""
+    """Non-null host addresses: validation never dereferences them (no packed
+    expert weights unless asked for)."""
     vals = {n: 0x1000 + 0x100 * i for i, n in enumerate(lmoe._WEIGHT_FIELDS)}
+    vals["packed"] = None
     vals.update(override)
     return lmoe.Weights(**vals)
 
@@ -177,3 +179,41 @@ def test_binding_refuses_host_tensors(lib):
     sh = lmoe.shape_of(cfg)
     with pytest.raises(ValueError):
         lmoe.make_weights(sh, {"w_router": torch.zeros(cfg.E, cfg.H, dtype=torch.bfloat16)})
+
+
+def test_packed_bytes(lib):
+    sh = k3()
+    blocks = 896 * (1024 // 128) * (3584 // 64) + 896 * (3584 // 256) * (1024 // 64)
+    assert lmoe.packed_bytes(sh) == blocks * 32768
+    # padding: gate/value tiles of 128 units, out tiles of 256 rows
+    odd = k3(I=192, L=320)
+    assert lmoe.packed_bytes(odd) == 896 * (2 * 5 + 2 * 3) * 32768
+    assert lmoe.packed_bytes(k3(w_expert="f8")) == 0
+    assert lmoe.packed_bytes(k3(act="f32", w_expert="f32")) == 0
+    assert lmoe.packed_bytes(k3(T=-1)) == 0
+
+
+def test_packed_weights_validation(lib):
+    sh = k3()
+    # packed expert weights replace the row-major stacks
+    w = fake_weights(sh, packed=0x100000, w_gate=None, w_value=None, w_out=None)
+    assert lmoe.validate(sh, w, 1 << 40) == 0
+    assert lmoe.validate(sh, fake_weights(sh, packed=0x100010), 1 << 40) == 1
+    assert "aligned" in lmoe.last_error()
+    f8 = k3(w_expert="f8")
+    assert lmoe.validate(f8, fake_weights(f8, packed=0x100000), 1 << 40) == 2
+
+
+def test_pack_experts_rejects_before_any_gpu_call(lib):
+    sh = k3()
+    n = lmoe.packed_bytes(sh)
+    w = fake_weights(sh)
+    buf = ctypes.c_void_p(0x100000)
+    assert lib.lmoe_pack_experts(ctypes.byref(sh), None, buf, n, None) == 1
+    assert lib.lmoe_pack_experts(ctypes.byref(sh), ctypes.byref(fake_weights(sh, w_out=None)), buf, n, None) == 1
+    assert lib.lmoe_pack_experts(ctypes.byref(sh), ctypes.byref(w), None, n, None) == 1
+    assert lib.lmoe_pack_experts(ctypes.byref(sh), ctypes.byref(w), ctypes.c_void_p(0x100080), n, None) == 1
+    assert lib.lmoe_pack_experts(ctypes.byref(sh), ctypes.byref(w), buf, n - 1, None) == 1
+    assert "needed" in lmoe.last_error()
+    f8 = k3(w_expert="f8")
+    assert lib.lmoe_pack_experts(ctypes.byref(f8), ctypes.byref(fake_weights(f8)), buf, n, None) == 2

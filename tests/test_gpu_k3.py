@@ -69,6 +69,26 @@ def test_k3_t8192(dev, k3w):
     _run(get_config("k3_t8192"), k3w, dev)
 
 
+def test_k3_packed_matches_row_major(dev, k3w):
+    """The benchmark's configuration: expert weights packed once, then the
+    layer at T=8192 (256-row token tiles) and T=64 (32-row tiles); every output
+    is bitwise equal to the row-major path, which the oracle checks above."""
+    for name in ("k3_t8192", "k3_decode_t64"):
+        cfg = get_config(name)
+        note(f"[k3 packed] {name}")
+        x = make_x(cfg, dev)
+        sh = lmoe.shape_of(cfg)
+        w = lmoe.make_weights(sh, k3w)
+        y0, i0, _ = lmoe.forward(sh, w, x)
+        pk = lmoe.pack_experts(sh, w)
+        y1, i1, _ = lmoe.forward(sh, lmoe.with_packed(sh, w, pk), x)
+        torch.cuda.synchronize()
+        assert torch.equal(i0, i1)
+        assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+        del pk, y0, y1
+        torch.cuda.empty_cache()
+
+
 def test_k3_prefill_and_decode_batch_invariant(dev, k3w):
     cfg = get_config("k3_prefill_t2048")
     y, idx = _run(cfg, k3w, dev, sample=6)

@@ -285,3 +285,96 @@ def test_forward_deterministic_and_batch_invariant(dev):
     assert torch.equal(y1, y2) and torch.equal(i1, i2)
     assert torch.equal(i1[:40], ip)
     assert torch.equal(y1[:40], yp)
+
+
+# ----------------------------------------------------------------------------
+# Packed expert weights: the layout (bit-exact, against an index-only
+# re-arrangement written here) and the layer reading them (bitwise equal to
+# the row-major path: same products, same order).
+# ----------------------------------------------------------------------------
+
+def _packed_reference(g, cfg):
+    """The packed layout of include/lmoe.h built with plain tensor indexing
+    on the host (uint16 bit patterns)."""
+    E, I, L = cfg.E, cfg.I, cfg.L
+    wg, wv, wo = (g[n].cpu().view(torch.int16) for n in ("w_gate", "w_value", "w_out"))
+    r = torch.arange(256)
+    p = torch.arange(8)
+    ch = p[None, :] ^ ((r[:, None] >> 1) & 7)                       # [256, 8] source chunk per position
+    cols = (ch[:, :, None] * 8 + torch.arange(8)).reshape(256, 64)  # [256, 64] column within the k-tile
+    blocks = []
+    nft = -(-I // 128)
+    m = r % 64
+    u_all = (r // 64) * 32 + (m % 32)
+    val = m >= 32
+    for e in range(E):
+        for f in range(nft):
+            u = 128 * f + u_all
+            ok = u < I
+            uc = torch.where(ok, u, torch.zeros_like(u))
+            rows = torch.where(val[:, None], wv[e][uc], wg[e][uc])     # [256, L]
+            rows = torch.where(ok[:, None], rows, torch.zeros_like(rows))
+            for kt in range(L // 64):
+                blocks.append(torch.gather(rows[:, kt * 64:(kt + 1) * 64], 1, cols))
+    nfd = -(-L // 256)
+    for e in range(E):
+        for f in range(nfd):
+            fr = 256 * f + r
+            ok = fr < L
+            rows = wo[e][torch.where(ok, fr, torch.zeros_like(fr))]
+            rows = torch.where(ok[:, None], rows, torch.zeros_like(rows))
+            for kt in range(I // 64):
+                blocks.append(torch.gather(rows[:, kt * 64:(kt + 1) * 64], 1, cols))
+    return torch.stack(blocks).reshape(-1)
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "small_full_k"])
+def test_pack_layout(dev, name):
+    """small_bf16 pads gate/value tiles (I = 192), small_full_k pads out tiles (L = 128)."""
+    cfg = get_config(name)
+    note(f"[pack] {name} E={cfg.E} I={cfg.I} L={cfg.L}")
+    t, g = make_case(cfg, dev)
+    sh, w = _weights(cfg, g)
+    pk = lmoe.pack_experts(sh, w)
+    torch.cuda.synchronize()
+    assert pk.numel() == lmoe.packed_bytes(sh)
+    ref = _packed_reference(g, cfg)
+    got = pk.cpu().view(torch.int16)
+    assert got.shape == ref.shape
+    assert torch.equal(got, ref)
+
+
+@pytest.mark.parametrize("name,T", [("small_bf16", None), ("small_full_k", None), ("small_identity_bf16", None),
+                                    ("small_bf16", 20), ("small_bf16", 700), ("small_bf16", 2000)])
+def test_forward_packed_matches_row_major(dev, name, T):
+    """Same products in the same order: the packed layer is bitwise equal to
+    the row-major one, also with the row-major stacks withheld."""
+    cfg = get_config(name) if T is None else replace(get_config(name), T=T, name=f"{name}_T{T}")
+    note(f"[packed forward] {cfg.name}")
+    t, g = make_case(cfg, dev)
+    sh, w = _weights(cfg, g)
+    y0, i0, w0 = lmoe.forward(sh, w, g["x"])
+    pk = lmoe.pack_experts(sh, w)
+    wp = lmoe.with_packed(sh, w, pk)
+    y1, i1, w1 = lmoe.forward(sh, wp, g["x"])
+    only = {k: v for k, v in g.items() if k not in ("w_gate", "w_value", "w_out")}
+    wpo = lmoe.with_packed(sh, lmoe.make_weights(sh, only), pk)
+    y2, _, _ = lmoe.forward(sh, wpo, g["x"])
+    torch.cuda.synchronize()
+    assert torch.equal(i0, i1) and torch.equal(w0, w1)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    assert torch.equal(y0.view(torch.int16), y2.view(torch.int16))
+
+
+def test_expert_gemm_packed(dev):
+    cfg = get_config("small_bf16")
+    note("[packed expert_gemm] small_bf16")
+    t, g = make_case(cfg, dev)
+    sh, w = _weights(cfg, g)
+    idx, tw, z = lmoe.route(sh, w, g["x"])
+    offsets, sorted_, pos = lmoe.permute(sh, idx)
+    o0 = lmoe.expert_gemm(sh, w, z, offsets, sorted_)
+    wp = lmoe.with_packed(sh, w, lmoe.pack_experts(sh, w))
+    o1 = lmoe.expert_gemm(sh, wp, z, offsets, sorted_)
+    torch.cuda.synchronize()
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
