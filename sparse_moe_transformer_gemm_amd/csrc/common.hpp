@@ -45,6 +45,44 @@ __device__ __forceinline__ float situ_glu(float g, float v, float c, float inv_c
   return gc / (1.f + expf(-gc)) * vc;
 }
 
+// Uniform reads, through the scalar cache, of index data that no kernel in
+// flight writes (expert tile list, offsets, the sorted assignment order).
+// Each returns with the value loaded (the wait is inside), so no vector-memory
+// counter is involved: the GEMM main loops' DMA accounting stays exact and no
+// compiler-inserted vmcnt(0) drains their pipeline.  Reads only.
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ int sload1(const int* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ i32x2 sload2(const int* p) {
+  i32x2 v;
+  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ i32x4 sload4(const int* p) {
+  i32x4 v;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+// Eight uniform ints p[idx[0..7]] (any addresses) in one round trip.
+__device__ __forceinline__ i32x8 sload_gather8(const int* p, const int (&idx)[8]) {
+  int v0, v1, v2, v3, v4, v5, v6, v7;
+  asm volatile(
+      "s_load_dword %0, %8, 0x0\n\ts_load_dword %1, %9, 0x0\n\ts_load_dword %2, %10, 0x0\n\t"
+      "s_load_dword %3, %11, 0x0\n\ts_load_dword %4, %12, 0x0\n\ts_load_dword %5, %13, 0x0\n\t"
+      "s_load_dword %6, %14, 0x0\n\ts_load_dword %7, %15, 0x0\n\ts_waitcnt lgkmcnt(0)"
+      : "=&s"(v0), "=&s"(v1), "=&s"(v2), "=&s"(v3), "=&s"(v4), "=&s"(v5), "=&s"(v6), "=&s"(v7)
+      : "s"(p + idx[0]), "s"(p + idx[1]), "s"(p + idx[2]), "s"(p + idx[3]), "s"(p + idx[4]), "s"(p + idx[5]),
+        "s"(p + idx[6]), "s"(p + idx[7])
+      : "memory");
+  i32x8 v = {v0, v1, v2, v3, v4, v5, v6, v7};
+  return v;
+}
+
 // Work-group id -> logical index so that each XCD receives a contiguous range
 // of logical tiles (neighbouring tiles share operands in that XCD's L2).
 // `padded` is a multiple of kXcds and the grid size.

@@ -99,10 +99,14 @@ struct DenseXProb {
 
   __device__ bool setup(int bid, State& st) const {
     if (bid >= padded) return false;
-    const int lg = xcd_remap(bid, padded);
+    return setup_lg(xcd_remap(bid, padded), st);
+  }
+  __device__ int num_logical() const { return ntt * nft; }
+  // logical tile -> (token tile, feature tile): 8 token tiles per group,
+  // feature tiles run over the group, so 8 neighbours share one weight tile
+  // and an XCD's window covers a few weight tiles
+  __device__ bool setup_lg(int lg, State& st) const {
     if (lg >= ntt * nft) return false;
-    // 8 token tiles per group, feature tiles run over the group: 8 neighbours
-    // share one weight tile, and an XCD's window covers a few weight tiles.
     const int grp = lg / (8 * nft);
     const int gsz = min(8, ntt - grp * 8);
     const int within = lg - grp * 8 * nft;
@@ -128,6 +132,9 @@ struct DenseXProb {
   __device__ const char* x_row(const State& st, int, int r) const {
     const int64_t t = (int64_t)st.tt * Cfg::BT + r;
     return t < T ? x + t * K * (int64_t)sizeof(CT) : nullptr;
+  }
+  __device__ const char* x_row_grp(const State& st, int s, int r0, int lane) const {
+    return x_row(st, s, min(r0 + (lane >> 3), tokens_valid(st) - 1));
   }
   __device__ const char* w_row(const State& st, int, int r, const float** scrow) const {
     const NSeg& s = st.s;
@@ -181,7 +188,10 @@ struct UpProb {
 
   __device__ bool setup(int bid, State& st) const {
     if (bid >= padded) return false;
-    const int lg = xcd_remap(bid, padded);
+    return setup_lg(xcd_remap(bid, padded), st);
+  }
+  __device__ int num_logical() const { return ntt * nft; }
+  __device__ bool setup_lg(int lg, State& st) const {
     if (lg >= ntt * nft) return false;
     const int grp = lg / (8 * nft);
     const int gsz = min(8, ntt - grp * 8);
@@ -198,6 +208,9 @@ struct UpProb {
   __device__ const char* x_row(const State& st, int s, int r) const {
     const int64_t t = (int64_t)st.tt * Cfg::BT + r;
     return t < T ? ks[s].x + t * ks[s].ldx * (int64_t)sizeof(CT) : nullptr;
+  }
+  __device__ const char* x_row_grp(const State& st, int s, int r0, int lane) const {
+    return x_row(st, s, min(r0 + (lane >> 3), tokens_valid(st) - 1));
   }
   __device__ const char* w_row(const State& st, int s, int r, const float** scrow) const {
     const int f = st.ft * Cfg::BF + r;
@@ -231,20 +244,23 @@ struct ExpertTiles {
   const int* tile_count;
   int nft;
 
+  __device__ int num_logical() const { return sload1(tile_count) * nft; }
   __device__ bool locate(int bid, ExpertState& st) const {
-    const int R = *tile_count * nft;
+    const int R = num_logical();
     const int per = (R + kXcds - 1) / kXcds;
     if (bid >= per * kXcds) return false;
-    const int lg = (bid % kXcds) * per + bid / kXcds;
+    return locate_lg((bid % kXcds) * per + bid / kXcds, R, st);
+  }
+  __device__ bool locate_lg(int lg, int R, ExpertState& st) const {
     if (lg >= R) return false;
-    const int4 te = tiles[lg / nft];
+    const i32x4 te = sload4(reinterpret_cast<const int*>(tiles + lg / nft));
     const int local = lg - te.y * nft;
     st.ft = local / te.z;
     const int mt = local - st.ft * te.z;
     st.e = te.x;
-    const int beg = offsets[st.e];
-    st.m0 = beg + mt * Cfg::BT;
-    st.rows = min(Cfg::BT, offsets[st.e + 1] - st.m0);
+    const i32x2 ob = sload2(offsets + st.e);
+    st.m0 = ob.x + mt * Cfg::BT;
+    st.rows = min(Cfg::BT, ob.y - st.m0);
     return st.rows > 0;
   }
 };
@@ -266,6 +282,8 @@ struct ExpertGVProb {
 
   typedef ExpertState State;
   __device__ bool setup(int bid, State& st) const { return et.locate(bid, st); }
+  __device__ int num_logical() const { return et.num_logical(); }
+  __device__ bool setup_lg(int lg, State& st) const { return et.locate_lg(lg, et.num_logical(), st); }
   __device__ int num_ksegs() const { return 1; }
   __device__ int seg_ktiles(int) const { return L * (int)sizeof(CT) / 128; }
   __device__ bool seg_f8(const State&, int) const { return f8; }
@@ -275,6 +293,20 @@ struct ExpertGVProb {
     if (r >= st.rows) return nullptr;
     const int t = sorted[st.m0 + r] / k;
     return z + (int64_t)t * ldz * (int64_t)sizeof(CT);
+  }
+  // Row r0 + lane / 8 for r0 < rows (rows past the valid ones map to the last
+  // valid row): the group's 8 assignment ids are read as uniform scalars, so
+  // the call needs no vector-memory wait.
+  __device__ const char* x_row_grp(const State& st, int, int r0, int lane) const {
+    int idx[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) idx[q] = st.m0 + min(r0 + q, st.rows - 1);
+    const i32x8 v = sload_gather8(sorted, idx);
+    const int q8 = lane >> 3;
+    int a = v[0];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) a = q8 == q ? v[q] : a;
+    return z + (int64_t)(a / k) * ldz * (int64_t)sizeof(CT);
   }
   __device__ const char* w_row(const State& st, int, int r, const float** scrow) const {
     const int m = r & 63;
@@ -307,6 +339,8 @@ struct ExpertDownProb {
 
   typedef ExpertState State;
   __device__ bool setup(int bid, State& st) const { return et.locate(bid, st); }
+  __device__ int num_logical() const { return et.num_logical(); }
+  __device__ bool setup_lg(int lg, State& st) const { return et.locate_lg(lg, et.num_logical(), st); }
   __device__ int num_ksegs() const { return 1; }
   __device__ int seg_ktiles(int) const { return I * (int)sizeof(CT) / 128; }
   __device__ bool seg_f8(const State&, int) const { return f8; }
@@ -315,6 +349,9 @@ struct ExpertDownProb {
   __device__ const char* x_row(const State& st, int, int r) const {
     if (r >= st.rows) return nullptr;
     return act + (int64_t)(st.m0 + r) * I * (int64_t)sizeof(CT);
+  }
+  __device__ const char* x_row_grp(const State& st, int s, int r0, int lane) const {
+    return x_row(st, s, min(r0 + (lane >> 3), tokens_valid(st) - 1));
   }
   __device__ const char* w_row(const State& st, int, int r, const float** scrow) const {
     const int f = st.ft * Cfg::BF + r;

@@ -50,9 +50,12 @@ struct Tile2 {
 // Dense GEMMs over many tokens / few tokens (weight streaming); experts
 // holding many rows, a few dozen rows, or one or two rows (decode).
 // Split-ring tile (gemm3_kernel below): weights three stages deep, tokens two.
-template <int BF_, int BT_, int WF_, int WT_, int WAUX_>
+template <int BF_, int BT_, int WF_, int WT_, int WAUX_, int PERSIST_ = 0>
 struct Tile3 {
   static constexpr int BF = BF_, BT = BT_, WF = WF_, WT = WT_, WAUX = WAUX_;
+  // PERSIST: a grid of resident work-groups walks the tile list with one
+  // continuous DMA pipeline (gemm3p_kernel) instead of one tile per group
+  static constexpr int PERSIST = PERSIST_;
   static constexpr int NT = WF * WT * kWave, NW = WF * WT;
   static constexpr int FW = BF / WF, TW = BT / WT;
   static constexpr int FI = FW / 32, TI = TW / 32;
@@ -62,7 +65,7 @@ struct Tile3 {
   static constexpr int X_OFF = SW * BF * 128;
   static constexpr int LDS = SW * BF * 128 + SX * BT * 128;
   static constexpr bool kDma = true;
-  static constexpr int kKind = 3;
+  static constexpr int kKind = PERSIST ? 4 : 3;
   static_assert(FW % 64 == 0 && TW % 32 == 0, "wave tile");
   static_assert(QW % NW == 0 && QX % NW == 0, "DMA instructions split evenly over the waves");
   static_assert(NQW <= 63, "vmcnt range");
@@ -80,10 +83,10 @@ struct Tile3 {
 #define LMOE_T_THIN Tile2<64, 32, 1, 1, 4, 0>
 #endif
 #ifndef LMOE_T_EXPERT_GV
-#define LMOE_T_EXPERT_GV Tile3<256, 256, 4, 4, 0>
+#define LMOE_T_EXPERT_GV Tile3<256, 256, 4, 4, 0, 1>
 #endif
 #ifndef LMOE_T_EXPERT_DN
-#define LMOE_T_EXPERT_DN Tile3<256, 256, 4, 4, 0>
+#define LMOE_T_EXPERT_DN Tile3<256, 256, 4, 4, 0, 1>
 #endif
 #ifndef LMOE_T_MID_GV
 #define LMOE_T_MID_GV Tile2<256, 64, 4, 1, 3, 0>
@@ -183,14 +186,15 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
 // across the wave.  (A branch-free variant of this loop for full tiles was
 // measured to run the 256x256 dense GEMMs about 3x slower on MI355X, and to
 // slow the kernels launched after them, so it is not used.)
-template <int FI, int TI>
+template <int FI, int TI, bool DB = true>
 __device__ __forceinline__ void mma_ktile(f32x16 (&acc)[FI][TI], const char* sW, const char* sX, int wf0, int wt0,
                                           int lane, int tiv) {
   const int lr = lane & 31;
   const int sw = swz(lr);  // fragment row offsets are multiples of 32
   const char* pw = sW + (wf0 + lr) * 128;
   const char* px = sX + (wt0 + lr) * 128;
-  bf16x8 a[2][FI], b[2][TI];
+  constexpr int NB = DB ? 2 : 1;
+  bf16x8 a[NB][FI], b[NB][TI];
   auto load = [&](int ks, int buf) __attribute__((always_inline)) {
     const int ch = ((2 * ks + (lane >> 5)) ^ sw) << 4;
 #pragma unroll
@@ -199,15 +203,20 @@ __device__ __forceinline__ void mma_ktile(f32x16 (&acc)[FI][TI], const char* sW,
     for (int j = 0; j < TI; ++j)
       if (j < tiv) b[buf][j] = *reinterpret_cast<const bf16x8*>(px + j * 32 * 128 + ch);
   };
-  load(0, 0);
+  if (DB) load(0, 0);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    if (ks + 1 < 4) load(ks + 1, (ks + 1) & 1);
+    const int cur = DB ? (ks & 1) : 0;
+    if (DB) {
+      if (ks + 1 < 4) load(ks + 1, (ks + 1) & 1);
+    } else {
+      load(ks, 0);
+    }
 #pragma unroll
     for (int j = 0; j < TI; ++j)
       if (j < tiv) {
 #pragma unroll
-        for (int i = 0; i < FI; ++i) acc[i][j] = mfma32(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
+        for (int i = 0; i < FI; ++i) acc[i][j] = mfma32(a[cur][i], b[cur][j], acc[i][j]);
       }
   }
 }
@@ -425,6 +434,166 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3_kernel(const Prob p) {
                         lane, tiv);
   }
   p.epilogue(st, acc, wf0, wt0, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Persistent split-ring GEMM.  The grid holds a multiple of 8 work-groups, all
+// resident; work-group b serves XCD b % 8 and walks that XCD's contiguous
+// range of logical tiles with stride (grid / 8), so tiles that share operands
+// still run side by side in one L2.  The k-tiles of all its tiles form one
+// sequence g = 0 .. G-1 (nkt per tile) through the same rings, issued as in
+// gemm3_kernel: X(g+1) then W(g+2) in iteration g, wait vmcnt(NQW) at the top
+// of each iteration.  A finished tile's epilogue runs at the top of the next
+// iteration, after its wait and barrier and before that iteration's DMAs, so
+// its stores are older than every DMA the later waits count on.
+// ---------------------------------------------------------------------------
+template <class Cfg, class Prob>
+__global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  constexpr int FI = Cfg::FI, TI = Cfg::TI, NQW = Cfg::NQW, NQX = Cfg::NQX, NW = Cfg::NW;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wf0 = (wid % Cfg::WF) * Cfg::FW;
+  const int wt0 = (wid / Cfg::WF) * Cfg::TW;
+
+  // this work-group's tiles: logical xcd * per + slot + j * nslot
+  const int R = p.num_logical();
+  const int per = (R + kXcds - 1) / kXcds;
+  const int nslot = (int)gridDim.x / kXcds;
+  const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
+  const int lim = min(per, R - xcd * per);
+  const int ntile = lim > slot ? (lim - slot + nslot - 1) / nslot : 0;
+  if (ntile == 0) return;
+  auto tile_lg = [&](int j) __attribute__((always_inline)) { return xcd * per + slot + j * nslot; };
+
+  const int nks = p.num_ksegs();
+  int nkt = 0;
+  for (int s = 0; s < nks; ++s) nkt += p.seg_ktiles(s);
+  if (nkt == 0) return;
+  const int G = ntile * nkt;
+  int first_seg = 0;
+  while (first_seg < nks && p.seg_ktiles(first_seg) == 0) ++first_seg;
+
+  // compute side: current tile and its wave masks
+  typename Prob::State cst;
+  p.setup_lg(tile_lg(0), cst);
+  int cj = 0, ckt = 0;
+  int tiv = 0;
+  bool active = false;
+  auto masks = [&]() __attribute__((always_inline)) {
+    tiv = min(TI, max(0, (p.tokens_valid(cst) - wt0 + 31) >> 5));
+    active = tiv > 0 && wf0 < p.feats_valid(cst);
+  };
+  masks();
+
+  f32x16 acc[FI][TI];
+  auto zero = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < TI; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  };
+  zero();
+
+  // weight issue side
+  typename Prob::State wst = cst;
+  int wj = 0, wsg = first_seg, wk = 0;
+  const char* srcW[NQW];
+  const char* wblk = nullptr;
+  int64_t wstep = 128;
+  auto set_w = [&]() __attribute__((always_inline)) {
+    wblk = p.w_block(wst);
+    wstep = wblk ? kPackBlock : 128;
+    const float* dummy = nullptr;
+    const char* w0 = p.w_row(wst, wsg, 0, &dummy);
+#pragma unroll
+    for (int i = 0; i < NQW; ++i) {
+      const int q = wid + NW * i;
+      if (wblk) {
+        srcW[i] = wblk + q * 1024 + lane * 16;
+      } else {
+        const int row = q * 8 + (lane >> 3);
+        const char* rp = p.w_row(wst, wsg, row, &dummy);
+        srcW[i] = (rp ? rp : w0) + (((lane & 7) ^ swz(row)) << 4);
+      }
+    }
+  };
+  // token issue side
+  typename Prob::State xst = cst;
+  int xj = 0, xsg = first_seg, xk = 0;
+  const char* srcX[NQX];
+  bool xon[NQX];
+  // (row groups wholly past the valid rows are never issued and need no
+  // source; x_row_grp maps the missing rows of a partial group to a valid one)
+  auto set_x = [&]() __attribute__((always_inline)) {
+    const int xrows = p.tokens_valid(xst);
+#pragma unroll
+    for (int i = 0; i < NQX; ++i) {
+      const int r0 = (wid + NW * i) * 8;
+      xon[i] = r0 < xrows;
+      if (xon[i]) srcX[i] = p.x_row_grp(xst, xsg, r0, lane) + (((lane & 7) ^ swz(r0 + (lane >> 3))) << 4);
+    }
+  };
+  set_w();
+  set_x();
+  auto issue_w = [&](int buf) __attribute__((always_inline)) {
+    char* base = smem + buf * Cfg::BF * 128;
+#pragma unroll
+    for (int i = 0; i < NQW; ++i) dma16<Cfg::WAUX>(srcW[i] + wk * wstep, base + (wid + NW * i) * 1024);
+    if (++wk == p.seg_ktiles(wsg)) {
+      wk = 0;
+      do { ++wsg; } while (wsg < nks && p.seg_ktiles(wsg) == 0);
+      if (wsg == nks && ++wj < ntile) {
+        p.setup_lg(tile_lg(wj), wst);
+        wsg = first_seg;
+      }
+      if (wsg < nks) set_w();
+    }
+  };
+  auto issue_x = [&](int buf) __attribute__((always_inline)) {
+    char* base = smem + Cfg::X_OFF + buf * Cfg::BT * 128;
+#pragma unroll
+    for (int i = 0; i < NQX; ++i)
+      if (xon[i]) dma16<LMOE_X_AUX>(srcX[i] + (int64_t)xk * 128, base + (wid + NW * i) * 1024);
+    if (++xk == p.seg_ktiles(xsg)) {
+      xk = 0;
+      do { ++xsg; } while (xsg < nks && p.seg_ktiles(xsg) == 0);
+      if (xsg == nks && ++xj < ntile) {
+        p.setup_lg(tile_lg(xj), xst);
+        xsg = first_seg;
+      }
+      if (xsg < nks) set_x();
+    }
+  };
+
+  issue_x(0);
+  issue_w(0);
+  if (G > 1) issue_w(1);
+  bool pending = false;  // a finished tile's accumulators await their epilogue
+  for (int g = 0; g < G; ++g) {
+    if (g + 1 < G) wait_vmcnt_barrier<NQW>();
+    else wait_vmcnt_barrier<0>();
+    if (pending) {
+      p.epilogue(cst, acc, wf0, wt0, lane);
+      zero();
+      ++cj;
+      p.setup_lg(tile_lg(cj), cst);
+      masks();
+      pending = false;
+    }
+    if (g + 1 < G) issue_x((g + 1) & 1);
+    if (g + 2 < G) issue_w((g + 2) % 3);
+    if (active)
+      mma_ktile<FI, TI, false>(acc, smem + (g % 3) * Cfg::BF * 128, smem + Cfg::X_OFF + (g & 1) * Cfg::BT * 128, wf0,
+                               wt0, lane, tiv);
+    if (++ckt == nkt) {
+      ckt = 0;
+      pending = true;
+    }
+  }
+  p.epilogue(cst, acc, wf0, wt0, lane);
 }
 
 }  // namespace lmoe

@@ -188,11 +188,31 @@ lmoe_status check_ws(const lmoe_shape* sh, const void* ws, size_t ws_bytes) {
 // ---------------------------------------------------------------------------
 // GEMM launches.
 // ---------------------------------------------------------------------------
+// Work-groups of a persistent GEMM: one per compute unit (their LDS use
+// leaves room for one group per CU), a multiple of the XCD count.
+int persistent_grid() {
+  static std::once_flag once;
+  static int n = 0;
+  std::call_once(once, [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      n = cus;
+    else
+      n = 256;
+    n = (n + kXcds - 1) / kXcds * kXcds;
+  });
+  return n;
+}
+
 template <class Cfg, typename CT, class Prob>
 hipError_t launch_gemm(const Prob& p, int64_t grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   void (*kern)(const Prob);
-  if constexpr (Cfg::kKind == 3) kern = gemm3_kernel<Cfg, Prob>;
+  if constexpr (Cfg::kKind == 4) {
+    kern = gemm3p_kernel<Cfg, Prob>;
+    grid = persistent_grid();
+  } else if constexpr (Cfg::kKind == 3) kern = gemm3_kernel<Cfg, Prob>;
   else if constexpr (Cfg::kKind == 2) kern = gemm2_kernel<Cfg, Prob>;
   else kern = gemm_kernel<Cfg, CT, Prob>;
   static std::once_flag once;
