@@ -191,7 +191,8 @@ def main():
     ms_ev, stages = timed_loop(lmoe, sh, w, x, y, idx, tw, ws, a.steps, 1, per_stage=True)
     touched = int(torch.unique(idx).numel())
 
-    flops = lmoe.layer_flops(sh)
+    proj = not cfg.identity_proj
+    flops = lmoe.layer_flops(sh, projections=proj)
     tflops = flops / (ms * 1e-3) / 1e12
     tok_s = T / (ms * 1e-3)
 
@@ -203,7 +204,7 @@ def main():
     gv_ms = stages["expert_gate_value"]
     gv_gbs = gv_bytes / (gv_ms * 1e-3) / 1e9
     dn_bytes = lmoe.expert_bytes(sh, touched, "down") + T * cfg.k * cfg.I * es + T * cfg.k * cfg.L * es
-    layer_bytes = lmoe.expert_bytes(sh, touched) + lmoe.dense_bytes(sh) + 2 * T * cfg.H * es
+    layer_bytes = lmoe.expert_bytes(sh, touched) + lmoe.dense_bytes(sh, projections=proj) + 2 * T * cfg.H * es
 
     out = {
         "metric": METRIC,

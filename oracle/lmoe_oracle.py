@@ -170,6 +170,33 @@ def route(x, w_router, b_router, k):
     return dict(logits=logits, scores=scores, biased=biased, idx=idx, gap=gap, w=w)
 
 
+def quantile_thresholds(scores, k):
+    """Quantile Balancing (P3, Stable LatentMoE bullet: per-expert top-k
+    thresholds are solved for directly instead of nudging biases by fixed
+    steps; P2, the balancing passage: the thresholds come from the batch's
+    score distribution, as the score an expert needs to keep its fair share
+    of tokens).  Reading taken: expert e's threshold is the (1 - k/E)
+    quantile of its scores over the T tokens of the batch, interpolated
+    linearly between order statistics: with the column sorted ascending,
+    h = (T - 1)(1 - k/E) and tau = s_(floor h) + frac(h) (s_(floor h + 1) -
+    s_(floor h)).  About T k / E tokens then score at or above tau_e."""
+    T, E = scores.shape
+    if T == 0:
+        raise ValueError("quantile thresholds need at least one token")
+    h = (T - 1) * (1.0 - k / E)
+    lo = int(np.floor(h))
+    hi = min(lo + 1, T - 1)
+    frac = h - lo
+    col = np.sort(scores, axis=0)  # each expert's scores, ascending
+    return col[lo] + frac * (col[hi] - col[lo])
+
+
+def quantile_bias(logits, k):
+    """Selection bias of Quantile Balancing: b_e = -tau_e, so that the a1
+    selection on s + b ranks each expert's scores against its own threshold."""
+    return -quantile_thresholds(sigmoid(logits), k)
+
+
 def combine_weights(scores, idx):
     sel = np.take_along_axis(scores, idx, axis=1)
     if sel.shape[0] == 0:

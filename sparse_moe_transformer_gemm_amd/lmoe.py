@@ -289,12 +289,14 @@ def up(sh: Shape, w: Weights, n, x, y=None, ws=None, stream=None):
 # work accounting (used by the benchmark)
 # ----------------------------------------------------------------------------
 
-def layer_flops(sh: Shape, tokens=None) -> float:
+def layer_flops(sh: Shape, tokens=None, projections=True) -> float:
     """Algorithmic FLOPs of one layer call (2 per multiply-add): router, down,
-    k experts per token (gate, value, out), up, shared experts."""
+    k experts per token (gate, value, out), up, shared experts.  projections
+    False: identity down/up projections (no latent) cost nothing."""
     T = sh.T if tokens is None else tokens
     H, L, E, k, I, S, Is = sh.H, sh.L, sh.E, sh.k, sh.I, sh.S, sh.Is
-    per_tok = 2 * (E * H + L * H + k * 3 * L * I + H * L + S * 3 * H * Is)
+    proj = 2 * L * H if projections else 0
+    per_tok = 2 * (E * H + k * 3 * L * I + S * 3 * H * Is) + 2 * proj
     return float(T) * per_tok
 
 
@@ -310,11 +312,11 @@ def expert_bytes(sh: Shape, touched: int, which="all") -> float:
     return float(touched) * per
 
 
-def dense_bytes(sh: Shape) -> float:
-    """Router, down, up and shared-expert weight bytes."""
+def dense_bytes(sh: Shape, projections=True) -> float:
+    """Router, down, up and shared-expert weight bytes (plus the bias and gamma)."""
     ab = {F32: 4, BF16: 2}[sh.act]
     wb = {F32: 4, BF16: 2, F8E4M3: 1}[sh.w_expert]
-    b = sh.E * sh.H * ab + 4 * sh.E + 2 * sh.L * sh.H * ab + 4 * sh.L
+    b = sh.E * sh.H * ab + 4 * sh.E + (2 * sh.L * sh.H * ab if projections else 0) + 4 * sh.L
     b += sh.S * 3 * sh.H * sh.Is * wb
     if sh.w_expert == F8E4M3:
         b += sh.S * 3 * (sh.H // 128) * (sh.Is // 128) * 4

@@ -70,6 +70,10 @@ _LIST = [
     LayerConfig("k3_fp8_t8192", T=8192, act="bf16", w_expert="f8", seed=1, **K3),
     LayerConfig("fp8_448x8_l7168_t8192", T=8192, H=7168, L=7168, E=448, k=8, S=2,
                 I=1024, Is=1024, act="bf16", w_expert="f8", seed=1),
+    # The pages' 448/8 comparison read as a classic MoE with no latent (identity
+    # projections): experts on the full 7168-wide hidden state.
+    LayerConfig("k3_448x8_identity_t8192", T=8192, H=7168, L=7168, E=448, k=8, S=2,
+                I=1024, Is=1024, act="bf16", w_expert="bf16", seed=1, identity_proj=True),
 ]
 
 CONFIGS = {c.name: c for c in _LIST}

@@ -409,6 +409,69 @@ def pin_empty_batch():
     assert out["idx"].shape == (0, spec["k"])
 
 
+def pin_quantile_thresholds_library_and_brute_force():
+    """tau_e against numpy's own quantile (method 'linear') and against the
+    definition written out with a pure-Python sort of one column."""
+    rng = np.random.default_rng(71)
+    for T, E, k in ((1, 4, 2), (2, 5, 1), (37, 16, 2), (100, 7, 3), (64, 8, 8)):
+        s = rng.random((T, E))
+        tau = O.quantile_thresholds(s, k)
+        assert tau.shape == (E,)
+        close(tau, np.quantile(s, 1.0 - k / E, axis=0, method="linear"), rtol=0, atol=1e-15)
+        for e in range(E):
+            col = sorted(float(v) for v in s[:, e])
+            h = (T - 1) * (1.0 - k / E)
+            lo = math.floor(h)
+            hi = min(lo + 1, T - 1)
+            want = col[lo] + (h - lo) * (col[hi] - col[lo])
+            assert abs(tau[e] - want) <= 1e-15
+
+
+def pin_quantile_fair_share():
+    """About T k / E tokens score at or above each threshold: the count is
+    T - floor(h) (or one less where tau falls strictly between two order
+    statistics), with h = (T - 1)(1 - k/E), so it is within one of T k / E."""
+    rng = np.random.default_rng(72)
+    for T, E, k in ((500, 12, 3), (999, 9, 2), (64, 16, 4)):
+        s = rng.random((T, E))
+        tau = O.quantile_thresholds(s, k)
+        above = (s >= tau[None, :]).sum(axis=0)
+        h = (T - 1) * (1.0 - k / E)
+        assert np.all((above == T - math.floor(h)) | (above == T - math.floor(h) - 1))
+        assert np.all(np.abs(above - T * k / E) <= 1.0 + 1e-9)
+
+
+def pin_quantile_special_cases():
+    rng = np.random.default_rng(73)
+    s = rng.random((40, 6))
+    close(O.quantile_thresholds(s, 6), s.min(axis=0), rtol=0, atol=0)  # k = E: every token qualifies
+    close(O.quantile_thresholds(s[:1], 2), s[0], rtol=0, atol=0)       # one token
+    const = np.full((25, 5), 0.375)
+    close(O.quantile_thresholds(const, 2), np.full(5, 0.375), rtol=0, atol=0)
+    perm = rng.permutation(40)
+    close(O.quantile_thresholds(s[perm], 2), O.quantile_thresholds(s, 2), rtol=0, atol=0)
+    close(O.quantile_thresholds(s + 0.25, 2), O.quantile_thresholds(s, 2) + 0.25, rtol=0, atol=1e-15)
+    # the bias is minus the threshold of the sigmoid scores
+    lg = rng.standard_normal((30, 5)) * 2
+    close(O.quantile_bias(lg, 2), -np.quantile(scipy.special.expit(lg), 1 - 2 / 5, axis=0), rtol=0, atol=1e-15)
+
+
+def pin_quantile_bias_balances_a_skewed_router():
+    """With per-expert score offsets (a router that favours some experts), the
+    plain top-k piles tokens on the favoured experts; the quantile bias,
+    applied through the same selection, brings every expert within a factor
+    of 2 of T k / E (here the plain maximum is over 5 times that)."""
+    rng = np.random.default_rng(74)
+    T, E, k = 4000, 16, 2
+    logits = rng.standard_normal((T, E)) + np.linspace(-3, 3, E)[None, :]
+    s = O.sigmoid(logits)
+    plain = np.bincount(O.select_topk(s, k)[0].ravel(), minlength=E)
+    qb = np.bincount(O.select_topk(s + O.quantile_bias(logits, k)[None, :], k)[0].ravel(), minlength=E)
+    fair = T * k / E
+    assert plain.max() > 3 * fair
+    assert qb.max() < 2 * fair and qb.min() > 0.5 * fair
+
+
 PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]
 
 
@@ -514,6 +577,21 @@ def _mut_sigmoid_tanh(u):
     return np.tanh(u)
 
 
+def _mut_quantile_of_k_over_e(scores, k):
+    T, E = scores.shape
+    return np.quantile(scores, k / E, axis=0)
+
+
+def _mut_quantile_nearest_lower(scores, k):
+    T, E = scores.shape
+    h = (T - 1) * (1.0 - k / E)
+    return np.sort(scores, axis=0)[int(np.floor(h))]
+
+
+def _mut_quantile_bias_plus(logits, k):
+    return O.quantile_thresholds(O.sigmoid(logits), k)
+
+
 MUTANTS = {
     "situ_glu": [_mut_value_uncapped, _mut_gate_value_swapped],
     "silu": [_mut_silu_sign],
@@ -526,6 +604,8 @@ MUTANTS = {
     "shared_experts": [_mut_no_shared],
     "bf16_bits_to_f64": [_mut_bf16_truncates_low_byte],
     "sigmoid": [_mut_sigmoid_tanh],
+    "quantile_thresholds": [_mut_quantile_of_k_over_e, _mut_quantile_nearest_lower],
+    "quantile_bias": [_mut_quantile_bias_plus],
 }
 
 
