@@ -187,6 +187,25 @@ lmoe_status lmoe_combine_norm(const lmoe_shape *shape, const void *expert_out, c
 lmoe_status lmoe_up(const lmoe_shape *shape, const lmoe_weights *w, const void *n, const void *x,
                     void *y, void *ws, size_t ws_bytes, void *stream);
 
+/* Router logits only: logits [T, E] fp32 = x . W_r^T (products of act-dtype
+ * operands, fp32 accumulation), the first output of lmoe_route.  Needs
+ * w_router only; no workspace.                                                */
+lmoe_status lmoe_router_logits(const lmoe_shape *shape, const lmoe_weights *w, const void *x, float *logits,
+                               void *stream);
+
+/* Quantile Balancing thresholds (P3 Stable LatentMoE bullet: per-expert top-k
+ * thresholds solved for directly; P2 balancing passage: read off the batch's
+ * score distribution as each expert's fair share).  For each expert e, with
+ * its T scores s = sigmoid(logits[:, e]) (fp32) sorted ascending and
+ * h = (T - 1)(1 - k/E): tau_e = s_(floor h) + (h - floor h)(s_(floor h + 1) -
+ * s_(floor h)), so about T k / E tokens score at or above tau_e; bias [E] fp32
+ * receives -tau_e, the selection bias of lmoe_route / lmoe_forward that ranks
+ * each expert's scores against its threshold.  logits [T, E] fp32 device
+ * memory (e.g. from lmoe_router_logits); T >= 1.  The workspace (as for the
+ * layer) holds T * E keys.                                                     */
+lmoe_status lmoe_quantile_bias(const lmoe_shape *shape, const float *logits, float *bias, void *ws, size_t ws_bytes,
+                               void *stream);
+
 /* Packed routed-expert weights.  The expert GEMMs stream each 256-row by
  * 64-column tile of an expert matrix as one contiguous 32 KB block laid out
  * exactly as they stage it in on-chip memory, so every load is a dense 1 KB

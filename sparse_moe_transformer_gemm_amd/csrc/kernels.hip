@@ -284,4 +284,96 @@ hipError_t launch_combine_norm(bool bf16_act, const void* O, const int32_t* pos,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Quantile Balancing thresholds: tau_e = (1 - k/E) quantile over the batch of
+// expert e's sigmoid scores, linear between the order statistics floor(h) and
+// floor(h) + 1 with h = (T - 1)(1 - k/E); bias_e = -tau_e.
+// ---------------------------------------------------------------------------
+// Order-preserving fp32 <-> uint32 keys (unsigned key order = numeric order).
+__device__ __forceinline__ uint32_t f2key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key2f(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k); }
+
+// logits [T, E] -> keys [E, T] of sigmoid(logit), through a 64 x 64 LDS tile
+// (coalesced reads along E, coalesced writes along T).
+__global__ __launch_bounds__(256) void qb_keys_kernel(const float* logits, int64_t T, int E, uint32_t* keys) {
+  __shared__ uint32_t tile[64][65];
+  const int tid = threadIdx.x;
+  const int e0 = blockIdx.x * 64;
+  const int64_t t0 = (int64_t)blockIdx.y * 64;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = (tid >> 6) + 4 * i, c = tid & 63;
+    const int64_t t = t0 + r;
+    const int e = e0 + c;
+    if (t < T && e < E) tile[r][c] = f2key(1.f / (1.f + expf(-logits[t * E + e])));
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = (tid >> 6) + 4 * i, r = tid & 63;
+    const int64_t t = t0 + r;
+    const int e = e0 + c;
+    if (t < T && e < E) keys[(int64_t)e * T + t] = tile[r][c];
+  }
+}
+
+// One work-group per expert: the two order statistics by radix selection
+// (4 passes of 8 bits, most significant first) over the expert's keys.
+__global__ __launch_bounds__(256) void qb_select_kernel(const uint32_t* keys, int64_t T, int E, int k, float* bias) {
+  __shared__ uint32_t hist[256];
+  __shared__ int64_t rank_s;
+  __shared__ uint32_t bin_s;
+  const int tid = threadIdx.x;
+  const int e = blockIdx.x;
+  const uint32_t* col = keys + (int64_t)e * T;
+  const double h = (double)(T - 1) * (1.0 - (double)k / (double)E);
+  const int64_t lo = (int64_t)floor(h);
+  const int64_t hi = lo + 1 < T ? lo + 1 : T - 1;
+  uint32_t kv[2];
+  for (int which = 0; which < 2; ++which) {
+    int64_t r = which ? hi : lo;  // 0-based rank among the keys matching the prefix
+    uint32_t prefix = 0, mask = 0;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      hist[tid] = 0;
+      __syncthreads();
+      for (int64_t t = tid; t < T; t += 256) {
+        const uint32_t v = col[t];
+        if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int64_t cum = 0;
+        int b = 0;
+        while (b < 255 && cum + (int64_t)hist[b] <= r) cum += hist[b++];
+        rank_s = r - cum;
+        bin_s = (uint32_t)b;
+      }
+      __syncthreads();
+      prefix |= bin_s << shift;
+      mask |= 255u << shift;
+      r = rank_s;
+      __syncthreads();
+    }
+    kv[which] = prefix;
+  }
+  if (tid == 0) {
+    const double xl = key2f(kv[0]), xh = key2f(kv[1]);
+    bias[e] = (float)(-(xl + (h - (double)lo) * (xh - xl)));
+  }
+}
+
+hipError_t launch_quantile_bias(const float* logits, int64_t T, int E, int k, uint32_t* keys, float* bias,
+                                hipStream_t st) {
+  if (T <= 0 || (T + 63) / 64 > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(qb_keys_kernel, dim3((unsigned)((E + 63) / 64), (unsigned)((T + 63) / 64)), dim3(256), 0, st,
+                     logits, T, E, keys);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(qb_select_kernel, dim3((unsigned)E), dim3(256), 0, st, keys, T, E, k, bias);
+  return hipGetLastError();
+}
+
 }  // namespace lmoe

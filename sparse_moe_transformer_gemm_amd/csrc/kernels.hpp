@@ -22,4 +22,9 @@ hipError_t launch_tiles(const int32_t* offsets, int E, int bt_a, int4* tiles_a, 
 hipError_t launch_combine_norm(bool bf16, const void* O, const int32_t* pos, const float* w, const float* gamma,
                                int64_t T, int L, int k, float eps, void* n, hipStream_t st);
 
+// Quantile Balancing: bias[e] = -(1 - k/E) quantile of sigmoid(logits[:, e]);
+// keys: T * E uint32 scratch.
+hipError_t launch_quantile_bias(const float* logits, int64_t T, int E, int k, uint32_t* keys, float* bias,
+                                hipStream_t st);
+
 }  // namespace lmoe

@@ -623,6 +623,34 @@ lmoe_status lmoe_forward(const lmoe_shape* sh, const lmoe_weights* w, const void
   return LMOE_OK;
 }
 
+lmoe_status lmoe_router_logits(const lmoe_shape* sh, const lmoe_weights* w, const void* x, float* logits,
+                               void* stream) {
+  g_err[0] = 0;
+  if (lmoe_status s = check_shape(sh)) return s;
+  if (!w || !w->w_router) return fail(LMOE_EINVAL, "w_router is required");
+  if (sh->T == 0) return LMOE_OK;
+  if (!x || !logits) return fail(LMOE_EINVAL, "x and logits are required");
+  const Ctx c{sh, w, static_cast<hipStream_t>(stream)};
+  LMOE_HIP(bf16_act(sh) ? xgemm_any<bf16>(c, x, logits, nullptr, nullptr) : xgemm_any<float>(c, x, logits, nullptr,
+                                                                                               nullptr),
+           "router GEMM");
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_quantile_bias(const lmoe_shape* sh, const float* logits, float* bias, void* ws, size_t ws_bytes,
+                               void* stream) {
+  g_err[0] = 0;
+  if (lmoe_status s = check_shape(sh)) return s;
+  if (sh->T < 1) return fail(LMOE_EINVAL, "quantile thresholds need at least one token");
+  if ((sh->T + 63) / 64 > 65535) return fail(LMOE_EUNSUPPORTED, "T = %lld is too large", (long long)sh->T);
+  if (!logits || !bias) return fail(LMOE_EINVAL, "logits and bias are required");
+  if (lmoe_status s = check_ws(sh, ws, ws_bytes)) return s;
+  LMOE_HIP(launch_quantile_bias(logits, sh->T, sh->E, sh->k, at<uint32_t>(ws, plan(sh).logits), bias,
+                                static_cast<hipStream_t>(stream)),
+           "quantile thresholds");
+  return LMOE_OK;
+}
+
 size_t lmoe_packed_bytes(const lmoe_shape* sh) {
   if (check_shape(sh) != LMOE_OK) return 0;
   if (!(sh->act == LMOE_BF16 && sh->w_expert == LMOE_BF16)) return 0;

@@ -23,7 +23,8 @@ DTYPE_CODE = {"f32": F32, "bf16": BF16, "f8": F8E4M3}
 _TORCH = {F32: torch.float32, BF16: torch.bfloat16, F8E4M3: torch.float8_e4m3fn}
 
 EXPORTS = ("lmoe_validate", "lmoe_workspace_bytes", "lmoe_forward", "lmoe_route", "lmoe_permute",
-           "lmoe_expert_gemm", "lmoe_combine_norm", "lmoe_up", "lmoe_packed_bytes", "lmoe_pack_experts",
+           "lmoe_expert_gemm", "lmoe_combine_norm", "lmoe_up", "lmoe_router_logits", "lmoe_quantile_bias",
+           "lmoe_packed_bytes", "lmoe_pack_experts",
            "lmoe_status_str", "lmoe_last_error")
 
 
@@ -71,6 +72,8 @@ def load_library(path: str = LIB_PATH):
         "lmoe_expert_gemm": (ctypes.c_int, [sp, wp, vp, i32p, i32p, vp, vp, sz, vp]),
         "lmoe_combine_norm": (ctypes.c_int, [sp, vp, i32p, f32p, f32p, vp, vp]),
         "lmoe_up": (ctypes.c_int, [sp, wp, vp, vp, vp, vp, sz, vp]),
+        "lmoe_router_logits": (ctypes.c_int, [sp, wp, vp, f32p, vp]),
+        "lmoe_quantile_bias": (ctypes.c_int, [sp, f32p, f32p, vp, sz, vp]),
         "lmoe_packed_bytes": (sz, [sp]),
         "lmoe_pack_experts": (ctypes.c_int, [sp, wp, vp, sz, vp]),
         "lmoe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -133,6 +136,25 @@ def make_weights(sh: Shape, t: dict) -> Weights:
     w = Weights(**vals)
     w._keep = [t.get(n) for n in _WEIGHT_FIELDS]  # keep the tensors alive with the struct
     return w
+
+
+def router_logits(sh: Shape, w: Weights, x, out=None, stream=None):
+    """logits [T, E] fp32 = x . W_r^T."""
+    lib = load_library()
+    out = torch.empty((sh.T, sh.E), dtype=torch.float32, device=x.device) if out is None else out
+    _check(lib.lmoe_router_logits(ctypes.byref(sh), ctypes.byref(w), _ptr(x, _act_dtype(sh), "x"),
+                                  _ptr(out, torch.float32, "logits"), _stream(stream)))
+    return out
+
+
+def quantile_bias(sh: Shape, logits, out=None, ws=None, stream=None):
+    """Quantile Balancing selection bias [E] fp32 of a batch's router logits."""
+    lib = load_library()
+    out = torch.empty((sh.E,), dtype=torch.float32, device=logits.device) if out is None else out
+    ws = alloc_workspace(sh, logits.device) if ws is None else ws
+    _check(lib.lmoe_quantile_bias(ctypes.byref(sh), _ptr(logits, torch.float32, "logits"), _ptr(out, torch.float32, "bias"),
+                                  _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+    return out
 
 
 def packed_bytes(sh: Shape) -> int:

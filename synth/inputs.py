@@ -163,3 +163,15 @@ class LazyExperts:
 
     def __getitem__(self, e):
         return raw_numpy(self.t[int(e)])
+
+
+def make_router_logits(T: int, E: int, seed: int, spread: float = 0.0, std: float = 1.7) -> np.ndarray:
+    """Seeded fp32 router logits [T, E]: N(0, std^2) (std 1.7 is the logit
+    spread of the K3-shape router on N(0,1) inputs), plus a per-expert offset
+    growing linearly from -spread to +spread (a router that favours some
+    experts; 0: none)."""
+    rng = np.random.default_rng(derive_seed(seed, "router_logits", T * 4096 + E))
+    lg = rng.standard_normal((T, E)) * std
+    if spread:
+        lg = lg + np.linspace(-spread, spread, E)[None, :]
+    return lg.astype(np.float32)

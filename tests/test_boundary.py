@@ -217,3 +217,20 @@ def test_pack_experts_rejects_before_any_gpu_call(lib):
     assert "needed" in lmoe.last_error()
     f8 = k3(w_expert="f8")
     assert lib.lmoe_pack_experts(ctypes.byref(f8), ctypes.byref(fake_weights(f8)), buf, n, None) == 2
+
+
+def test_router_logits_and_quantile_bias_reject_before_any_gpu_call(lib):
+    sh = k3(T=64)
+    w = fake_weights(sh)
+    buf = ctypes.c_void_p(0x100000)
+    assert lib.lmoe_router_logits(ctypes.byref(sh), None, buf, buf, None) == 1
+    assert lib.lmoe_router_logits(ctypes.byref(sh), ctypes.byref(fake_weights(sh, w_router=None)), buf, buf, None) == 1
+    assert lib.lmoe_router_logits(ctypes.byref(sh), ctypes.byref(w), None, buf, None) == 1
+    sh0 = k3(T=0)
+    assert lib.lmoe_router_logits(ctypes.byref(sh0), ctypes.byref(w), None, None, None) == 0  # empty batch: no-op
+    need = lmoe.workspace_bytes(sh)
+    assert lib.lmoe_quantile_bias(ctypes.byref(sh0), buf, buf, buf, need, None) == 1  # needs a token
+    assert "at least one token" in lmoe.last_error()
+    assert lib.lmoe_quantile_bias(ctypes.byref(sh), None, buf, buf, need, None) == 1
+    assert lib.lmoe_quantile_bias(ctypes.byref(sh), buf, None, buf, need, None) == 1
+    assert lib.lmoe_quantile_bias(ctypes.byref(sh), buf, buf, buf, need - 1, None) == 3
