@@ -68,6 +68,16 @@ __device__ __forceinline__ i32x4 sload4(const int* p) {
   asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
   return v;
 }
+// Two uniform ints *a, *b in one round trip.
+__device__ __forceinline__ i32x2 sload_pair(const int* a, const int* b) {
+  int v0, v1;
+  asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(v0), "=&s"(v1)
+               : "s"(a), "s"(b)
+               : "memory");
+  i32x2 v = {v0, v1};
+  return v;
+}
 // Eight uniform ints p[idx[0..7]] (any addresses) in one round trip.
 __device__ __forceinline__ i32x8 sload_gather8(const int* p, const int (&idx)[8]) {
   int v0, v1, v2, v3, v4, v5, v6, v7;

@@ -318,6 +318,29 @@ struct ExpertGVProb {
     if (f8) *scrow = (val ? sv : sg) + ((int64_t)st.e * (I >> 7) + (u >> 7)) * (L >> 7);
     return (val ? wv : wg) + off;
   }
+  // e4m3 block scales of the 32-row blocks r0 + 32 i (i < N) at 128-column
+  // block kb: a block's rows are all gate or all value rows of one 128-unit
+  // block (read through the scalar cache).
+  template <int N>
+  __device__ void w_scales(const State& st, int r0, int kb, float (&sc)[N]) const {
+    const float* p[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int r = r0 + 32 * i, m = r & 63;
+      const int u = st.ft * (Cfg::BF / 2) + (r >> 6) * 32;
+      p[i] = (m >= 32 ? sv : sg) + ((int64_t)st.e * (I >> 7) + (u >> 7)) * (L >> 7) + kb;
+    }
+#pragma unroll
+    for (int i = 0; i < N; i += 2) {
+      if (i + 1 < N) {
+        const i32x2 v = sload_pair(reinterpret_cast<const int*>(p[i]), reinterpret_cast<const int*>(p[i + 1]));
+        sc[i] = __int_as_float(v.x);
+        sc[i + 1] = __int_as_float(v.y);
+      } else {
+        sc[i] = __int_as_float(sload1(reinterpret_cast<const int*>(p[i])));
+      }
+    }
+  }
   // k-tile 0 block of this tile in the packed layout (k-tile kt at + kt * 32 KB)
   __device__ const char* w_block(const State& st) const {
     if (!wpk) return nullptr;
@@ -363,6 +386,18 @@ struct ExpertDownProb {
   __device__ const char* w_block(const State& st) const {
     if (!wpk) return nullptr;
     return wpk + ((int64_t)st.e * et.nft + st.ft) * (int64_t)(I / 64) * kPackBlock;
+  }
+  // e4m3 block scales of the 32-row blocks r0 + 32 i at 128-column block kb.
+  // A wave's rows (r0 a multiple of its 64- or 128-row slab) lie in one
+  // 128-row block, so they share one scale.
+  template <int N>
+  __device__ void w_scales(const State& st, int r0, int kb, float (&sc)[N]) const {
+    static_assert(N * 32 <= 128, "a wave slab within one 128-row scale block");
+    const int f0 = st.ft * Cfg::BF + r0;
+    const float s = __int_as_float(
+        sload1(reinterpret_cast<const int*>(so + ((int64_t)st.e * (L >> 7) + (f0 >> 7)) * (I >> 7) + kb)));
+#pragma unroll
+    for (int i = 0; i < N; ++i) sc[i] = s;
   }
   template <class Acc>
   __device__ __forceinline__ void epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const;

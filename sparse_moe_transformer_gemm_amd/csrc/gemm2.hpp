@@ -50,25 +50,33 @@ struct Tile2 {
 // Dense GEMMs over many tokens / few tokens (weight streaming); experts
 // holding many rows, a few dozen rows, or one or two rows (decode).
 // Split-ring tile (gemm3_kernel below): weights three stages deep, tokens two.
-template <int BF_, int BT_, int WF_, int WT_, int WAUX_, int PERSIST_ = 0>
+template <int BF_, int BT_, int WF_, int WT_, int WAUX_, int PERSIST_ = 0, int WF8_ = 0, int SW_ = 3>
 struct Tile3 {
   static constexpr int BF = BF_, BT = BT_, WF = WF_, WT = WT_, WAUX = WAUX_;
   // PERSIST: a grid of resident work-groups walks the tile list with one
   // continuous DMA pipeline (gemm3p_kernel) instead of one tile per group
   static constexpr int PERSIST = PERSIST_;
+  // WF8: e4m3 weights staged as such (64 bytes per row per 64-column k-tile)
+  // and widened to bf16 with their block scale at the fragment load
+  static constexpr int WF8 = WF8_;
+  static constexpr int SW = SW_, SX = 2;  // weight / token ring depths
+  static constexpr int RBW = WF8 ? 64 : 128;              // weight row bytes per k-tile
+  static constexpr int RPIW = 1024 / RBW;                 // weight rows per DMA instruction
   static constexpr int NT = WF * WT * kWave, NW = WF * WT;
   static constexpr int FW = BF / WF, TW = BT / WT;
   static constexpr int FI = FW / 32, TI = TW / 32;
-  static constexpr int QW = BF / 8, QX = BT / 8;
+  static constexpr int QW = BF / RPIW, QX = BT / 8;
   static constexpr int NQW = QW / NW, NQX = QX / NW;
-  static constexpr int SW = 3, SX = 2;
-  static constexpr int X_OFF = SW * BF * 128;
-  static constexpr int LDS = SW * BF * 128 + SX * BT * 128;
+  static constexpr int WSTAGE = BF * RBW;
+  static constexpr int X_OFF = SW * WSTAGE;
+  static constexpr int LDS = SW * WSTAGE + SX * BT * 128;
   static constexpr bool kDma = true;
   static constexpr int kKind = PERSIST ? 4 : 3;
   static_assert(FW % 64 == 0 && TW % 32 == 0, "wave tile");
   static_assert(QW % NW == 0 && QX % NW == 0, "DMA instructions split evenly over the waves");
   static_assert(NQW <= 63, "vmcnt range");
+  static_assert(SW >= 3, "the weight ring runs at least two k-tiles ahead");
+  static_assert(PERSIST || (!WF8 && SW == 3), "one-tile-per-group kernel: bf16 weights, three stages");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
@@ -88,6 +96,14 @@ struct Tile3 {
 #ifndef LMOE_T_EXPERT_DN
 #define LMOE_T_EXPERT_DN Tile3<256, 256, 4, 4, 0, 1>
 #endif
+// e4m3 expert weights with bf16 activations (many rows per expert): half the
+// weight bytes per stage, so a five-deep weight ring fits beside the tokens.
+#ifndef LMOE_T_EXPERT_GV_F8
+#define LMOE_T_EXPERT_GV_F8 Tile3<256, 256, 4, 4, 0, 1, 1, 5>
+#endif
+#ifndef LMOE_T_EXPERT_DN_F8
+#define LMOE_T_EXPERT_DN_F8 Tile3<256, 256, 4, 4, 0, 1, 1, 5>
+#endif
 #ifndef LMOE_T_MID_GV
 #define LMOE_T_MID_GV Tile2<256, 64, 4, 1, 3, 0>
 #endif
@@ -104,11 +120,14 @@ typedef LMOE_T_DENSE T2Dense;
 typedef LMOE_T_THIN T2Thin;
 typedef LMOE_T_EXPERT_GV T2ExpertGV;
 typedef LMOE_T_EXPERT_DN T2ExpertDn;
+typedef LMOE_T_EXPERT_GV_F8 T2ExpertGVF8;
+typedef LMOE_T_EXPERT_DN_F8 T2ExpertDnF8;
 typedef LMOE_T_MID_GV T2MidGV;
 typedef LMOE_T_MID_DN T2MidDn;
 typedef LMOE_T_SMALL_GV T2SmallGV;
 typedef LMOE_T_SMALL_DN T2SmallDn;
-static_assert(T2ExpertGV::BT == T2ExpertDn::BT && T2MidGV::BT == T2MidDn::BT && T2SmallGV::BT == T2SmallDn::BT,
+static_assert(T2ExpertGV::BT == T2ExpertDn::BT && T2MidGV::BT == T2MidDn::BT && T2SmallGV::BT == T2SmallDn::BT &&
+                  T2ExpertGVF8::BT == T2ExpertDnF8::BT && T2ExpertGVF8::WF8 && T2ExpertDnF8::WF8,
               "expert GEMMs of one size class share the token tile");
 static_assert(T2ExpertGV::BF == kPackRows && T2ExpertDn::BF == kPackRows && T2MidGV::BF == kPackRows &&
                   T2MidDn::BF == kPackRows && T2SmallGV::BF == kPackRows && T2SmallDn::BF == kPackRows,
@@ -125,6 +144,9 @@ static_assert(T2ExpertGV::BF == kPackRows && T2ExpertDn::BF == kPackRows && T2Mi
 #define LMOE_SWZ 1
 #endif
 __device__ __forceinline__ int swz(int r) { return LMOE_SWZ == 1 ? ((r >> 1) & 7) : LMOE_SWZ == 2 ? (r & 7) : 0; }
+// 64-byte rows (e4m3 weights, 4 chunks): chunk c of row r at position
+// c ^ ((r >> 2) & 3), so 16 consecutive rows of one chunk hit distinct banks.
+__device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
 
 // 16 bytes per lane from `g` into LDS at `lds` + 16 * lane (lds wave-uniform).
 // A __device__ function, not a lambda: lambdas are also compiled for the host,
@@ -218,6 +240,42 @@ __device__ __forceinline__ void mma_ktile(f32x16 (&acc)[FI][TI], const char* sW,
 #pragma unroll
         for (int i = 0; i < FI; ++i) acc[i][j] = mfma32(a[cur][i], b[cur][j], acc[i][j]);
       }
+  }
+}
+
+// As mma_ktile, with the weight operand as e4m3 codes (64-byte rows): lane l
+// reads the 8 codes of k-step ks, half l / 32 of chunk ks, and widens them to
+// bf16 times the block scale sc[i] of its 32-row block (rounding as the
+// register-staged path does).  Raw codes are double-buffered across k-steps.
+template <int FI, int TI>
+__device__ __forceinline__ void mma_ktile_f8(f32x16 (&acc)[FI][TI], const char* sW, const char* sX, int wf0, int wt0,
+                                             int lane, int tiv, const float (&sc)[FI]) {
+  const int lr = lane & 31;
+  const int sw = swz(lr), sw64 = swz64(lr);  // fragment row offsets are multiples of 32
+  const char* pw = sW + (wf0 + lr) * 64 + ((lane >> 5) << 3);
+  const char* px = sX + (wt0 + lr) * 128;
+  uint2 q[2][FI];
+  auto loadw = [&](int ks, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FI; ++i) q[buf][i] = *reinterpret_cast<const uint2*>(pw + i * 32 * 64 + ((ks ^ sw64) << 4));
+  };
+  loadw(0, 0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks + 1 < 4) loadw(ks + 1, (ks + 1) & 1);
+    const int ch = ((2 * ks + (lane >> 5)) ^ sw) << 4;
+    bf16x8 b[TI];
+#pragma unroll
+    for (int j = 0; j < TI; ++j)
+      if (j < tiv) b[j] = *reinterpret_cast<const bf16x8*>(px + j * 32 * 128 + ch);
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const uint4 w = widen_e4m3(q[ks & 1][i], sc[i]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&w);
+#pragma unroll
+      for (int j = 0; j < TI; ++j)
+        if (j < tiv) acc[i][j] = mfma32(a, b[j], acc[i][j]);
+    }
   }
 }
 
@@ -497,15 +555,16 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
   };
   zero();
 
-  // weight issue side
+  // weight issue side (bf16 rows: 8 rows of 128 bytes per DMA instruction;
+  // e4m3 rows: 16 rows of 64 bytes)
   typename Prob::State wst = cst;
   int wj = 0, wsg = first_seg, wk = 0;
   const char* srcW[NQW];
   const char* wblk = nullptr;
-  int64_t wstep = 128;
+  int64_t wstep = Cfg::RBW;
   auto set_w = [&]() __attribute__((always_inline)) {
-    wblk = p.w_block(wst);
-    wstep = wblk ? kPackBlock : 128;
+    wblk = Cfg::WF8 ? nullptr : p.w_block(wst);
+    wstep = wblk ? kPackBlock : Cfg::RBW;
     const float* dummy = nullptr;
     const char* w0 = p.w_row(wst, wsg, 0, &dummy);
 #pragma unroll
@@ -514,9 +573,11 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
       if (wblk) {
         srcW[i] = wblk + q * 1024 + lane * 16;
       } else {
-        const int row = q * 8 + (lane >> 3);
+        constexpr int CPR = Cfg::RBW / 16;
+        const int row = q * Cfg::RPIW + lane / CPR;
+        const int chunk = (lane % CPR) ^ (Cfg::WF8 ? swz64(row) : swz(row));
         const char* rp = p.w_row(wst, wsg, row, &dummy);
-        srcW[i] = (rp ? rp : w0) + (((lane & 7) ^ swz(row)) << 4);
+        srcW[i] = (rp ? rp : w0) + (chunk << 4);
       }
     }
   };
@@ -539,7 +600,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
   set_w();
   set_x();
   auto issue_w = [&](int buf) __attribute__((always_inline)) {
-    char* base = smem + buf * Cfg::BF * 128;
+    char* base = smem + buf * Cfg::WSTAGE;
 #pragma unroll
     for (int i = 0; i < NQW; ++i) dma16<Cfg::WAUX>(srcW[i] + wk * wstep, base + (wid + NW * i) * 1024);
     if (++wk == p.seg_ktiles(wsg)) {
@@ -568,12 +629,22 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
     }
   };
 
+  // prologue: X(0), then W(0) .. W(SW-2); iteration g issues X(g+1) then
+  // W(g+SW-1).  At the top of iteration g the DMAs issued after X(g) are the
+  // weight tile W(g+SW-2) alone (NQW instructions, all older weight tiles
+  // precede X(g) or are older still), so vmcnt(NQW) completes X(g) and W(g);
+  // once W(g+SW-2) no longer exists the wait is vmcnt(0).
+  constexpr int SW = Cfg::SW;
   issue_x(0);
-  issue_w(0);
-  if (G > 1) issue_w(1);
+#pragma unroll
+  for (int s = 0; s < SW - 1; ++s)
+    if (s < G) issue_w(s);
+  float sc[FI];
+#pragma unroll
+  for (int i = 0; i < FI; ++i) sc[i] = 1.f;
   bool pending = false;  // a finished tile's accumulators await their epilogue
   for (int g = 0; g < G; ++g) {
-    if (g + 1 < G) wait_vmcnt_barrier<NQW>();
+    if (g + SW - 2 < G) wait_vmcnt_barrier<NQW>();
     else wait_vmcnt_barrier<0>();
     if (pending) {
       p.epilogue(cst, acc, wf0, wt0, lane);
@@ -584,10 +655,17 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
       pending = false;
     }
     if (g + 1 < G) issue_x((g + 1) & 1);
-    if (g + 2 < G) issue_w((g + 2) % 3);
-    if (active)
-      mma_ktile<FI, TI, false>(acc, smem + (g % 3) * Cfg::BF * 128, smem + Cfg::X_OFF + (g & 1) * Cfg::BT * 128, wf0,
-                               wt0, lane, tiv);
+    if (g + SW - 1 < G) issue_w((g + SW - 1) % SW);
+    if (active) {
+      const char* sW = smem + (g % SW) * Cfg::WSTAGE;
+      const char* sX = smem + Cfg::X_OFF + (g & 1) * Cfg::BT * 128;
+      if constexpr (Cfg::WF8) {
+        if ((ckt & 1) == 0) p.w_scales(cst, wf0, ckt >> 1, sc);  // one scale per 128 columns
+        mma_ktile_f8<FI, TI>(acc, sW, sX, wf0, wt0, lane, tiv, sc);
+      } else {
+        mma_ktile<FI, TI, false>(acc, sW, sX, wf0, wt0, lane, tiv);
+      }
+    }
     if (++ckt == nkt) {
       ckt = 0;
       pending = true;

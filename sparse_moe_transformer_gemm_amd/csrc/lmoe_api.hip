@@ -112,6 +112,11 @@ lmoe_status check_weights(const lmoe_shape* sh, const lmoe_weights* w, unsigned 
 // pipeline (gemm2.hpp); fp32 layers and e4m3 weights run the register-staged
 // mainloop (gemm.hpp), which widens e4m3 codes on the way into LDS.
 bool use_dma(const lmoe_shape* sh) { return sh->act == LMOE_BF16 && sh->w_expert == LMOE_BF16; }
+// e4m3 expert weights with bf16 activations and many rows per expert: the
+// persistent LDS-DMA expert GEMMs with the codes widened at the fragment load.
+bool use_dma_f8(const lmoe_shape* sh) {
+  return sh->act == LMOE_BF16 && sh->w_expert == LMOE_F8E4M3 && sh->T * (int64_t)sh->k >= 96 * (int64_t)sh->E;
+}
 
 // Experts: token tile by the mean rows per expert (T*k/E).
 enum ExpertTile { ET_SMALL, ET_MID, ET_BIG };
@@ -125,6 +130,7 @@ ExpertTile expert_tile(const lmoe_shape* sh) {
   return tk < 48 * (int64_t)sh->E ? ET_SMALL : ET_BIG;
 }
 int expert_bt(const lmoe_shape* sh) {
+  if (use_dma_f8(sh)) return T2ExpertGVF8::BT;
   const ExpertTile t = expert_tile(sh);
   if (use_dma(sh)) return t == ET_SMALL ? T2SmallGV::BT : t == ET_MID ? T2MidGV::BT : T2ExpertGV::BT;
   return t == ET_SMALL ? CfgSmall::BT : CfgBig::BT;
@@ -416,6 +422,7 @@ hipError_t expert_gv_any(const Ctx& c, const void* z, const int32_t* offsets, co
                          const int4* tiles, const int32_t* tcount, void* act) {
   const ExpertTile t = expert_tile(c.sh);
   if constexpr (sizeof(CT) == 2) {
+    if (use_dma_f8(c.sh)) return expert_gv<T2ExpertGVF8, CT>(c, z, offsets, sorted, tiles, tcount, act);
     if (use_dma(c.sh)) {
       if (t == ET_SMALL) return expert_gv<T2SmallGV, CT>(c, z, offsets, sorted, tiles, tcount, act);
       if (t == ET_MID) return expert_gv<T2MidGV, CT>(c, z, offsets, sorted, tiles, tcount, act);
@@ -430,6 +437,7 @@ hipError_t expert_down_any(const Ctx& c, const void* act, const int32_t* offsets
                            const int32_t* tcount, void* out) {
   const ExpertTile t = expert_tile(c.sh);
   if constexpr (sizeof(CT) == 2) {
+    if (use_dma_f8(c.sh)) return expert_down<T2ExpertDnF8, CT>(c, act, offsets, tiles, tcount, out);
     if (use_dma(c.sh)) {
       if (t == ET_SMALL) return expert_down<T2SmallDn, CT>(c, act, offsets, tiles, tcount, out);
       if (t == ET_MID) return expert_down<T2MidDn, CT>(c, act, offsets, tiles, tcount, out);

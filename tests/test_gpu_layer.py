@@ -55,11 +55,14 @@ def test_forward_small(dev, name):
         assert np.abs(forced["z"] @ O.decode(inp["w_gate"][0], "f32").T).max() > 300
 
 
-@pytest.mark.parametrize("T", [20, 300, 700, 2000])
-def test_forward_tile_variants(dev, T):
+@pytest.mark.parametrize("name,T", [("small_bf16", 20), ("small_bf16", 300), ("small_bf16", 700),
+                                    ("small_bf16", 2000), ("small_fp8", 700), ("small_fp8", 2000)])
+def test_forward_tile_variants(dev, name, T):
     """Token counts that select each kernel tile: thin / dense x- and up-GEMMs,
-    small / mid / big expert token tiles (experts with 1-3, ~50, ~330 rows)."""
-    cfg = replace(get_config("small_bf16"), T=T, name=f"small_bf16_T{T}")
+    small / mid / big expert token tiles (experts with 1-3, ~50, ~330 rows);
+    with e4m3 expert weights, the register-staged tiles at T=300 and the
+    LDS-DMA tiles that widen codes at the fragment load from T=700 on."""
+    cfg = replace(get_config(name), T=T, name=f"{name}_T{T}")
     note(f"[forward] {cfg.name}")
     t, g = make_case(cfg, dev)
     sh, w = _weights(cfg, g)
