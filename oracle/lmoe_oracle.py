@@ -99,6 +99,55 @@ def dequant_blocks(codes, scales):
     return q * np.repeat(np.repeat(s, F8_BLOCK, axis=0), F8_BLOCK, axis=1)
 
 
+def e4m3fn_encode(v):
+    """float -> OCP e4m3fn code: the nearest finite value, a tie going to the
+    code with an even mantissa (round to nearest even), magnitudes beyond 448
+    saturated to 448.  The sign bit is the sign of v, so a negative value
+    that rounds to zero gives the negative zero 0x80.  NaN -> 0x7F."""
+    v = np.asarray(v, dtype=np.float64)
+    pos = E4M3FN[:0x7F]  # codes 0 .. 126: every positive finite value, ascending
+    a = np.minimum(np.abs(v), pos[-1])
+    hi = np.clip(np.searchsorted(pos, a, side="left"), 1, 0x7E)
+    lo = hi - 1
+    dlo, dhi = a - pos[lo], pos[hi] - a
+    code = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(a == pos[hi], hi, code)
+    code = code.astype(np.uint8) | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
+    return np.where(np.isnan(v), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def quantize_1x128(v):
+    """Activation quantisation of the W8A8 expert GEMMs (per-token 1x128
+    blocks; the pages name the BF16/FP8 dynamic-range problem, P3 merged
+    summary, and fix no format).  Each row is cut into blocks of 128
+    consecutive columns; a block's scale is amax / 448 (1 for an all-zero
+    block) and its codes are e4m3fn(v / scale).  The value enters as fp32 and
+    the scale and quotient are fp32 operations, the precision the kernel
+    decides the codes in.  Returns codes [R, C] uint8, scales [R, C/128]
+    float32; value = code * scale."""
+    v32 = np.asarray(v, dtype=np.float64).astype(np.float32)
+    R, C = v32.shape
+    if C % F8_BLOCK:
+        raise ValueError("the quantised width must be a multiple of 128")
+    blocks = v32.reshape(R, C // F8_BLOCK, F8_BLOCK)
+    amax = np.abs(blocks).max(axis=2, initial=np.float32(0))
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = (blocks / scale[:, :, None]).astype(np.float32)
+    return e4m3fn_encode(q).reshape(R, C), scale
+
+
+def dequant_rows(codes, scales):
+    """e4m3fn codes [R, C] with one fp32 scale per row per 128 columns -> float64."""
+    q = e4m3fn_to_f64(codes)
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    return q * np.repeat(s, F8_BLOCK, axis=1)
+
+
+def fp8_activations(v):
+    """The values a W8A8 expert GEMM multiplies: v quantised 1x128, decoded."""
+    return dequant_rows(*quantize_1x128(v))
+
+
 def matrix(stack, scales, idx, tag):
     """Decoded fp64 matrix idx of a stacked weight tensor (experts or shared
     experts).  `stack` may be any indexable whose items are raw arrays."""
@@ -246,11 +295,13 @@ def permute(idx, E):
     return offsets, sorted_, pos
 
 
-def expert_ffn(zrows, wg, wv, wo, c):
+def expert_ffn(zrows, wg, wv, wo, c, a8=False):
     """One routed expert on its latent rows: gated FFN with gate and value
-    branches (P2 stabilizer passage) and the SiTU-GLU activation."""
+    branches (P2 stabilizer passage) and the SiTU-GLU activation.  With a8
+    (W8A8) the SiTU-GLU output is quantised 1x128 before the down GEMM; the
+    caller passes rows already quantised for the gate/value GEMM."""
     a = situ_glu(zrows @ wg.T, zrows @ wv.T, c)
-    return a, a @ wo.T
+    return a, (fp8_activations(a) if a8 else a) @ wo.T
 
 
 def combine(O, pos, w):
@@ -286,7 +337,9 @@ def forward(inp, spec, forced_idx=None, forced_tol=1e-3):
     w_router, b_router, w_down, w_gate, w_value, w_out, s_gate, s_value,
     s_out, gamma, w_up, ws_gate, ws_value, ws_out, ss_gate, ss_value, ss_out
     (expert stacks may be any indexable over experts).  `spec` gives act,
-    w_expert, k, cap, eps.  Returns every intermediate as float64/int64.
+    w_expert, k, cap, eps and optionally a8 (W8A8 routed experts: their
+    activations quantised 1x128 to e4m3fn, see quantize_1x128).  Returns
+    every intermediate as float64/int64 (A before any quantisation).
 
     Steps: route on x; z = latent down-projection of x; tokens grouped by
     expert; each expert's SiTU-GLU FFN on its latent rows; weighted combine;
@@ -294,6 +347,7 @@ def forward(inp, spec, forced_idx=None, forced_tol=1e-3):
     LatentMoE passage and stabilizer passage; P3 LatentMoE bullets)."""
     act, wt = spec["act"], spec["w_expert"]
     k, c, eps = int(spec["k"]), float(spec["cap"]), float(spec["eps"])
+    a8 = bool(spec.get("a8", False))
     x = decode(inp["x"], act)
     w_router = decode(inp["w_router"], act)
     b = np.asarray(inp["b_router"], dtype=np.float32).astype(np.float64)
@@ -311,6 +365,8 @@ def forward(inp, spec, forced_idx=None, forced_tol=1e-3):
 
     z = latent_down(x, w_down)
     L = z.shape[1]
+    # W8A8: each token's latent row is quantised once, whatever expert reads it
+    zx = fp8_activations(z) if a8 else z
     offsets, sorted_, pos = permute(idx, E)
     I = None
     A = None
@@ -323,7 +379,7 @@ def forward(inp, spec, forced_idx=None, forced_tol=1e-3):
         wg = matrix(inp["w_gate"], inp.get("s_gate"), e, wt)
         wv = matrix(inp["w_value"], inp.get("s_value"), e, wt)
         wo = matrix(inp["w_out"], inp.get("s_out"), e, wt)
-        a, o = expert_ffn(z[toks], wg, wv, wo, c)
+        a, o = expert_ffn(zx[toks], wg, wv, wo, c, a8)
         if A is None:
             I = a.shape[1]
             A = np.zeros((T * k, I))

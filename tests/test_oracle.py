@@ -472,6 +472,112 @@ def pin_quantile_bias_balances_a_skewed_router():
     assert qb.max() < 2 * fair and qb.min() > 0.5 * fair
 
 
+def pin_e4m3fn_encode():
+    """Rounding to e4m3fn against torch's own conversion, plus what the format
+    fixes: every finite value encodes to its own code, midpoints go to the
+    even code, magnitudes past 448 saturate, the sign survives rounding to 0."""
+    rng = np.random.default_rng(81)
+    v = rng.standard_normal(50000) * np.exp(rng.uniform(-14, 7, 50000))
+    want = torch.from_numpy(np.clip(v, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3fn_encode(v), want)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(O.e4m3fn_encode(O.E4M3FN[codes]), codes)
+    pos = O.E4M3FN[:0x7F]
+    mid = (pos[:-1] + pos[1:]) / 2
+    got = O.e4m3fn_encode(mid).astype(np.int64)
+    lo = np.arange(0x7E)
+    assert np.array_equal(got, np.where(lo % 2 == 0, lo, lo + 1))
+    assert np.array_equal(O.e4m3fn_encode(np.nextafter(mid, 0)), lo.astype(np.uint8))
+    assert np.array_equal(O.e4m3fn_encode(np.nextafter(mid, 1e9)), (lo + 1).astype(np.uint8))
+    assert list(O.e4m3fn_encode([500.0, -1e9, -1e-9, np.nan])) == [0x7E, 0xFE, 0x80, 0x7F]
+
+
+def pin_quantize_1x128_round_trip():
+    """Values built as code * 2^m with a 448 in every block come back as the
+    same codes and scale 2^m exactly; an all-zero block gets scale 1; scaling
+    one block by a power of two scales only that block's scale."""
+    rng = np.random.default_rng(82)
+    R, nb = 6, 3
+    codes = rng.integers(0, 256, (R, nb * 128)).astype(np.uint8)
+    codes[codes & 0x7F == 0x7F] = 0x11  # no NaN codes
+    codes[:, ::128] = np.where(rng.random((R, nb)) < 0.5, 0x7E, 0xFE)  # +-448 in each block
+    m = rng.integers(-20, 6, (R, nb))
+    v = O.E4M3FN[codes] * np.repeat(2.0 ** m, 128, axis=1)
+    q, sc = O.quantize_1x128(v)
+    assert sc.dtype == np.float32 and sc.shape == (R, nb)
+    assert np.array_equal(q, codes) and np.array_equal(sc, (2.0 ** m).astype(np.float32))
+    v2 = v.copy()
+    v2[2, 128:256] *= 2.0 ** -7
+    v2[4, :128] = 0.0
+    q2, sc2 = O.quantize_1x128(v2)
+    assert sc2[2, 1] == sc[2, 1] * 2.0 ** -7 and np.array_equal(q2[2], q[2])
+    assert sc2[4, 0] == 1.0 and not q2[4, :128].any()
+    keep = np.ones((R, nb), bool)
+    keep[2, 1] = keep[4, 0] = False
+    assert np.array_equal(sc2[keep], sc[keep])
+
+
+def pin_quantize_1x128_error_bound():
+    """Each block's largest magnitude maps to +-448, scale = fp32(amax / 448),
+    and the decoded error is at most half an e4m3 step (2^-4 relative for
+    normal codes, 2^-10 scale below them)."""
+    rng = np.random.default_rng(83)
+    v = rng.standard_normal((5, 384)) * np.exp(rng.uniform(-6, 6, (5, 384)))
+    q, sc = O.quantize_1x128(v)
+    v32 = v.astype(np.float32).astype(np.float64)
+    blocks = np.abs(v32).reshape(5, 3, 128)
+    amax = blocks.max(axis=2)
+    assert np.array_equal(sc, (amax.astype(np.float32) / np.float32(448)).astype(np.float32))
+    arg = blocks.argmax(axis=2)
+    for r in range(5):
+        for b in range(3):
+            assert q[r, b * 128 + arg[r, b]] & 0x7F == 0x7E
+    deq = O.dequant_rows(q, sc)
+    scale = np.repeat(sc.astype(np.float64), 128, axis=1)
+    err = np.abs(deq - v32)
+    normal = np.abs(v32) / scale >= 2.0 ** -6
+    assert np.all(err[normal] <= 2.0 ** -4 * np.abs(v32[normal]) * (1 + 1e-6))
+    assert np.all(err[~normal] <= 2.0 ** -10 * scale[~normal] * (1 + 1e-6))
+
+
+def _a8_layer(seed, T=7, **kw):
+    base = dict(H=128, L=128, E=4, k=2, S=1, I=128, Is=128)
+    base.update(kw)
+    inp, spec = rand_layer(seed, T=T, wstd=0.1, **base)
+    return inp, dict(spec, a8=True)
+
+
+def pin_a8_single_expert_written_out():
+    """E = k = 1, identity projections, no shared expert, W_o = identity: the
+    layer is RMSNorm of the quantised SiTU-GLU output of the quantised input,
+    written here with numpy and the pinned quantiser only."""
+    inp, spec = _a8_layer(84, T=5, E=1, k=1, S=0)
+    inp["w_down"] = inp["w_up"] = None
+    inp["w_out"] = np.eye(128)[None]
+    gamma = inp["gamma"].astype(np.float64)
+    xq = O.dequant_rows(*O.quantize_1x128(inp["x"]))
+    g = xq @ inp["w_gate"][0].T
+    vv = xq @ inp["w_value"][0].T
+    capg, capv = 100 * np.tanh(g / 100), 100 * np.tanh(vv / 100)
+    a = capg / (1 + np.exp(-capg)) * capv
+    aq = O.dequant_rows(*O.quantize_1x128(a))
+    want = gamma * aq / np.sqrt(np.mean(aq * aq, axis=1, keepdims=True) + spec["eps"])
+    close(O.forward(inp, spec)["y"], want, rtol=1e-10, atol=1e-12)
+
+
+def pin_a8_row_independence_and_bounded_change():
+    """W8A8 quantises each token on its own, so rows stay independent; the
+    output moves from the unquantised layer's by a few percent, not zero."""
+    inp, spec = _a8_layer(85, T=9)
+    full = O.forward(inp, spec)
+    sub = dict(inp, x=inp["x"][[6, 1, 3]])
+    close(O.forward(sub, spec)["y"], full["y"][[6, 1, 3]], rtol=1e-10, atol=1e-12)
+    ref = O.forward(inp, dict(spec, a8=False))
+    assert np.array_equal(full["idx"], ref["idx"])
+    rel = np.abs(full["y"] - ref["y"]).max(axis=1) / np.abs(ref["y"]).max(axis=1)
+    assert rel.max() < 0.1 and rel.min() > 1e-4
+
+
 PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]
 
 
@@ -592,7 +698,45 @@ def _mut_quantile_bias_plus(logits, k):
     return O.quantile_thresholds(O.sigmoid(logits), k)
 
 
+def _mut_encode_truncates(v):
+    v = np.asarray(v, dtype=np.float64)
+    pos = O.E4M3FN[:0x7F]
+    a = np.minimum(np.abs(v), pos[-1])
+    code = (np.searchsorted(pos, a, side="right") - 1).astype(np.uint8)
+    return np.where(np.isnan(v), 0x7F, code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def _mut_quantize_per_row(v):
+    v32 = np.asarray(v, dtype=np.float64).astype(np.float32)
+    R, C = v32.shape
+    amax = np.abs(v32).max(axis=1, keepdims=True)
+    scale = np.where(amax > 0, amax / np.float32(448), np.float32(1)).astype(np.float32)
+    return O.e4m3fn_encode(v32 / scale), np.repeat(scale, C // 128, axis=1)
+
+
+def _mut_quantize_e4m3_max_240(v):
+    v32 = np.asarray(v, dtype=np.float64).astype(np.float32)
+    R, C = v32.shape
+    b = v32.reshape(R, C // 128, 128)
+    amax = np.abs(b).max(axis=2)
+    scale = np.where(amax > 0, amax / np.float32(240), np.float32(1)).astype(np.float32)
+    return O.e4m3fn_encode(b / scale[:, :, None]).reshape(R, C), scale
+
+
+def _mut_fp8_activations_skipped(v):
+    return np.asarray(v, dtype=np.float64)
+
+
+def _mut_expert_ffn_a_not_quantised(zrows, wg, wv, wo, c, a8=False):
+    a = O.situ_glu(zrows @ wg.T, zrows @ wv.T, c)
+    return a, a @ wo.T
+
+
 MUTANTS = {
+    "e4m3fn_encode": [_mut_encode_truncates],
+    "quantize_1x128": [_mut_quantize_per_row, _mut_quantize_e4m3_max_240],
+    "fp8_activations": [_mut_fp8_activations_skipped],
+    "expert_ffn": [_mut_expert_ffn_a_not_quantised],
     "situ_glu": [_mut_value_uncapped, _mut_gate_value_swapped],
     "silu": [_mut_silu_sign],
     "rmsnorm": [_mut_norm_no_gamma, _mut_norm_sum_not_mean],
