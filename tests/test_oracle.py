@@ -540,6 +540,49 @@ def pin_quantize_1x128_error_bound():
     assert np.all(err[~normal] <= 2.0 ** -10 * scale[~normal] * (1 + 1e-6))
 
 
+def pin_bf16_round():
+    """Against torch's float32 -> bf16 conversion (one rounding of an exact
+    float32), and at ties: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 and
+    goes to 1 (even), 1 + 3 * 2^-8 goes to 1 + 2^-6; a hair past a tie goes up."""
+    rng = np.random.default_rng(86)
+    v = (rng.standard_normal(40000) * np.exp(rng.uniform(-30, 30, 40000))).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(O.bf16_round(v.astype(np.float64)), want)
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 1 + 2.0 ** -8 + 2.0 ** -40])
+    assert list(O.bf16_round(ties)) == [1.0, 1 + 2.0 ** -6, -1.0, 1 + 2.0 ** -7]
+    assert O.round_to_act(np.array([1 + 2.0 ** -30]), "f32")[0] == 1.0
+    assert O.round_to_act(np.array([1 + 2.0 ** -30]), "f64")[0] == 1 + 2.0 ** -30
+
+
+def pin_a8_quantises_the_stored_activation():
+    """A bf16 layer's W8A8 path quantises z as the bf16 tensor holds it: the
+    quantiser applied to z itself and to its bf16 rounding differ on some
+    blocks of this layer, and the forward follows the rounded one."""
+    inp, spec = _a8_layer(87, T=6, E=1, k=1, S=0)
+    inp["w_down"] = inp["w_up"] = None
+    inp["w_out"] = np.eye(128)[None]
+    x = inp["x"] + 2.0 ** -9 * np.sign(inp["x"])  # values near bf16 rounding ties
+    inp["x"] = x
+    spec = dict(spec, act="bf16")
+    inp_bf = dict(inp, x=O.bf16_round(x))
+    to_bits = lambda a: (torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+                         .astype(np.uint16))
+    got = O.forward(dict(inp, x=to_bits(O.bf16_round(x))), spec)["y"]
+    ref = O.forward(dict(inp_bf, x=to_bits(inp_bf["x"])), spec)["y"]
+    close(got, ref, rtol=0, atol=0)
+    zq_direct = O.dequant_rows(*O.quantize_1x128(x))
+    zq_stored = O.dequant_rows(*O.quantize_1x128(O.bf16_round(x)))
+    assert not np.array_equal(zq_direct, zq_stored)
+    g = zq_stored @ inp["w_gate"][0].T
+    vv = zq_stored @ inp["w_value"][0].T
+    capg, capv = 100 * np.tanh(g / 100), 100 * np.tanh(vv / 100)
+    a = O.bf16_round(capg / (1 + np.exp(-capg)) * capv)
+    aq = O.dequant_rows(*O.quantize_1x128(a))
+    gamma = inp["gamma"].astype(np.float64)
+    want = gamma * aq / np.sqrt(np.mean(aq * aq, axis=1, keepdims=True) + spec["eps"])
+    close(got, want, rtol=1e-10, atol=1e-12)
+
+
 def _a8_layer(seed, T=7, **kw):
     base = dict(H=128, L=128, E=4, k=2, S=1, I=128, Is=128)
     base.update(kw)
@@ -723,19 +766,29 @@ def _mut_quantize_e4m3_max_240(v):
     return O.e4m3fn_encode(b / scale[:, :, None]).reshape(R, C), scale
 
 
-def _mut_fp8_activations_skipped(v):
+def _mut_fp8_activations_skipped(v, act="f64"):
     return np.asarray(v, dtype=np.float64)
 
 
-def _mut_expert_ffn_a_not_quantised(zrows, wg, wv, wo, c, a8=False):
+def _mut_fp8_activations_unrounded(v, act="f64"):
+    return O.dequant_rows(*O.quantize_1x128(v))
+
+
+def _mut_expert_ffn_a_not_quantised(zrows, wg, wv, wo, c, a8=False, act="f64"):
     a = O.situ_glu(zrows @ wg.T, zrows @ wv.T, c)
     return a, a @ wo.T
+
+
+def _mut_bf16_round_truncates(v):
+    m, e = np.frexp(np.asarray(v, dtype=np.float64))
+    return np.ldexp(np.trunc(np.ldexp(m, 8)), e - 8)
 
 
 MUTANTS = {
     "e4m3fn_encode": [_mut_encode_truncates],
     "quantize_1x128": [_mut_quantize_per_row, _mut_quantize_e4m3_max_240],
-    "fp8_activations": [_mut_fp8_activations_skipped],
+    "fp8_activations": [_mut_fp8_activations_skipped, _mut_fp8_activations_unrounded],
+    "bf16_round": [_mut_bf16_round_truncates],
     "expert_ffn": [_mut_expert_ffn_a_not_quantised],
     "situ_glu": [_mut_value_uncapped, _mut_gate_value_swapped],
     "silu": [_mut_silu_sign],
