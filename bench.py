@@ -221,6 +221,7 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, K3 layer shape)",
         "config": {"workload": cfg.name, "T": T, "H": cfg.H, "L": cfg.L, "E": cfg.E, "k": cfg.k, "I": cfg.I,
                    "S": cfg.S, "Is": cfg.Is, "act": cfg.act, "w_expert": cfg.w_expert,
+                   "expert_act": "f8 (1x128 scales)" if cfg.a8 else cfg.act,
                    "expert_weights": "packed" if packed is not None else "row-major",
                    "parallelism": "single GPU"},
         "tflops": round(tflops, 2),
@@ -315,7 +316,7 @@ def cpu_baseline(cfg, g, idx, y, n, dev):
             inp[k] = raw_numpy(v[rt])
         else:
             inp[k] = raw_numpy(v)
-    spec = dict(act=cfg.act, w_expert=cfg.w_expert, k=cfg.k, cap=cfg.cap, eps=cfg.eps)
+    spec = dict(act=cfg.act, w_expert=cfg.w_expert, k=cfg.k, cap=cfg.cap, eps=cfg.eps, a8=cfg.a8)
     print(f"# oracle: {len(rows)} tokens on {cores} host cores", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     ref = O.forward(inp, spec, forced_idx=forced, forced_tol=1e-5)

@@ -92,6 +92,16 @@ typedef struct {
   int32_t w_expert;       /* lmoe_dtype                                          */
   float cap;              /* SiTU-GLU cap, 100 in the K3 layer                   */
   float rms_eps;          /* RMSNorm epsilon, 1e-6                               */
+  int32_t a8;             /* 0: the routed experts multiply act-dtype activations
+                             (W8A16 with F8E4M3 weights).  1: W8A8 -- z and the
+                             SiTU-GLU output are quantised per token per 128
+                             columns to e4m3fn (see lmoe_quantize_1x128) and the
+                             routed expert GEMMs multiply e4m3 by e4m3, with fp32
+                             accumulation and the block scales applied once per
+                             128 columns.  Needs act BF16 and w_expert F8E4M3
+                             (P3 merged summary: the BF16/FP8 range problem;
+                             the format is this library's reading).  Weight and
+                             activation scales must be positive and finite.    */
 } lmoe_shape;
 
 /* Weights.  Expert stacks are [E, I, L] (gate, value) and [E, L, I] (out);
@@ -229,6 +239,18 @@ lmoe_status lmoe_quantile_bias(const lmoe_shape *shape, const float *logits, flo
 size_t lmoe_packed_bytes(const lmoe_shape *shape);
 lmoe_status lmoe_pack_experts(const lmoe_shape *shape, const lmoe_weights *w, void *packed, size_t bytes,
                               void *stream);
+
+/* Per-token 1x128 activation quantisation of the W8A8 expert GEMMs (the
+ * precision question of P3's merged summary; the format is this library's
+ * reading).  x: BF16 [R, C] on the device, row-major, C a multiple of 128.
+ * Outputs (device, caller-owned, not aliasing x): q [R, C] e4m3fn codes, row
+ * stride C; scales [C/128, R] fp32, block-major (the scale of row r, columns
+ * 128 b .. 128 b + 127 at scales[b * R + r]).  scale = amax / 448 in fp32 (1 for
+ * an all-zero block); code = e4m3fn(x / scale), an fp32 division rounded to
+ * nearest even.  Inputs are taken to be finite.  R = 0 is an empty call;
+ * EINVAL for a negative R, C not a positive multiple of 128, or a NULL pointer.
+ * Asynchronous on `stream`.                                                    */
+lmoe_status lmoe_quantize_1x128(const void *x, int64_t R, int32_t C, void *q, float *scales, void *stream);
 
 /* Name of a status code; message of the calling thread's last failure.       */
 const char *lmoe_status_str(lmoe_status s);

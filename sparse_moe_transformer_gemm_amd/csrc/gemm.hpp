@@ -277,7 +277,9 @@ struct ExpertGVProb {
   const float* sv;
   char* act;          // [T*k, I]
   const char* wpk;    // packed gate/value blocks (see lmoe_pack_experts) or NULL
-  int I, L, k, f8;
+  const float* xs;    // W8A8: z block scales in expert order, [L/128, ldxs]
+  int64_t ldxs;
+  int I, L, k, f8, a8;  // a8: z holds e4m3 codes (W8A8)
   float cap, inv_cap;
 
   typedef ExpertState State;
@@ -289,25 +291,33 @@ struct ExpertGVProb {
   __device__ bool seg_f8(const State&, int) const { return f8; }
   __device__ int tokens_valid(const State& st) const { return st.rows; }
   __device__ int feats_valid(const State&) const { return Cfg::BF; }
+  __device__ int64_t xes() const { return a8 ? 1 : (int64_t)sizeof(CT); }
   __device__ const char* x_row(const State& st, int, int r) const {
     if (r >= st.rows) return nullptr;
     const int t = sorted[st.m0 + r] / k;
-    return z + (int64_t)t * ldz * (int64_t)sizeof(CT);
+    return z + (int64_t)t * ldz * xes();
   }
-  // Row r0 + lane / 8 for r0 < rows (rows past the valid ones map to the last
-  // valid row): the group's 8 assignment ids are read as uniform scalars, so
-  // the call needs no vector-memory wait.
+  // Row r0 + lane / (64 / RPI) for r0 < rows (rows past the valid ones map to
+  // the last valid row): the group's RPI assignment ids are read as uniform
+  // scalars, so the call needs no vector-memory wait.
+  template <int RPI = 8>
   __device__ const char* x_row_grp(const State& st, int, int r0, int lane) const {
-    int idx[8];
+    static_assert(RPI == 8 || RPI == 16, "8 or 16 rows per DMA instruction");
+    const int q = lane / (64 / RPI);
+    int a = 0;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) idx[q] = st.m0 + min(r0 + q, st.rows - 1);
-    const i32x8 v = sload_gather8(sorted, idx);
-    const int q8 = lane >> 3;
-    int a = v[0];
+    for (int h = 0; h < RPI / 8; ++h) {
+      int idx[8];
 #pragma unroll
-    for (int q = 1; q < 8; ++q) a = q8 == q ? v[q] : a;
-    return z + (int64_t)(a / k) * ldz * (int64_t)sizeof(CT);
+      for (int u = 0; u < 8; ++u) idx[u] = st.m0 + min(r0 + 8 * h + u, st.rows - 1);
+      const i32x8 v = sload_gather8(sorted, idx);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a = q == 8 * h + u ? v[u] : a;
+    }
+    return z + (int64_t)(a / k) * ldz * xes();
   }
+  // W8A8: scales of 128-column block kb of this tile's rows (row r at + r)
+  __device__ const float* x_scale(const State& st, int kb) const { return xs + kb * ldxs + st.m0; }
   __device__ const char* w_row(const State& st, int, int r, const float** scrow) const {
     const int m = r & 63;
     const int u = st.ft * (Cfg::BF / 2) + (r >> 6) * 32 + (m & 31);
@@ -358,7 +368,9 @@ struct ExpertDownProb {
   const float* so;    // [E, L/128, I/128]
   char* out;          // [T*k, L]
   const char* wpk;    // packed out blocks (see lmoe_pack_experts) or NULL
-  int I, L, f8;
+  const float* xs;    // W8A8: act block scales, [I/128, ldxs]
+  int64_t ldxs;
+  int I, L, f8, a8;   // a8: act holds e4m3 codes (W8A8)
 
   typedef ExpertState State;
   __device__ bool setup(int bid, State& st) const { return et.locate(bid, st); }
@@ -371,11 +383,13 @@ struct ExpertDownProb {
   __device__ int feats_valid(const State& st) const { return min(Cfg::BF, L - st.ft * Cfg::BF); }
   __device__ const char* x_row(const State& st, int, int r) const {
     if (r >= st.rows) return nullptr;
-    return act + (int64_t)(st.m0 + r) * I * (int64_t)sizeof(CT);
+    return act + (int64_t)(st.m0 + r) * I * (a8 ? 1 : (int64_t)sizeof(CT));
   }
+  template <int RPI = 8>
   __device__ const char* x_row_grp(const State& st, int s, int r0, int lane) const {
-    return x_row(st, s, min(r0 + (lane >> 3), tokens_valid(st) - 1));
+    return x_row(st, s, min(r0 + lane / (64 / RPI), tokens_valid(st) - 1));
   }
+  __device__ const float* x_scale(const State& st, int kb) const { return xs + kb * ldxs + st.m0; }
   __device__ const char* w_row(const State& st, int, int r, const float** scrow) const {
     const int f = st.ft * Cfg::BF + r;
     if (f >= L) return nullptr;
@@ -426,6 +440,13 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// 32x32x64 e4m3 x e4m3 block: lane l holds 32 codes of row (column) l % 32
+// for each operand.  The E8M0 block scales of the instruction are left at
+// 127 (2^0), so the products are the plain code products.
+__device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 // 8 e4m3 codes -> 8 bf16 of code * scale.

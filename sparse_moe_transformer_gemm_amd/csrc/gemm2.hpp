@@ -50,7 +50,7 @@ struct Tile2 {
 // Dense GEMMs over many tokens / few tokens (weight streaming); experts
 // holding many rows, a few dozen rows, or one or two rows (decode).
 // Split-ring tile (gemm3_kernel below): weights three stages deep, tokens two.
-template <int BF_, int BT_, int WF_, int WT_, int WAUX_, int PERSIST_ = 0, int WF8_ = 0, int SW_ = 3>
+template <int BF_, int BT_, int WF_, int WT_, int WAUX_, int PERSIST_ = 0, int WF8_ = 0, int SW_ = 3, int XF8_ = 0>
 struct Tile3 {
   static constexpr int BF = BF_, BT = BT_, WF = WF_, WT = WT_, WAUX = WAUX_;
   // PERSIST: a grid of resident work-groups walks the tile list with one
@@ -59,17 +59,24 @@ struct Tile3 {
   // WF8: e4m3 weights staged as such (64 bytes per row per 64-column k-tile)
   // and widened to bf16 with their block scale at the fragment load
   static constexpr int WF8 = WF8_;
+  // XF8: token rows staged as e4m3 codes as well (W8A8), multiplied by
+  // e4m3 x e4m3 MFMAs; the fp32 scale of each row's 128-column block rides
+  // with the token tile into a pair of LDS scale slots
+  static constexpr int XF8 = XF8_;
   static constexpr int SW = SW_, SX = 2;  // weight / token ring depths
   static constexpr int RBW = WF8 ? 64 : 128;              // weight row bytes per k-tile
   static constexpr int RPIW = 1024 / RBW;                 // weight rows per DMA instruction
+  static constexpr int RBX = XF8 ? 64 : 128;              // token row bytes per k-tile
+  static constexpr int RPIX = 1024 / RBX;                 // token rows per DMA instruction
   static constexpr int NT = WF * WT * kWave, NW = WF * WT;
   static constexpr int FW = BF / WF, TW = BT / WT;
   static constexpr int FI = FW / 32, TI = TW / 32;
-  static constexpr int QW = BF / RPIW, QX = BT / 8;
+  static constexpr int QW = BF / RPIW, QX = BT / RPIX;
   static constexpr int NQW = QW / NW, NQX = QX / NW;
-  static constexpr int WSTAGE = BF * RBW;
+  static constexpr int WSTAGE = BF * RBW, XSTAGE = BT * RBX;
   static constexpr int X_OFF = SW * WSTAGE;
-  static constexpr int LDS = SW * WSTAGE + SX * BT * 128;
+  static constexpr int SC_OFF = X_OFF + SX * XSTAGE;
+  static constexpr int LDS = SC_OFF + (XF8 ? SX * BT * 4 : 0);
   static constexpr bool kDma = true;
   static constexpr int kKind = PERSIST ? 4 : 3;
   static_assert(FW % 64 == 0 && TW % 32 == 0, "wave tile");
@@ -77,6 +84,8 @@ struct Tile3 {
   static_assert(NQW <= 63, "vmcnt range");
   static_assert(SW >= 3, "the weight ring runs at least two k-tiles ahead");
   static_assert(PERSIST || (!WF8 && SW == 3), "one-tile-per-group kernel: bf16 weights, three stages");
+  static_assert(!XF8 || (WF8 && PERSIST), "e4m3 tokens go with e4m3 weights in the persistent kernel");
+  static_assert(!XF8 || (BT % 64 == 0 && BT / 64 <= NW), "one 4-byte scale DMA per 64 token rows");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
@@ -104,6 +113,14 @@ struct Tile3 {
 #ifndef LMOE_T_EXPERT_DN_F8
 #define LMOE_T_EXPERT_DN_F8 Tile3<256, 256, 4, 4, 0, 1, 1, 5>
 #endif
+// W8A8 experts: 64-byte rows on both sides (64 columns per k-tile), so a
+// seven-deep weight ring fits beside the token ring and its scale slots.
+#ifndef LMOE_T_EXPERT_GV_A8
+#define LMOE_T_EXPERT_GV_A8 Tile3<256, 256, 4, 4, 0, 1, 1, 7, 1>
+#endif
+#ifndef LMOE_T_EXPERT_DN_A8
+#define LMOE_T_EXPERT_DN_A8 Tile3<256, 256, 4, 4, 0, 1, 1, 7, 1>
+#endif
 #ifndef LMOE_T_MID_GV
 #define LMOE_T_MID_GV Tile2<256, 64, 4, 1, 3, 0>
 #endif
@@ -122,12 +139,15 @@ typedef LMOE_T_EXPERT_GV T2ExpertGV;
 typedef LMOE_T_EXPERT_DN T2ExpertDn;
 typedef LMOE_T_EXPERT_GV_F8 T2ExpertGVF8;
 typedef LMOE_T_EXPERT_DN_F8 T2ExpertDnF8;
+typedef LMOE_T_EXPERT_GV_A8 T2ExpertGVA8;
+typedef LMOE_T_EXPERT_DN_A8 T2ExpertDnA8;
 typedef LMOE_T_MID_GV T2MidGV;
 typedef LMOE_T_MID_DN T2MidDn;
 typedef LMOE_T_SMALL_GV T2SmallGV;
 typedef LMOE_T_SMALL_DN T2SmallDn;
 static_assert(T2ExpertGV::BT == T2ExpertDn::BT && T2MidGV::BT == T2MidDn::BT && T2SmallGV::BT == T2SmallDn::BT &&
-                  T2ExpertGVF8::BT == T2ExpertDnF8::BT && T2ExpertGVF8::WF8 && T2ExpertDnF8::WF8,
+                  T2ExpertGVF8::BT == T2ExpertDnF8::BT && T2ExpertGVF8::WF8 && T2ExpertDnF8::WF8 &&
+                  T2ExpertGVA8::BT == T2ExpertDnA8::BT && T2ExpertGVA8::XF8 && T2ExpertDnA8::XF8,
               "expert GEMMs of one size class share the token tile");
 static_assert(T2ExpertGV::BF == kPackRows && T2ExpertDn::BF == kPackRows && T2MidGV::BF == kPackRows &&
                   T2MidDn::BF == kPackRows && T2SmallGV::BF == kPackRows && T2SmallDn::BF == kPackRows,
@@ -193,6 +213,11 @@ __global__ __launch_bounds__(256) void pack_experts_kernel(const char* wg, const
     if (src) v = *reinterpret_cast<const uint4*>(src);
     *reinterpret_cast<uint4*>(out + c * 16) = v;
   }
+}
+
+// 4 bytes per lane from `g` into LDS at `lds` + 4 * lane (lds wave-uniform).
+__device__ __forceinline__ void dma4(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }
 
 template <int N>
@@ -277,6 +302,35 @@ __device__ __forceinline__ void mma_ktile_f8(f32x16 (&acc)[FI][TI], const char* 
         if (j < tiv) acc[i][j] = mfma32(a, b[j], acc[i][j]);
     }
   }
+}
+
+// One k-tile (64 columns) with both operands as e4m3 codes in swizzled
+// 64-byte rows: one 32x32x64 MFMA per block.  Lane l supplies chunks
+// 2 (l / 32) and 2 (l / 32) + 1 of row l % 32 of each operand; the two
+// operands use the same lane-to-column map, so every code meets its partner.
+template <int FI, int TI>
+__device__ __forceinline__ void mma_ktile_a8(f32x16 (&acc)[FI][TI], const char* sW, const char* sX, int wf0, int wt0,
+                                             int lane, int tiv) {
+  const int lr = lane & 31, h = lane >> 5;
+  const int s = swz64(lr);  // fragment row offsets are multiples of 32
+  const int c0 = ((2 * h) ^ s) << 4, c1 = ((2 * h + 1) ^ s) << 4;
+  const char* pw = sW + (wf0 + lr) * 64;
+  const char* px = sX + (wt0 + lr) * 64;
+  auto frag = [&](const char* p) __attribute__((always_inline)) {
+    const i32x4 u = *reinterpret_cast<const i32x4*>(p + c0);
+    const i32x4 v = *reinterpret_cast<const i32x4*>(p + c1);
+    return i32x8{u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
+  };
+  i32x8 a[FI];
+#pragma unroll
+  for (int i = 0; i < FI; ++i) a[i] = frag(pw + i * 32 * 64);
+#pragma unroll
+  for (int j = 0; j < TI; ++j)
+    if (j < tiv) {
+      const i32x8 b = frag(px + j * 32 * 64);
+#pragma unroll
+      for (int i = 0; i < FI; ++i) acc[i][j] = mfma8(a[i], b, acc[i][j]);
+    }
 }
 
 template <class Cfg, class Prob>
@@ -586,15 +640,21 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
   int xj = 0, xsg = first_seg, xk = 0;
   const char* srcX[NQX];
   bool xon[NQX];
+  int xrows = 0, xg = 0;  // valid rows of the issue-side tile; X k-tiles issued
   // (row groups wholly past the valid rows are never issued and need no
   // source; x_row_grp maps the missing rows of a partial group to a valid one)
   auto set_x = [&]() __attribute__((always_inline)) {
-    const int xrows = p.tokens_valid(xst);
+    xrows = p.tokens_valid(xst);
 #pragma unroll
     for (int i = 0; i < NQX; ++i) {
-      const int r0 = (wid + NW * i) * 8;
+      const int r0 = (wid + NW * i) * Cfg::RPIX;
       xon[i] = r0 < xrows;
-      if (xon[i]) srcX[i] = p.x_row_grp(xst, xsg, r0, lane) + (((lane & 7) ^ swz(r0 + (lane >> 3))) << 4);
+      if (xon[i]) {
+        if constexpr (Cfg::XF8)
+          srcX[i] = p.template x_row_grp<Cfg::RPIX>(xst, xsg, r0, lane) + (((lane & 3) ^ swz64(r0 + (lane >> 2))) << 4);
+        else
+          srcX[i] = p.x_row_grp(xst, xsg, r0, lane) + (((lane & 7) ^ swz(r0 + (lane >> 3))) << 4);
+      }
     }
   };
   set_w();
@@ -614,10 +674,19 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
     }
   };
   auto issue_x = [&](int buf) __attribute__((always_inline)) {
-    char* base = smem + Cfg::X_OFF + buf * Cfg::BT * 128;
+    char* base = smem + Cfg::X_OFF + buf * Cfg::XSTAGE;
 #pragma unroll
     for (int i = 0; i < NQX; ++i)
-      if (xon[i]) dma16<LMOE_X_AUX>(srcX[i] + (int64_t)xk * 128, base + (wid + NW * i) * 1024);
+      if (xon[i]) dma16<LMOE_X_AUX>(srcX[i] + (int64_t)xk * Cfg::RBX, base + (wid + NW * i) * 1024);
+    if constexpr (Cfg::XF8) {
+      // the k-tile that opens a 128-column block brings the block's row
+      // scales: wave w loads rows 64 w .. 64 w + 63 (clamped to valid rows)
+      // into scale slot (block index & 1)
+      if ((xk & 1) == 0 && wid * 64 < xrows)
+        dma4(p.x_scale(xst, xk >> 1) + min(wid * 64 + lane, xrows - 1),
+             smem + Cfg::SC_OFF + ((xg >> 1) & 1) * (Cfg::BT * 4) + wid * 256);
+    }
+    ++xg;
     if (++xk == p.seg_ktiles(xsg)) {
       xk = 0;
       do { ++xsg; } while (xsg < nks && p.seg_ktiles(xsg) == 0);
@@ -635,6 +704,12 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
   // precede X(g) or are older still), so vmcnt(NQW) completes X(g) and W(g);
   // once W(g+SW-2) no longer exists the wait is vmcnt(0).
   constexpr int SW = Cfg::SW;
+  if constexpr (Cfg::XF8) {
+    // scale slots start at 1 (entries of row groups that are never loaded
+    // stay positive and finite); ordered before the first scale DMA
+    for (int i = tid; i < Cfg::SX * Cfg::BT; i += Cfg::NT) reinterpret_cast<float*>(smem + Cfg::SC_OFF)[i] = 1.f;
+    __syncthreads();
+  }
   issue_x(0);
 #pragma unroll
   for (int s = 0; s < SW - 1; ++s)
@@ -642,12 +717,31 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
   float sc[FI];
 #pragma unroll
   for (int i = 0; i < FI; ++i) sc[i] = 1.f;
+  // W8A8: acc holds the sum over 128-column blocks divided by sp, the
+  // product of the weight and row scales of the current block; entering a
+  // new block multiplies acc by old / new product, and the epilogue by sp.
+  float sp[FI][TI];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < TI; ++j) sp[i][j] = 1.f;
+  auto finish = [&]() __attribute__((always_inline)) {
+    if constexpr (Cfg::XF8) {
+#pragma unroll
+      for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < TI; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] *= sp[i][j];
+    }
+    p.epilogue(cst, acc, wf0, wt0, lane);
+  };
   bool pending = false;  // a finished tile's accumulators await their epilogue
   for (int g = 0; g < G; ++g) {
     if (g + SW - 2 < G) wait_vmcnt_barrier<NQW>();
     else wait_vmcnt_barrier<0>();
     if (pending) {
-      p.epilogue(cst, acc, wf0, wt0, lane);
+      finish();
       zero();
       ++cj;
       p.setup_lg(tile_lg(cj), cst);
@@ -658,8 +752,30 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
     if (g + SW - 1 < G) issue_w((g + SW - 1) % SW);
     if (active) {
       const char* sW = smem + (g % SW) * Cfg::WSTAGE;
-      const char* sX = smem + Cfg::X_OFF + (g & 1) * Cfg::BT * 128;
-      if constexpr (Cfg::WF8) {
+      const char* sX = smem + Cfg::X_OFF + (g & 1) * Cfg::XSTAGE;
+      if constexpr (Cfg::XF8) {
+        if ((ckt & 1) == 0) {
+          // every slot entry is a positive finite scale (the slots start at
+          // 1 and hold real row scales after), so the ratio is finite; at a
+          // tile's first block acc is zero and the product stays zero
+          p.w_scales(cst, wf0, ckt >> 1, sc);
+          const float* sxs =
+              reinterpret_cast<const float*>(smem + Cfg::SC_OFF + ((g >> 1) & 1) * (Cfg::BT * 4)) + wt0 + (lane & 31);
+#pragma unroll
+          for (int j = 0; j < TI; ++j) {
+            const float sx = sxs[j * 32];
+#pragma unroll
+            for (int i = 0; i < FI; ++i) {
+              const float sn = sc[i] * sx;
+              const float r = sp[i][j] * __builtin_amdgcn_rcpf(sn);
+#pragma unroll
+              for (int q = 0; q < 16; ++q) acc[i][j][q] *= r;
+              sp[i][j] = sn;
+            }
+          }
+        }
+        mma_ktile_a8<FI, TI>(acc, sW, sX, wf0, wt0, lane, tiv);
+      } else if constexpr (Cfg::WF8) {
         if ((ckt & 1) == 0) p.w_scales(cst, wf0, ckt >> 1, sc);  // one scale per 128 columns
         mma_ktile_f8<FI, TI>(acc, sW, sX, wf0, wt0, lane, tiv, sc);
       } else {
@@ -671,7 +787,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
       pending = true;
     }
   }
-  p.epilogue(cst, acc, wf0, wt0, lane);
+  finish();
 }
 
 }  // namespace lmoe

@@ -376,4 +376,73 @@ hipError_t launch_quantile_bias(const float* logits, int64_t T, int E, int k, ui
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// W8A8 activations: per row, per 128 consecutive columns, scale = amax / 448
+// in fp32 (1 for an all-zero block) and code = e4m3fn(x / scale): a correctly
+// rounded fp32 division, then the hardware conversion, which rounds to
+// nearest even.  Every |x / scale| <= 448 up to one rounding of the quotient,
+// which the conversion rounds back to 448.  Sixteen lanes share one block,
+// eight bf16 each: one 16-byte load and one 8-byte store per lane.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __restrict__ x, int64_t R, int C,
+                                                          uint8_t* __restrict__ q, float* __restrict__ sc) {
+  const int nb = C >> 7;
+  const int64_t unit = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (row, block)
+  if (unit >= R * nb) return;  // whole 16-lane groups leave together
+  const int64_t r = unit / nb;
+  const int b = (int)(unit - r * nb);
+  const int sub = threadIdx.x & 15;
+  const int64_t off = r * C + b * 128 + sub * 8;
+  const uint4 v = *reinterpret_cast<const uint4*>(x + off);
+  const unsigned w[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
+  const float s = amax > 0.f ? amax / 448.f : 1.f;
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] / s, f[1] / s, 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2] / s, f[3] / s, lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4] / s, f[5] / s, 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6] / s, f[7] / s, hi, true);
+  *reinterpret_cast<uint2*>(q + off) = uint2{(unsigned)lo, (unsigned)hi};
+  if (sub == 0) sc[(int64_t)b * R + r] = s;
+}
+
+hipError_t launch_quant_1x128(const void* x, int64_t R, int C, void* q, float* sc, hipStream_t st) {
+  const int64_t units = R * (C / 128);
+  if (units == 0) return hipSuccess;
+  const int64_t blocks = (units + 15) / 16;
+  if (blocks > INT_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_1x128_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(x), R, C, static_cast<uint8_t*>(q), sc);
+  return hipGetLastError();
+}
+
+// Row scales in expert order: out[b * tk + a] = s_tok[b * T + sorted[a] / k].
+__global__ __launch_bounds__(256) void gather_scales_kernel(const float* __restrict__ s_tok, int64_t T, int nb,
+                                                            const int32_t* __restrict__ sorted, int64_t tk, int k,
+                                                            float* __restrict__ out) {
+  const int64_t a = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (a >= tk) return;
+  // entries past the last expert's range may hold anything: clamp the token
+  const int64_t t = min(max((int64_t)(sorted[a] / k), (int64_t)0), T - 1);
+  for (int b = 0; b < nb; ++b) out[b * tk + a] = s_tok[b * T + t];
+}
+
+hipError_t launch_gather_scales(const float* s_tok, int64_t T, int nb, const int32_t* sorted, int k, float* out,
+                                hipStream_t st) {
+  const int64_t tk = T * k;
+  if (tk == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_scales_kernel, dim3((unsigned)((tk + 255) / 256)), dim3(256), 0, st, s_tok, T, nb, sorted,
+                     tk, k, out);
+  return hipGetLastError();
+}
+
 }  // namespace lmoe

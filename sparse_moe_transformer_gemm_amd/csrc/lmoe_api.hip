@@ -65,6 +65,9 @@ lmoe_status check_shape(const lmoe_shape* sh) {
   if (sh->S > 8) return fail(LMOE_EUNSUPPORTED, "S = %d > 8", sh->S);
   if (sh->T * (int64_t)sh->k >= (int64_t(1) << 31)) return fail(LMOE_EUNSUPPORTED, "T*k must be < 2^31");
   if (sh->T >= (int64_t(1) << 31)) return fail(LMOE_EUNSUPPORTED, "T must be < 2^31");
+  if (sh->a8 != 0 && sh->a8 != 1) return fail(LMOE_EINVAL, "a8 = %d is neither 0 nor 1", sh->a8);
+  if (sh->a8 && !(sh->act == LMOE_BF16 && sh->w_expert == LMOE_F8E4M3))
+    return fail(LMOE_EUNSUPPORTED, "W8A8 (a8 = 1) needs act BF16 and F8E4M3 expert weights");
   return LMOE_OK;
 }
 
@@ -115,8 +118,11 @@ bool use_dma(const lmoe_shape* sh) { return sh->act == LMOE_BF16 && sh->w_expert
 // e4m3 expert weights with bf16 activations and many rows per expert: the
 // persistent LDS-DMA expert GEMMs with the codes widened at the fragment load.
 bool use_dma_f8(const lmoe_shape* sh) {
-  return sh->act == LMOE_BF16 && sh->w_expert == LMOE_F8E4M3 && sh->T * (int64_t)sh->k >= 96 * (int64_t)sh->E;
+  return sh->act == LMOE_BF16 && sh->w_expert == LMOE_F8E4M3 && !sh->a8 &&
+         sh->T * (int64_t)sh->k >= 96 * (int64_t)sh->E;
 }
+// W8A8: e4m3 x e4m3 persistent expert GEMMs at every token count.
+bool use_a8(const lmoe_shape* sh) { return sh->a8 != 0; }
 
 // Experts: token tile by the mean rows per expert (T*k/E).
 enum ExpertTile { ET_SMALL, ET_MID, ET_BIG };
@@ -130,6 +136,7 @@ ExpertTile expert_tile(const lmoe_shape* sh) {
   return tk < 48 * (int64_t)sh->E ? ET_SMALL : ET_BIG;
 }
 int expert_bt(const lmoe_shape* sh) {
+  if (use_a8(sh)) return T2ExpertGVA8::BT;
   if (use_dma_f8(sh)) return T2ExpertGVF8::BT;
   const ExpertTile t = expert_tile(sh);
   if (use_dma(sh)) return t == ET_SMALL ? T2SmallGV::BT : t == ET_MID ? T2MidGV::BT : T2ExpertGV::BT;
@@ -145,7 +152,9 @@ int64_t max_tiles(const lmoe_shape* sh, int bt) {
 }
 
 struct Plan {
-  size_t logits, z, hs, n, idx, w, bcounts, offsets, sorted, pos, tiles_a, tiles_b, tcount, act, out, total;
+  size_t logits, z, hs, n, idx, w, bcounts, offsets, sorted, pos, tiles_a, tiles_b, tcount, act, out;
+  size_t zq, zs_tok, zs, aq, as;  // W8A8 only: e4m3 z, its scales by token and in expert order; e4m3 act, scales
+  size_t total;
 };
 
 Plan plan(const lmoe_shape* sh) {
@@ -174,6 +183,13 @@ Plan plan(const lmoe_shape* sh) {
   p.tcount = take(8);
   p.act = take(tk * sh->I * es);
   p.out = take(tk * sh->L * es);
+  if (sh->a8) {
+    p.zq = take(T * sh->L);
+    p.zs_tok = take(T * (sh->L / 128) * 4);
+    p.zs = take(tk * (sh->L / 128) * 4);
+    p.aq = take(tk * sh->I);
+    p.as = take(tk * (sh->I / 128) * 4);
+  }
   p.total = off;
   return p;
 }
@@ -352,9 +368,10 @@ hipError_t upgemm(const Ctx& c, const void* n, const void* hs, void* y) {
   return launch_gemm<Cfg, CT>(p, p.padded, c.st);
 }
 
+// xs: W8A8 row scales (z then holds e4m3 codes), [L/128, T*k] in expert order.
 template <class Cfg, typename CT>
 hipError_t expert_gv(const Ctx& c, const void* z, const int32_t* offsets, const int32_t* sorted,
-                     const int4* tiles, const int32_t* tcount, void* act) {
+                     const int4* tiles, const int32_t* tcount, void* act, const float* xs = nullptr) {
   const lmoe_shape* sh = c.sh;
   ExpertGVProb<Cfg, CT> p{};
   p.et.offsets = offsets;
@@ -374,14 +391,18 @@ hipError_t expert_gv(const Ctx& c, const void* z, const int32_t* offsets, const 
   p.L = sh->L;
   p.k = sh->k;
   p.f8 = is_f8(sh);
+  p.a8 = xs != nullptr;
+  p.xs = xs;
+  p.ldxs = sh->T * sh->k;
   p.cap = sh->cap;
   p.inv_cap = c.inv_cap();
   return launch_gemm<Cfg, CT>(p, pad8(max_tiles(sh, Cfg::BT) * p.et.nft), c.st);
 }
 
+// xs: W8A8 row scales (act then holds e4m3 codes), [I/128, T*k].
 template <class Cfg, typename CT>
 hipError_t expert_down(const Ctx& c, const void* act, const int32_t* offsets, const int4* tiles,
-                       const int32_t* tcount, void* out) {
+                       const int32_t* tcount, void* out, const float* xs = nullptr) {
   const lmoe_shape* sh = c.sh;
   ExpertDownProb<Cfg, CT> p{};
   p.et.offsets = offsets;
@@ -396,7 +417,31 @@ hipError_t expert_down(const Ctx& c, const void* act, const int32_t* offsets, co
   p.I = sh->I;
   p.L = sh->L;
   p.f8 = is_f8(sh);
+  p.a8 = xs != nullptr;
+  p.xs = xs;
+  p.ldxs = sh->T * sh->k;
   return launch_gemm<Cfg, CT>(p, pad8(max_tiles(sh, Cfg::BT) * p.et.nft), c.st);
+}
+
+// W8A8 gate/value: z (or x) quantised per token, its row scales put in expert
+// order, then the e4m3 x e4m3 GEMM with the SiTU-GLU epilogue (bf16 act).
+hipError_t expert_gv_a8(const Ctx& c, const Plan& pl, void* ws, const void* z, const int32_t* offsets,
+                        const int32_t* sorted, const int4* tiles, const int32_t* tcount, void* act) {
+  const lmoe_shape* sh = c.sh;
+  hipError_t e = launch_quant_1x128(z, sh->T, sh->L, at<void>(ws, pl.zq), at<float>(ws, pl.zs_tok), c.st);
+  if (e != hipSuccess) return e;
+  e = launch_gather_scales(at<float>(ws, pl.zs_tok), sh->T, sh->L / 128, sorted, sh->k, at<float>(ws, pl.zs), c.st);
+  if (e != hipSuccess) return e;
+  return expert_gv<T2ExpertGVA8, bf16>(c, at<void>(ws, pl.zq), offsets, sorted, tiles, tcount, act,
+                                       at<float>(ws, pl.zs));
+}
+// W8A8 down: the SiTU-GLU output quantised per row, then the e4m3 x e4m3 GEMM.
+hipError_t expert_down_a8(const Ctx& c, const Plan& pl, void* ws, const void* act, const int32_t* offsets,
+                          const int4* tiles, const int32_t* tcount, void* out) {
+  const lmoe_shape* sh = c.sh;
+  hipError_t e = launch_quant_1x128(act, sh->T * sh->k, sh->I, at<void>(ws, pl.aq), at<float>(ws, pl.as), c.st);
+  if (e != hipSuccess) return e;
+  return expert_down<T2ExpertDnA8, bf16>(c, at<void>(ws, pl.aq), offsets, tiles, tcount, out, at<float>(ws, pl.as));
 }
 
 // Dispatch on (dtype, tile).
@@ -544,6 +589,12 @@ lmoe_status lmoe_expert_gemm(const lmoe_shape* sh, const lmoe_weights* w, const 
   void* act = at<void>(ws, pl.act);
   int4* tiles = at<int4>(ws, pl.tiles_a);
   int32_t* tc = at<int32_t>(ws, pl.tcount);
+  if (use_a8(sh)) {
+    LMOE_HIP(launch_tiles(offsets, sh->E, expert_bt(sh), tiles, tc, 0, nullptr, nullptr, c.st), "tile list");
+    LMOE_HIP(expert_gv_a8(c, pl, ws, z, offsets, sorted, tiles, tc, act), "expert gate/value GEMM");
+    LMOE_HIP(expert_down_a8(c, pl, ws, act, offsets, tiles, tc, expert_out), "expert down GEMM");
+    return LMOE_OK;
+  }
   LMOE_HIP(bf16_act(sh) ? experts_any<bf16>(c, z, offsets, sorted, act, expert_out, tiles, tc)
                         : experts_any<float>(c, z, offsets, sorted, act, expert_out, tiles, tc),
            "expert GEMMs");
@@ -615,12 +666,14 @@ lmoe_status lmoe_forward(const lmoe_shape* sh, const lmoe_weights* w, const void
   const void* zin = z ? z : x;
   const int4* tiles = at<int4>(ws, pl.tiles_a);
   const int32_t* tc = at<int32_t>(ws, pl.tcount);
-  LMOE_HIP(bf ? expert_gv_any<bf16>(c, zin, offsets, sorted, tiles, tc, act)
-              : expert_gv_any<float>(c, zin, offsets, sorted, tiles, tc, act),
+  LMOE_HIP(use_a8(sh) ? expert_gv_a8(c, pl, ws, zin, offsets, sorted, tiles, tc, act)
+           : bf      ? expert_gv_any<bf16>(c, zin, offsets, sorted, tiles, tc, act)
+                     : expert_gv_any<float>(c, zin, offsets, sorted, tiles, tc, act),
            "expert gate/value GEMM");
   if (lmoe_status s = record(ev, 4, c.st)) return s;
-  hipError_t e = bf ? expert_down_any<bf16>(c, act, offsets, tiles, tc, out)
-                    : expert_down_any<float>(c, act, offsets, tiles, tc, out);
+  hipError_t e = use_a8(sh) ? expert_down_a8(c, pl, ws, act, offsets, tiles, tc, out)
+                 : bf       ? expert_down_any<bf16>(c, act, offsets, tiles, tc, out)
+                            : expert_down_any<float>(c, act, offsets, tiles, tc, out);
   LMOE_HIP(e, "expert down GEMM");
   if (lmoe_status s = record(ev, 5, c.st)) return s;
   LMOE_HIP(launch_combine_norm(bf, out, pos, tw, w->gamma, sh->T, sh->L, sh->k, sh->rms_eps, n, c.st),
@@ -656,6 +709,20 @@ lmoe_status lmoe_quantile_bias(const lmoe_shape* sh, const float* logits, float*
   LMOE_HIP(launch_quantile_bias(logits, sh->T, sh->E, sh->k, at<uint32_t>(ws, plan(sh).logits), bias,
                                 static_cast<hipStream_t>(stream)),
            "quantile thresholds");
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_quantize_1x128(const void* x, int64_t R, int32_t C, void* q, float* scales, void* stream) {
+  g_err[0] = 0;
+  if (R < 0) return fail(LMOE_EINVAL, "R = %lld < 0", (long long)R);
+  if (C <= 0 || C % 128) return fail(LMOE_EINVAL, "C = %d is not a positive multiple of 128", C);
+  if (R == 0) return LMOE_OK;
+  if (!x || !q || !scales) return fail(LMOE_EINVAL, "x, q and scales are required");
+  if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(q) & 7) ||
+      (reinterpret_cast<uintptr_t>(scales) & 3))
+    return fail(LMOE_EINVAL, "x must be 16-byte, q 8-byte and scales 4-byte aligned");
+  if (R * (int64_t)(C / 128) > (int64_t)INT32_MAX * 16) return fail(LMOE_EUNSUPPORTED, "too many blocks");
+  LMOE_HIP(launch_quant_1x128(x, R, C, q, scales, static_cast<hipStream_t>(stream)), "1x128 quantisation");
   return LMOE_OK;
 }
 

@@ -24,7 +24,7 @@ _TORCH = {F32: torch.float32, BF16: torch.bfloat16, F8E4M3: torch.float8_e4m3fn}
 
 EXPORTS = ("lmoe_validate", "lmoe_workspace_bytes", "lmoe_forward", "lmoe_route", "lmoe_permute",
            "lmoe_expert_gemm", "lmoe_combine_norm", "lmoe_up", "lmoe_router_logits", "lmoe_quantile_bias",
-           "lmoe_packed_bytes", "lmoe_pack_experts",
+           "lmoe_packed_bytes", "lmoe_pack_experts", "lmoe_quantize_1x128",
            "lmoe_status_str", "lmoe_last_error")
 
 
@@ -38,7 +38,7 @@ class Shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("L", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("I", ctypes.c_int32), ("S", ctypes.c_int32), ("Is", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("w_expert", ctypes.c_int32), ("cap", ctypes.c_float),
-                ("rms_eps", ctypes.c_float)]
+                ("rms_eps", ctypes.c_float), ("a8", ctypes.c_int32)]
 
 
 _WEIGHT_FIELDS = ("w_router", "b_router", "w_down", "w_gate", "w_value", "w_out", "s_gate", "s_value", "s_out",
@@ -76,6 +76,7 @@ def load_library(path: str = LIB_PATH):
         "lmoe_quantile_bias": (ctypes.c_int, [sp, f32p, f32p, vp, sz, vp]),
         "lmoe_packed_bytes": (sz, [sp]),
         "lmoe_pack_experts": (ctypes.c_int, [sp, wp, vp, sz, vp]),
+        "lmoe_quantize_1x128": (ctypes.c_int, [vp, ctypes.c_int64, ctypes.c_int32, vp, f32p, vp]),
         "lmoe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "lmoe_last_error": (ctypes.c_char_p, []),
     }
@@ -96,16 +97,16 @@ def _check(status):
 # marshalling helpers
 # ----------------------------------------------------------------------------
 
-def make_shape(T, H, L, E, k, I, S, Is, act="bf16", w_expert="bf16", cap=100.0, eps=1e-6) -> Shape:
+def make_shape(T, H, L, E, k, I, S, Is, act="bf16", w_expert="bf16", cap=100.0, eps=1e-6, a8=False) -> Shape:
     return Shape(int(T), int(H), int(L), int(E), int(k), int(I), int(S), int(Is), DTYPE_CODE[act],
-                 DTYPE_CODE[w_expert], float(cap), float(eps))
+                 DTYPE_CODE[w_expert], float(cap), float(eps), int(bool(a8)))
 
 
 def shape_of(cfg, T=None) -> Shape:
     """Shape from any object with the fields T, H, L, E, k, I, S, Is, act,
-    w_expert, cap, eps (e.g. synth.LayerConfig)."""
+    w_expert, cap, eps and optionally a8 (e.g. synth.LayerConfig)."""
     return make_shape(cfg.T if T is None else T, cfg.H, cfg.L, cfg.E, cfg.k, cfg.I, cfg.S, cfg.Is, cfg.act,
-                      cfg.w_expert, cfg.cap, cfg.eps)
+                      cfg.w_expert, cfg.cap, cfg.eps, getattr(cfg, "a8", False))
 
 
 def _ptr(t, dtype=None, name="tensor"):
@@ -155,6 +156,24 @@ def quantile_bias(sh: Shape, logits, out=None, ws=None, stream=None):
     _check(lib.lmoe_quantile_bias(ctypes.byref(sh), _ptr(logits, torch.float32, "logits"), _ptr(out, torch.float32, "bias"),
                                   _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
     return out
+
+
+def quantize_1x128(x, q=None, scales=None, stream=None):
+    """Per-row 1x128 e4m3fn quantisation of a bf16 [R, C] device tensor:
+    returns (codes [R, C] float8_e4m3fn, scales [C/128, R] fp32, block-major);
+    see lmoe_quantize_1x128 in include/lmoe.h."""
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [R, C]")
+    R, C = x.shape
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.float8_e4m3fn, device=x.device)
+    if scales is None:
+        scales = torch.empty((C // 128 if C % 128 == 0 else 0, R), dtype=torch.float32, device=x.device)
+    _check(lib.lmoe_quantize_1x128(_ptr(x, torch.bfloat16, "x"), ctypes.c_int64(R), ctypes.c_int32(C),
+                                   _ptr(q, torch.float8_e4m3fn, "q"), _ptr(scales, torch.float32, "scales"),
+                                   _stream(stream)))
+    return q, scales
 
 
 def packed_bytes(sh: Shape) -> int:

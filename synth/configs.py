@@ -33,6 +33,7 @@ class LayerConfig:
     x_scale: float = 1.0      # multiplies x ~ N(0,1) (stress inputs)
     identity_proj: bool = False   # no latent projections (L == H)
     x_seed: int = -1          # seed of x if it differs from the weights' seed
+    a8: bool = False          # W8A8 routed experts (e4m3 activations, 1x128 scales)
 
     @property
     def tk(self) -> int:
@@ -56,6 +57,8 @@ _LIST = [
                 act="bf16", w_expert="bf16", seed=3),
     LayerConfig("small_fp8", T=301, H=512, L=256, E=20, k=4, S=2, I=256, Is=128,
                 act="bf16", w_expert="f8", seed=4),
+    LayerConfig("small_w8a8", T=301, H=512, L=256, E=20, k=4, S=2, I=256, Is=128,
+                act="bf16", w_expert="f8", seed=4, a8=True),
     LayerConfig("small_identity_bf16", T=130, H=256, L=256, E=12, k=3, S=1, I=128,
                 Is=128, act="bf16", w_expert="bf16", seed=5, identity_proj=True),
     # Every expert selected (k == E) and no shared expert.
@@ -68,6 +71,7 @@ _LIST = [
     LayerConfig("k3_zipf_t16384", T=16384, act="bf16", w_expert="bf16", seed=1,
                 bias="zipf1.1", **K3),
     LayerConfig("k3_fp8_t8192", T=8192, act="bf16", w_expert="f8", seed=1, **K3),
+    LayerConfig("k3_w8a8_t8192", T=8192, act="bf16", w_expert="f8", seed=1, a8=True, **K3),
     LayerConfig("fp8_448x8_l7168_t8192", T=8192, H=7168, L=7168, E=448, k=8, S=2,
                 I=1024, Is=1024, act="bf16", w_expert="f8", seed=1),
     # The pages' 448/8 comparison read as a classic MoE with no latent (identity

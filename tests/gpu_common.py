@@ -31,7 +31,7 @@ def tol_of(cfg):
 
 
 def spec_of(cfg):
-    return dict(act=cfg.act, w_expert=cfg.w_expert, k=cfg.k, cap=cfg.cap, eps=cfg.eps)
+    return dict(act=cfg.act, w_expert=cfg.w_expert, k=cfg.k, cap=cfg.cap, eps=cfg.eps, a8=cfg.a8)
 
 
 def upload(t, dev):

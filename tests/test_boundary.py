@@ -22,7 +22,7 @@ from synth import get_config  # noqa: E402
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(lmoe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(lmoe_[a-z0-9_]+)\s*\(", src)))
 
 
 def fake_weights(sh, **override):
@@ -59,8 +59,8 @@ def k3(**kw):
 
 
 def test_valid_layers_pass(lib):
-    for name in ("tiny_f32", "small_bf16", "small_fp8", "small_identity_bf16", "k3_t8192", "k3_fp8_t8192",
-                 "fp8_448x8_l7168_t8192", "k3_zipf_t16384", "k3_decode_t64"):
+    for name in ("tiny_f32", "small_bf16", "small_fp8", "small_w8a8", "small_identity_bf16", "k3_t8192",
+                 "k3_fp8_t8192", "k3_w8a8_t8192", "fp8_448x8_l7168_t8192", "k3_zipf_t16384", "k3_decode_t64"):
         cfg = get_config(name)
         sh = lmoe.shape_of(cfg)
         over = {"w_down": None, "w_up": None} if cfg.identity_proj else {}
@@ -97,6 +97,8 @@ def test_workspace_grows_with_tokens(lib):
     (dict(act="f32"), 2),                    # f32 layer with bf16 experts
     (dict(act="bf16", w_expert="f32"), 2),
     (dict(T=(1 << 31) // 16), 2),            # T*k reaches 2^31
+    (dict(a8=True), 2),                      # W8A8 with bf16 expert weights
+    (dict(a8=True, w_expert="f32", act="f32"), 2),
 ])
 def test_shape_errors(lib, kw, code):
     sh = k3(**kw)
@@ -234,3 +236,27 @@ def test_router_logits_and_quantile_bias_reject_before_any_gpu_call(lib):
     assert lib.lmoe_quantile_bias(ctypes.byref(sh), None, buf, buf, need, None) == 1
     assert lib.lmoe_quantile_bias(ctypes.byref(sh), buf, None, buf, need, None) == 1
     assert lib.lmoe_quantile_bias(ctypes.byref(sh), buf, buf, buf, need - 1, None) == 3
+
+
+def test_a8_flag_values(lib):
+    sh = k3(w_expert="f8", a8=True)
+    assert lmoe.validate(sh, fake_weights(sh), lmoe.workspace_bytes(sh)) == 0, lmoe.last_error()
+    # W8A8 needs the e4m3 copies of z and of the SiTU-GLU output
+    assert lmoe.workspace_bytes(sh) > lmoe.workspace_bytes(k3(w_expert="f8"))
+    sh.a8 = 2
+    assert lmoe.validate(sh, fake_weights(sh), 1 << 40) == 1
+    assert "a8" in lmoe.last_error()
+
+
+def test_quantize_1x128_rejects_before_any_gpu_call(lib):
+    buf = ctypes.c_void_p(0x100000)
+    q = lib.lmoe_quantize_1x128
+    assert q(buf, -1, 128, buf, buf, None) == 1
+    assert q(buf, 4, 100, buf, buf, None) == 1
+    assert q(buf, 4, 0, buf, buf, None) == 1
+    assert q(buf, 0, 128, None, None, None) == 0  # empty: no-op
+    assert q(None, 4, 128, buf, buf, None) == 1
+    assert q(buf, 4, 128, None, buf, None) == 1
+    assert q(buf, 4, 128, buf, None, None) == 1
+    assert q(ctypes.c_void_p(0x100008), 4, 128, buf, buf, None) == 1  # x not 16-byte aligned
+    assert "aligned" in lmoe.last_error()

@@ -110,7 +110,8 @@ def test_k3_zipf_t16384(dev, k3w):
     assert int(counts.max()) == cfg.T  # the most favoured expert is in every token's top-16
 
 
-@pytest.mark.parametrize("name", ["k3_fp8_t8192", "fp8_448x8_l7168_t8192", "k3_448x8_identity_t8192"])
+@pytest.mark.parametrize("name", ["k3_fp8_t8192", "k3_w8a8_t8192", "fp8_448x8_l7168_t8192",
+                                  "k3_448x8_identity_t8192"])
 def test_comparison_layers(dev, k3w, name):
     """fp8 expert weights at the K3 shape, and the 448/8 layer at latent 7168:
     with a real square projection (fp8) and with none (bf16)."""

@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 
 lmoe = pytest.importorskip("sparse_moe_transformer_gemm_amd.lmoe")
 
-SMALL = ["tiny_f32", "tiny_situ_stress", "small_bf16", "small_fp8", "small_identity_bf16", "small_full_k"]
+SMALL = ["tiny_f32", "tiny_situ_stress", "small_bf16", "small_fp8", "small_w8a8", "small_identity_bf16",
+         "small_full_k"]
 
 
 @pytest.fixture(scope="module")
@@ -56,12 +57,14 @@ def test_forward_small(dev, name):
 
 
 @pytest.mark.parametrize("name,T", [("small_bf16", 20), ("small_bf16", 300), ("small_bf16", 700),
-                                    ("small_bf16", 2000), ("small_fp8", 700), ("small_fp8", 2000)])
+                                    ("small_bf16", 2000), ("small_fp8", 700), ("small_fp8", 2000),
+                                    ("small_w8a8", 20), ("small_w8a8", 2000)])
 def test_forward_tile_variants(dev, name, T):
     """Token counts that select each kernel tile: thin / dense x- and up-GEMMs,
     small / mid / big expert token tiles (experts with 1-3, ~50, ~330 rows);
     with e4m3 expert weights, the register-staged tiles at T=300 and the
-    LDS-DMA tiles that widen codes at the fragment load from T=700 on."""
+    LDS-DMA tiles that widen codes at the fragment load from T=700 on; W8A8
+    with nearly empty and with full token tiles."""
     cfg = replace(get_config(name), T=T, name=f"{name}_T{T}")
     note(f"[forward] {cfg.name}")
     t, g = make_case(cfg, dev)
@@ -160,11 +163,13 @@ def _oracle_experts(inp, cfg, z64, idx):
         wg = O.matrix(inp["w_gate"], inp.get("s_gate"), e, cfg.w_expert)
         wv = O.matrix(inp["w_value"], inp.get("s_value"), e, cfg.w_expert)
         wo = O.matrix(inp["w_out"], inp.get("s_out"), e, cfg.w_expert)
-        out[lo:hi] = O.expert_ffn(z64[srt[lo:hi] // cfg.k], wg, wv, wo, cfg.cap)[1]
+        zx = O.fp8_activations(z64, cfg.act) if cfg.a8 else z64
+        out[lo:hi] = O.expert_ffn(zx[srt[lo:hi] // cfg.k], wg, wv, wo, cfg.cap, cfg.a8, cfg.act)[1]
     return out, off, srt
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "tiny_situ_stress", "small_bf16", "small_fp8", "small_full_k"])
+@pytest.mark.parametrize("name", ["tiny_f32", "tiny_situ_stress", "small_bf16", "small_fp8", "small_w8a8",
+                                  "small_full_k"])
 def test_expert_gemm(dev, name):
     cfg = get_config(name)
     note(f"[expert_gemm] {name}")
@@ -381,3 +386,64 @@ def test_expert_gemm_packed(dev):
     o1 = lmoe.expert_gemm(sh, wp, z, offsets, sorted_)
     torch.cuda.synchronize()
     assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+
+
+def _quant_input(R, C, seed):
+    """bf16 rows whose 128-column blocks span 1e-30 .. 1e4 in magnitude, with
+    all-zero blocks, lone nonzeros, negative zeros and values far below their
+    block's maximum (codes in the e4m3 subnormal range and rounded to zero)."""
+    rng = np.random.default_rng(seed)
+    nb = C // 128
+    mag = np.exp(rng.uniform(np.log(1e-30), np.log(1e4), (R, nb)))
+    v = rng.standard_normal((R, C)) * np.repeat(mag, 128, axis=1)
+    v[:, ::7] *= 1e-4  # far below the block max
+    v[3, C - 128:] = 0.0
+    v[4, :] = -0.0
+    v[5, :128] = 0.0
+    v[5, 17] = -2.5
+    v[6, C - 56] = 1e30  # one huge value, the rest of its block rounds to zero
+    return torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("R,C", [(1, 128), (333, 384), (1000, 1024)])
+def test_quantize_1x128_bit_exact(dev, R, C):
+    """Codes and scales bit for bit against the oracle's quantiser, which takes
+    the same fp32 decisions (scale = amax / 448, code = e4m3fn(x / scale))."""
+    note(f"[quantize_1x128] R={R} C={C}")
+    x = _quant_input(max(R, 8), C, seed=R + C)[:R].contiguous()
+    q, sc = lmoe.quantize_1x128(x.to(dev))
+    torch.cuda.synchronize()
+    rq, rs = O.quantize_1x128(to_f64(x))
+    got_q = q.cpu().view(torch.uint8).numpy()
+    got_s = sc.cpu().numpy()
+    assert got_s.shape == (C // 128, R)
+    bad = np.argwhere(got_q != rq)
+    if bad.size:
+        r, c = bad[0]
+        note(f"    first code mismatch at ({r}, {c}): x={float(x[r, c])!r} got {got_q[r, c]:#04x} want {rq[r, c]:#04x}")
+    assert bad.size == 0
+    assert np.array_equal(got_s.T.view(np.uint32), rs.view(np.uint32))
+
+
+def test_quantize_1x128_expert_rows_at_k3_size(dev):
+    """The down GEMM's input at the 8192-token K3 layer: 131072 rows of 1024,
+    sampled rows checked bit for bit."""
+    R, C = 8192 * 16, 1024
+    note(f"[quantize_1x128] R={R} C={C}")
+    gen = torch.Generator().manual_seed(31)
+    x = (torch.randn((R, C), generator=gen) * 0.3).to(torch.bfloat16)
+    q, sc = lmoe.quantize_1x128(x.to(dev))
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(5).choice(R, 300, replace=False)
+    rows[0], rows[1] = 0, R - 1
+    rq, rs = O.quantize_1x128(to_f64(x[torch.from_numpy(rows)]))
+    assert np.array_equal(q[torch.from_numpy(rows).to(dev)].cpu().view(torch.uint8).numpy(), rq)
+    assert np.array_equal(sc[:, torch.from_numpy(rows).to(dev)].cpu().numpy().T, rs)
+
+
+def test_quantize_1x128_rejects(dev):
+    x = torch.zeros((4, 256), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(lmoe.LmoeError):
+        lmoe.quantize_1x128(x[:, :200].contiguous())
+    q, sc = lmoe.quantize_1x128(x[:0])
+    assert q.shape == (0, 256) and sc.shape == (2, 0)
