@@ -220,6 +220,22 @@ __device__ __forceinline__ void dma4(const void* g, char* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }
 
+// Stacked e4m3 matrices [n, R, C] with one fp32 scale per 128x128 block
+// ([n, R/128, C/128]) -> bf16 of code * scale, rounded exactly as the
+// register-staged GEMMs widen codes (widen_e4m3).  8 codes per thread.
+__global__ __launch_bounds__(256) void dequant_blocks_kernel(const char* q, const float* s, int64_t n, int R, int C,
+                                                             char* out) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= n * R * (int64_t)(C / 8)) return;
+  const int64_t e = g * 8;
+  const int64_t row = e / C;
+  const int c = (int)(e - row * C);
+  const int64_t m = row / R;
+  const int r = (int)(row - m * R);
+  const float sc = s[(m * (R / 128) + r / 128) * (C / 128) + c / 128];
+  *reinterpret_cast<uint4*>(out + e * 2) = widen_e4m3(*reinterpret_cast<const uint2*>(q + e), sc);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");

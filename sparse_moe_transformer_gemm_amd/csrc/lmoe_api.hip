@@ -154,6 +154,7 @@ int64_t max_tiles(const lmoe_shape* sh, int bt) {
 struct Plan {
   size_t logits, z, hs, n, idx, w, bcounts, offsets, sorted, pos, tiles_a, tiles_b, tcount, act, out;
   size_t zq, zs_tok, zs, aq, as;  // W8A8 only: e4m3 z, its scales by token and in expert order; e4m3 act, scales
+  size_t shared_bf16;              // e4m3 shared experts decoded to bf16 (gate, value, out)
   size_t total;
 };
 
@@ -183,6 +184,7 @@ Plan plan(const lmoe_shape* sh) {
   p.tcount = take(8);
   p.act = take(tk * sh->I * es);
   p.out = take(tk * sh->L * es);
+  if (sh->w_expert == LMOE_F8E4M3 && sh->S > 0) p.shared_bf16 = take((size_t)3 * sh->S * sh->Is * sh->H * 2);
   if (sh->a8) {
     p.zq = take(T * sh->L);
     p.zs_tok = take(T * (sh->L / 128) * 4);
@@ -444,6 +446,43 @@ hipError_t expert_down_a8(const Ctx& c, const Plan& pl, void* ws, const void* ac
   return expert_down<T2ExpertDnA8, bf16>(c, at<void>(ws, pl.aq), offsets, tiles, tcount, out, at<float>(ws, pl.as));
 }
 
+// e4m3 shared experts at prefill sizes: decoded once per call to bf16 in the
+// workspace, so that the route and up GEMMs (whose router, down and up
+// segments are bf16) run whole on the LDS-DMA kernels.  The view describes a
+// layer with bf16 expert weights for those two GEMMs only.
+struct DenseView {
+  lmoe_shape sh;
+  lmoe_weights w;
+};
+bool shared_to_bf16(const lmoe_shape* sh) {
+  return sh->act == LMOE_BF16 && is_f8(sh) && sh->S > 0 && !dense_small(sh);
+}
+hipError_t dequant_blocks(const void* q, const float* s, int64_t n, int R, int C, void* out, hipStream_t st) {
+  const int64_t groups = n * R * (int64_t)(C / 8);
+  if (groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant_blocks_kernel, dim3((unsigned)cdiv(groups, 256)), dim3(256), 0, st,
+                     static_cast<const char*>(q), s, n, R, C, static_cast<char*>(out));
+  return hipGetLastError();
+}
+hipError_t dense_view(const Ctx& c, const Plan& pl, void* ws, DenseView& v) {
+  v.sh = *c.sh;
+  v.w = *c.w;
+  if (!shared_to_bf16(c.sh)) return hipSuccess;
+  const lmoe_shape* sh = c.sh;
+  char* base = at<char>(ws, pl.shared_bf16);
+  const size_t one = (size_t)sh->S * sh->Is * sh->H * 2;
+  hipError_t e = dequant_blocks(c.w->ws_gate, c.w->ss_gate, sh->S, sh->Is, sh->H, base, c.st);
+  if (e == hipSuccess) e = dequant_blocks(c.w->ws_value, c.w->ss_value, sh->S, sh->Is, sh->H, base + one, c.st);
+  if (e == hipSuccess) e = dequant_blocks(c.w->ws_out, c.w->ss_out, sh->S, sh->H, sh->Is, base + 2 * one, c.st);
+  v.sh.w_expert = LMOE_BF16;
+  v.sh.a8 = 0;
+  v.w.ws_gate = base;
+  v.w.ws_value = base + one;
+  v.w.ws_out = base + 2 * one;
+  v.w.ss_gate = v.w.ss_value = v.w.ss_out = nullptr;
+  return e;
+}
+
 // Dispatch on (dtype, tile).
 template <typename CT>
 hipError_t xgemm_any(const Ctx& c, const void* x, float* logits, void* z, void* hs) {
@@ -621,8 +660,12 @@ lmoe_status lmoe_up(const lmoe_shape* sh, const lmoe_weights* w, const void* n, 
   if (lmoe_status s = check_ws(sh, ws, ws_bytes)) return s;
   if (sh->T == 0) return LMOE_OK;
   if (!n || !y || (sh->S > 0 && !x)) return fail(LMOE_EINVAL, "n, x, y are required");
-  const Ctx c{sh, w, static_cast<hipStream_t>(stream)};
-  void* hs = at<void>(ws, plan(sh).hs);
+  const Ctx c0{sh, w, static_cast<hipStream_t>(stream)};
+  const Plan pl = plan(sh);
+  DenseView dv;
+  LMOE_HIP(dense_view(c0, pl, ws, dv), "shared expert decode");
+  const Ctx c{&dv.sh, &dv.w, c0.st};
+  void* hs = at<void>(ws, pl.hs);
   if (sh->S > 0)
     LMOE_HIP(bf16_act(sh) ? xgemm_any<bf16>(c, x, nullptr, nullptr, hs) : xgemm_any<float>(c, x, nullptr, nullptr, hs),
              "shared gate/value GEMM");
@@ -653,7 +696,10 @@ lmoe_status lmoe_forward(const lmoe_shape* sh, const lmoe_weights* w, const void
   void* out = at<void>(ws, pl.out);
 
   if (lmoe_status s = record(ev, 0, c.st)) return s;
-  LMOE_HIP(bf ? xgemm_any<bf16>(c, x, logits, z, hs) : xgemm_any<float>(c, x, logits, z, hs), "route GEMM");
+  DenseView dv;
+  LMOE_HIP(dense_view(c, pl, ws, dv), "shared expert decode");
+  const Ctx cd{&dv.sh, &dv.w, c.st};  // route and up GEMMs
+  LMOE_HIP(bf ? xgemm_any<bf16>(cd, x, logits, z, hs) : xgemm_any<float>(cd, x, logits, z, hs), "route GEMM");
   if (lmoe_status s = record(ev, 1, c.st)) return s;
   LMOE_HIP(launch_topk(logits, w->b_router, sh->T, sh->E, sh->k, idx, tw, c.st), "top-k");
   if (lmoe_status s = record(ev, 2, c.st)) return s;
@@ -679,7 +725,7 @@ lmoe_status lmoe_forward(const lmoe_shape* sh, const lmoe_weights* w, const void
   LMOE_HIP(launch_combine_norm(bf, out, pos, tw, w->gamma, sh->T, sh->L, sh->k, sh->rms_eps, n, c.st),
            "combine + norm");
   if (lmoe_status s = record(ev, 6, c.st)) return s;
-  LMOE_HIP(bf ? upgemm_any<bf16>(c, n, hs, y) : upgemm_any<float>(c, n, hs, y), "up GEMM");
+  LMOE_HIP(bf ? upgemm_any<bf16>(cd, n, hs, y) : upgemm_any<float>(cd, n, hs, y), "up GEMM");
   if (lmoe_status s = record(ev, 7, c.st)) return s;
   return LMOE_OK;
 }
