@@ -286,11 +286,19 @@ __device__ __forceinline__ void mma_ktile(f32x16 (&acc)[FI][TI], const char* sW,
 
 // As mma_ktile, with the weight operand as e4m3 codes (64-byte rows): lane l
 // reads the 8 codes of k-step ks, half l / 32 of chunk ks, and widens them to
-// bf16 times the block scale sc[i] of its 32-row block (rounding as the
-// register-staged path does).  Raw codes are double-buffered across k-steps.
+// bf16 unscaled (exact: every e4m3 value is a bf16 value); the caller applies
+// the block scales to the accumulators once per 128 columns.  Raw codes are
+// double-buffered across k-steps.
+__device__ __forceinline__ bf16x8 widen_e4m3_exact(uint2 q) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)q.x, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)q.x, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)q.y, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)q.y, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
 template <int FI, int TI>
 __device__ __forceinline__ void mma_ktile_f8(f32x16 (&acc)[FI][TI], const char* sW, const char* sX, int wf0, int wt0,
-                                             int lane, int tiv, const float (&sc)[FI]) {
+                                             int lane, int tiv) {
   const int lr = lane & 31;
   const int sw = swz(lr), sw64 = swz64(lr);  // fragment row offsets are multiples of 32
   const char* pw = sW + (wf0 + lr) * 64 + ((lane >> 5) << 3);
@@ -311,8 +319,7 @@ __device__ __forceinline__ void mma_ktile_f8(f32x16 (&acc)[FI][TI], const char* 
       if (j < tiv) b[j] = *reinterpret_cast<const bf16x8*>(px + j * 32 * 128 + ch);
 #pragma unroll
     for (int i = 0; i < FI; ++i) {
-      const uint4 w = widen_e4m3(q[ks & 1][i], sc[i]);
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&w);
+      const bf16x8 a = widen_e4m3_exact(q[ks & 1][i]);
 #pragma unroll
       for (int j = 0; j < TI; ++j)
         if (j < tiv) acc[i][j] = mfma32(a, b[j], acc[i][j]);
@@ -733,16 +740,16 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
   float sc[FI];
 #pragma unroll
   for (int i = 0; i < FI; ++i) sc[i] = 1.f;
-  // W8A8: acc holds the sum over 128-column blocks divided by sp, the
-  // product of the weight and row scales of the current block; entering a
-  // new block multiplies acc by old / new product, and the epilogue by sp.
+  // e4m3 weights: acc holds the sum over 128-column blocks divided by sp,
+  // the current block's weight scale (times the row scale under W8A8);
+  // entering a new block multiplies acc by old / new, the epilogue by sp.
   float sp[FI][TI];
 #pragma unroll
   for (int i = 0; i < FI; ++i)
 #pragma unroll
     for (int j = 0; j < TI; ++j) sp[i][j] = 1.f;
   auto finish = [&]() __attribute__((always_inline)) {
-    if constexpr (Cfg::XF8) {
+    if constexpr (Cfg::WF8) {
 #pragma unroll
       for (int i = 0; i < FI; ++i)
 #pragma unroll
@@ -769,17 +776,19 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
     if (active) {
       const char* sW = smem + (g % SW) * Cfg::WSTAGE;
       const char* sX = smem + Cfg::X_OFF + (g & 1) * Cfg::XSTAGE;
-      if constexpr (Cfg::XF8) {
+      if constexpr (Cfg::WF8) {
         if ((ckt & 1) == 0) {
-          // every slot entry is a positive finite scale (the slots start at
-          // 1 and hold real row scales after), so the ratio is finite; at a
-          // tile's first block acc is zero and the product stays zero
+          // a new 128-column block: weight scales, and under W8A8 the row
+          // scales from the slot this block's first k-tile filled.  Every
+          // scale is positive and finite (the slots start at 1 and hold real
+          // row scales after), so the ratio is finite; at a tile's first
+          // block acc is zero and stays zero
           p.w_scales(cst, wf0, ckt >> 1, sc);
           const float* sxs =
               reinterpret_cast<const float*>(smem + Cfg::SC_OFF + ((g >> 1) & 1) * (Cfg::BT * 4)) + wt0 + (lane & 31);
 #pragma unroll
           for (int j = 0; j < TI; ++j) {
-            const float sx = sxs[j * 32];
+            const float sx = Cfg::XF8 ? sxs[j * 32] : 1.f;
 #pragma unroll
             for (int i = 0; i < FI; ++i) {
               const float sn = sc[i] * sx;
@@ -790,10 +799,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
             }
           }
         }
-        mma_ktile_a8<FI, TI>(acc, sW, sX, wf0, wt0, lane, tiv);
-      } else if constexpr (Cfg::WF8) {
-        if ((ckt & 1) == 0) p.w_scales(cst, wf0, ckt >> 1, sc);  // one scale per 128 columns
-        mma_ktile_f8<FI, TI>(acc, sW, sX, wf0, wt0, lane, tiv, sc);
+        if constexpr (Cfg::XF8) mma_ktile_a8<FI, TI>(acc, sW, sX, wf0, wt0, lane, tiv);
+        else mma_ktile_f8<FI, TI>(acc, sW, sX, wf0, wt0, lane, tiv);
       } else {
         mma_ktile<FI, TI, false>(acc, sW, sX, wf0, wt0, lane, tiv);
       }
