@@ -353,6 +353,13 @@ def shared_experts(x, ws_gate, ws_value, ws_out, ss, tag, S, c):
     return y
 
 
+def _vector(v):
+    """A per-feature vector (gamma, b_router): stored fp32 values widen
+    exactly; a float64 array (test inputs only) is taken as it is."""
+    a = np.asarray(v)
+    return a.astype(np.float64) if a.dtype == np.float64 else a.astype(np.float32).astype(np.float64)
+
+
 def forward(inp, spec, forced_idx=None, forced_tol=1e-3):
     """Whole layer.  `inp` holds raw storage arrays under the keys x,
     w_router, b_router, w_down, w_gate, w_value, w_out, s_gate, s_value,
@@ -375,7 +382,7 @@ def forward(inp, spec, forced_idx=None, forced_tol=1e-3):
     b = np.asarray(inp["b_router"], dtype=np.float32).astype(np.float64)
     w_down = decode(inp.get("w_down"), act)
     w_up = decode(inp.get("w_up"), act)
-    gamma = np.asarray(inp["gamma"], dtype=np.float32).astype(np.float64)
+    gamma = _vector(inp["gamma"])
     T, H = x.shape
     E = w_router.shape[0]
 
@@ -420,4 +427,157 @@ def forward(inp, spec, forced_idx=None, forced_tol=1e-3):
     out = dict(r)
     out.update(z=z, offsets=offsets, sorted=sorted_, pos=pos, A=A, O=O, c=comb, n=n,
                shared=sh, y=y)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Backward pass (gradients of <y, dy> with respect to x and every weight)
+# ----------------------------------------------------------------------------
+# The pages motivate the layer's stabilisers by training (P2 stabilizer
+# passage); the gradients below are the chain rule of the forward above,
+# written step by step in reverse.  The top-k selection is piecewise constant,
+# so no gradient flows through the choice of experts or the selection bias;
+# the combine weights carry the router's gradient.
+
+def situ_glu_grad(g, v, c, da):
+    """d/dg and d/dv of a = silu(cap g) * cap v, times da.  cap'(u) =
+    1 - tanh(u / c)^2 (1 for c = inf); silu'(u) = sigma(u) (1 + u (1 -
+    sigma(u)))."""
+    if np.isfinite(c):
+        tg, tv = np.tanh(g / c), np.tanh(v / c)
+        cg, cv = c * tg, c * tv
+        dcg, dcv = 1.0 - tg * tg, 1.0 - tv * tv
+    else:
+        cg, cv, dcg, dcv = g, v, 1.0, 1.0
+    sg = sigmoid(cg)
+    dsilu = sg * (1.0 + cg * (1.0 - sg))
+    return da * cv * dsilu * dcg, da * cg * sg * dcv
+
+
+def rmsnorm_grad(c, gamma, eps, dn):
+    """n = gamma * c * r with r = (mean(c^2) + eps)^-1/2 per row.  Returns
+    dc = r u - r^3 c (u . c) / L with u = gamma * dn, and dgamma = sum over
+    rows of dn * c * r."""
+    L = c.shape[1]
+    r = 1.0 / np.sqrt(np.mean(c * c, axis=1, keepdims=True) + eps)
+    u = gamma[None, :] * dn
+    dc = r * u - r ** 3 * c * np.sum(u * c, axis=1, keepdims=True) / L
+    return dc, np.sum(dn * c * r, axis=0)
+
+
+def combine_grad(O, pos, w, dc):
+    """c_t = sum_j w_tj O[pos(t, j)]: dO[pos(t, j)] = w_tj dc_t and dw_tj =
+    dc_t . O[pos(t, j)]."""
+    T, k = w.shape
+    p = pos.reshape(T, k)
+    dO = np.zeros_like(O)
+    dw = np.zeros((T, k))
+    for j in range(k):
+        dO[p[:, j]] = w[:, j:j + 1] * dc
+        dw[:, j] = np.sum(dc * O[p[:, j]], axis=1)
+    return dO, dw
+
+
+def route_grad(scores, idx, dw):
+    """w_tj = s_tj / S_t over the selected scores (S_t their sum), s =
+    sigmoid(logit): ds_tj = (dw_tj - sum_j' dw_tj' w_tj') / S_t, and
+    dlogit = ds * s (1 - s) at the selected experts, 0 elsewhere."""
+    T, E = scores.shape
+    sel = np.take_along_axis(scores, idx, axis=1)
+    S = sel.sum(axis=1, keepdims=True)
+    w = sel / S
+    ds = (dw - np.sum(dw * w, axis=1, keepdims=True)) / S
+    dlogits = np.zeros((T, E))
+    np.put_along_axis(dlogits, idx, ds * sel * (1.0 - sel), axis=1)
+    return dlogits
+
+
+def backward(inp, spec, dy, forced_idx=None, forced_tol=1e-3):
+    """Gradients of sum(y * dy) for one layer (the forward's inputs and spec;
+    dy [T, H] float64).  Returns the forward's intermediates plus dx and
+    d<weight> for every weight present (dw_router, dw_down, dw_gate,
+    dw_value, dw_out, dgamma, dw_up, dws_gate, dws_value, dws_out).  Expert
+    weights are decoded exactly as in the forward; W8A8 is not covered."""
+    act, wt = spec["act"], spec["w_expert"]
+    k, c, eps = int(spec["k"]), float(spec["cap"]), float(spec["eps"])
+    if spec.get("a8"):
+        raise ValueError("the backward covers the unquantised layer")
+    f = forward(inp, spec, forced_idx=forced_idx, forced_tol=forced_tol)
+    x = decode(inp["x"], act)
+    w_router = decode(inp["w_router"], act)
+    w_down = decode(inp.get("w_down"), act)
+    w_up = decode(inp.get("w_up"), act)
+    gamma = _vector(inp["gamma"])
+    dy = np.asarray(dy, dtype=np.float64)
+    T, H = x.shape
+    E = w_router.shape[0]
+    idx, wts, z = f["idx"], f["w"], f["z"]
+    L = z.shape[1]
+    g = {}
+
+    # up-projection: y = n W_up^T + shared
+    dn = dy if w_up is None else dy @ w_up
+    if w_up is not None:
+        g["dw_up"] = dy.T @ f["n"]
+    # shared experts
+    dx = np.zeros((T, H))
+    S = 0 if inp.get("ws_gate") is None else len(inp["ws_gate"])
+    ss = (inp.get("ss_gate"), inp.get("ss_value"), inp.get("ss_out"))
+    if S:
+        dsg, dsv, dso = [], [], []
+        for s in range(S):
+            wg = matrix(inp["ws_gate"], ss[0], s, wt)
+            wv = matrix(inp["ws_value"], ss[1], s, wt)
+            wo = matrix(inp["ws_out"], ss[2], s, wt)
+            gs, vs = x @ wg.T, x @ wv.T
+            hs = situ_glu(gs, vs, c)
+            dso.append(dy.T @ hs)
+            dgs, dvs = situ_glu_grad(gs, vs, c, dy @ wo)
+            dsg.append(dgs.T @ x)
+            dsv.append(dvs.T @ x)
+            dx += dgs @ wg + dvs @ wv
+        g["dws_gate"], g["dws_value"], g["dws_out"] = np.stack(dsg), np.stack(dsv), np.stack(dso)
+    # RMSNorm and combine
+    dcomb, g["dgamma"] = rmsnorm_grad(f["c"], gamma, eps, dn)
+    dO, dwts = combine_grad(f["O"], f["pos"], wts, dcomb)
+    # routed experts (sorted order)
+    offsets, sorted_ = f["offsets"], f["sorted"]
+    I = f["A"].shape[1]
+    dgate = np.zeros((E, I, L))
+    dvalue = np.zeros((E, I, L))
+    dout = np.zeros((E, L, I))
+    dzrows = np.zeros((T * k, L))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        zr = z[sorted_[lo:hi] // k]
+        wg = matrix(inp["w_gate"], inp.get("s_gate"), e, wt)
+        wv = matrix(inp["w_value"], inp.get("s_value"), e, wt)
+        wo = matrix(inp["w_out"], inp.get("s_out"), e, wt)
+        ge, ve = zr @ wg.T, zr @ wv.T
+        ae = situ_glu(ge, ve, c)
+        dout[e] = dO[lo:hi].T @ ae
+        dge, dve = situ_glu_grad(ge, ve, c, dO[lo:hi] @ wo)
+        dgate[e] = dge.T @ zr
+        dvalue[e] = dve.T @ zr
+        dzrows[lo:hi] = dge @ wg + dve @ wv
+    g["dw_gate"], g["dw_value"], g["dw_out"] = dgate, dvalue, dout
+    # each token's latent gradient: sum over its k assignments
+    dz = np.zeros((T, L))
+    p = f["pos"].reshape(T, k)
+    for j in range(k):
+        dz += dzrows[p[:, j]]
+    if w_down is None:
+        dx += dz
+    else:
+        g["dw_down"] = dz.T @ x
+        dx += dz @ w_down
+    # router, through the combine weights
+    dlogits = route_grad(f["scores"], idx, dwts)
+    g["dw_router"] = dlogits.T @ x
+    dx += dlogits @ w_router
+    g["dx"] = dx
+    out = dict(f)
+    out.update(g, dn=dn, dc=dcomb, dO=dO, dwts=dwts, dz=dz, dlogits=dlogits)
     return out

@@ -621,6 +621,96 @@ def pin_a8_row_independence_and_bounded_change():
     assert rel.max() < 0.1 and rel.min() > 1e-4
 
 
+_GRADS = ("dx", "dw_router", "dw_down", "dw_gate", "dw_value", "dw_out", "dgamma", "dw_up", "dws_gate",
+          "dws_value", "dws_out")
+_PARAM = {"dx": "x", "dw_router": "w_router", "dw_down": "w_down", "dw_gate": "w_gate", "dw_value": "w_value",
+          "dw_out": "w_out", "dgamma": "gamma", "dw_up": "w_up", "dws_gate": "ws_gate", "dws_value": "ws_value",
+          "dws_out": "ws_out"}
+
+
+def _torch_layer_grads(inp, spec, idx, dy):
+    """The layer written again with torch ops on float64 leaves, one token
+    and slot at a time, differentiated by torch.autograd."""
+    c = float(spec["cap"])
+    capf = (lambda u: c * torch.tanh(u / c)) if math.isfinite(c) else (lambda u: u)
+    leaves = {}
+    for name in ("x", "w_router", "w_down", "w_gate", "w_value", "w_out", "gamma", "w_up", "ws_gate", "ws_value",
+                 "ws_out"):
+        if inp.get(name) is not None:
+            leaves[name] = t64(inp[name]).clone().requires_grad_(True)
+    x = leaves["x"]
+    T = x.shape[0]
+    k = idx.shape[1]
+    s = torch.sigmoid(x @ leaves["w_router"].T)
+    ti = torch.from_numpy(np.asarray(idx, dtype=np.int64))
+    sel = s.gather(1, ti)
+    w = sel / sel.sum(1, keepdim=True)
+    z = x @ leaves["w_down"].T if "w_down" in leaves else x
+    rows = []
+    for t in range(T):
+        acc = 0
+        for j in range(k):
+            e = int(idx[t, j])
+            a = F.silu(capf(leaves["w_gate"][e] @ z[t])) * capf(leaves["w_value"][e] @ z[t])
+            acc = acc + w[t, j] * (leaves["w_out"][e] @ a)
+        rows.append(acc)
+    comb = torch.stack(rows)
+    n = leaves["gamma"] * comb / torch.sqrt((comb * comb).mean(1, keepdim=True) + spec["eps"])
+    y = n @ leaves["w_up"].T if "w_up" in leaves else n
+    if "ws_gate" in leaves:
+        for si in range(leaves["ws_gate"].shape[0]):
+            h = F.silu(capf(x @ leaves["ws_gate"][si].T)) * capf(x @ leaves["ws_value"][si].T)
+            y = y + h @ leaves["ws_out"][si].T
+    (y * t64(dy)).sum().backward()
+    return {g: leaves[p].grad.numpy() for g, p in _PARAM.items() if p in leaves}
+
+
+def _bwd_cases():
+    yield rand_layer(91, T=7, E=5, k=2, S=2, I=6, Is=5, L=8, H=10)
+    yield rand_layer(92, T=6, E=4, k=3, S=0, identity=True, H=9, I=4)
+    yield rand_layer(93, T=5, E=6, k=2, S=1, I=5, Is=3, cap=float("inf"))
+    inp, spec = rand_layer(94, T=5, E=3, k=1, S=1, I=4, Is=4, cap=1.5)  # a small cap, well inside the tanh
+    yield inp, spec
+
+
+def pin_backward_vs_torch_autograd():
+    """Every gradient against torch.autograd of an independent torch forward
+    (same selection), on layers with and without projections, shared experts
+    and the cap."""
+    for inp, spec in _bwd_cases():
+        f = O.forward(inp, spec)
+        dy = np.random.default_rng(95).standard_normal(f["y"].shape)
+        b = O.backward(inp, spec, dy)
+        ref = _torch_layer_grads(inp, spec, f["idx"], dy)
+        for gname, want in ref.items():
+            close(b[gname], want, rtol=1e-9, atol=1e-11)
+        assert set(ref) == {gname for gname in _GRADS if gname in b}
+
+
+def pin_backward_finite_differences():
+    """Central differences of <y, dy> along a random direction of each input
+    and weight, with the selection held fixed (the oracle's own forward)."""
+    for inp, spec in _bwd_cases():
+        f = O.forward(inp, spec)
+        rng = np.random.default_rng(96)
+        dy = rng.standard_normal(f["y"].shape)
+        b = O.backward(inp, spec, dy)
+        h = 1e-6
+        for gname, pname in _PARAM.items():
+            if inp.get(pname) is None:
+                continue
+            base = np.asarray(inp[pname], dtype=np.float64)
+            d = rng.standard_normal(base.shape)
+            fx = []
+            for sign in (1, -1):
+                pert = dict(inp)
+                pert[pname] = base + sign * h * d  # float64 (gamma too: taken as it is)
+                fx.append(np.sum(O.forward(pert, spec, forced_idx=f["idx"])["y"] * dy))
+            fd = (fx[0] - fx[1]) / (2 * h)
+            an = float(np.sum(b[gname] * d))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (gname, fd, an)
+
+
 PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]
 
 
@@ -784,7 +874,41 @@ def _mut_bf16_round_truncates(v):
     return np.ldexp(np.trunc(np.ldexp(m, 8)), e - 8)
 
 
+def _mut_situ_grad_no_cap_slope(g, v, c, da):
+    cg, cv = O.cap(g, c), O.cap(v, c)
+    sg = O.sigmoid(cg)
+    return da * cv * sg * (1.0 + cg * (1.0 - sg)), da * cg * sg
+
+
+def _mut_rmsnorm_grad_no_mean_term(c, gamma, eps, dn):
+    r = 1.0 / np.sqrt(np.mean(c * c, axis=1, keepdims=True) + eps)
+    return r * gamma[None, :] * dn, np.sum(dn * c * r, axis=0)
+
+
+def _mut_combine_grad_unweighted(O_, pos, w, dc):
+    T, k = w.shape
+    p = pos.reshape(T, k)
+    dO = np.zeros_like(O_)
+    dw = np.zeros((T, k))
+    for j in range(k):
+        dO[p[:, j]] = dc
+        dw[:, j] = np.sum(dc * O_[p[:, j]], axis=1)
+    return dO, dw
+
+
+def _mut_route_grad_unrenormalised(scores, idx, dw):
+    sel = np.take_along_axis(scores, idx, axis=1)
+    S = sel.sum(axis=1, keepdims=True)
+    out = np.zeros_like(scores)
+    np.put_along_axis(out, idx, dw / S * sel * (1 - sel), axis=1)
+    return out
+
+
 MUTANTS = {
+    "situ_glu_grad": [_mut_situ_grad_no_cap_slope],
+    "rmsnorm_grad": [_mut_rmsnorm_grad_no_mean_term],
+    "combine_grad": [_mut_combine_grad_unweighted],
+    "route_grad": [_mut_route_grad_unrenormalised],
     "e4m3fn_encode": [_mut_encode_truncates],
     "quantize_1x128": [_mut_quantize_per_row, _mut_quantize_e4m3_max_240],
     "fp8_activations": [_mut_fp8_activations_skipped, _mut_fp8_activations_unrounded],
