@@ -252,6 +252,37 @@ lmoe_status lmoe_pack_experts(const lmoe_shape *shape, const lmoe_weights *w, vo
  * Asynchronous on `stream`.                                                    */
 lmoe_status lmoe_quantize_1x128(const void *x, int64_t R, int32_t C, void *q, float *scales, void *stream);
 
+/* Backward pass of the layer (the pages motivate the cap and the norm by
+ * training stability, P2 stabilizer passage): gradients of sum(y * dy) with
+ * respect to x and every weight, for BF16 layers with BF16 expert weights in
+ * the row-major layout (w_gate / w_value / w_out; a packed copy is not read).
+ * The forward is recomputed inside, from x, with the same selection rule;
+ * the selection and its bias carry no gradient, the combine weights carry the
+ * router's.  Every gradient is fp32 and written whole (experts no token chose
+ * get zeros).  Device pointers, caller-owned, not aliasing each other or the
+ * inputs:
+ *   dx [T, H] (may be NULL when T == 0); dw_router [E, H]; dw_down [L, H] (not written when w_down is
+ *   NULL); dw_gate, dw_value [E, I, L]; dw_out [E, L, I]; dgamma [L];
+ *   dw_up [H, L] (not written when w_up is NULL); dws_gate, dws_value
+ *   [S, Is, H], dws_out [S, H, Is] (not written when S == 0).
+ * dy [T, H] is BF16.  topk_idx [T, k] receives the selection if not NULL.
+ * The workspace holds lmoe_backward_workspace_bytes(shape) bytes (256-byte
+ * aligned).  T <= 65535.  EUNSUPPORTED for other dtypes, for a8 and for larger
+ * T; EINVAL for a missing
+ * pointer; EWORKSPACE for a short workspace.  Asynchronous on `stream`.      */
+typedef struct {
+  float *dx;
+  float *dw_router;
+  float *dw_down;
+  float *dw_gate, *dw_value, *dw_out;
+  float *dgamma;
+  float *dw_up;
+  float *dws_gate, *dws_value, *dws_out;
+} lmoe_grads;
+size_t lmoe_backward_workspace_bytes(const lmoe_shape *shape);
+lmoe_status lmoe_backward(const lmoe_shape *shape, const lmoe_weights *w, const void *x, const void *dy,
+                          int32_t *topk_idx, const lmoe_grads *grads, void *ws, size_t ws_bytes, void *stream);
+
 /* Name of a status code; message of the calling thread's last failure.       */
 const char *lmoe_status_str(lmoe_status s);
 const char *lmoe_last_error(void);

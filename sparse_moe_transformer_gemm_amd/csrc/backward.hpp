@@ -1,0 +1,405 @@
+// Backward pass of the layer: a generic MFMA GEMM for the gradient GEMMs
+// (dense and per-expert, with either operand stored k-contiguous or
+// row-contiguous) and the elementwise gradient kernels (SiTU-GLU, RMSNorm,
+// weighted combine, router).  Gradients are fp32.
+//
+// Sources: P2 wpnews.pro "The 2.8-Trillion-Parameter Problem", stabilizer
+// passage (the cap and the norm are there to keep training stable); the
+// chain rule of the forward steps of P2's Stable LatentMoE passage.
+#pragma once
+
+#include "common.hpp"
+
+namespace lmoe {
+
+// ---------------------------------------------------------------------------
+// Generic GEMM: C[m, n] (= or +=) sum_k A(m, k) B(n, k), fp32 out (or bf16),
+// bf16 32x32x16 MFMAs with fp32 accumulation; fp32 operands are rounded to
+// bf16 (nearest even) as they are staged into LDS.
+//
+// An operand element (r, k) -- r the operand's row (m for A, n for B) -- is
+// stored at  base + sr * ld + k   (RC = 0: k contiguous), or
+//            base + sr * ld + r   (RC = 1: rows contiguous),
+// where the stored row sr is r (RC = 0) or k (RC = 1), plus the group's first
+// assignment row when `grow` is set, and then mapped through `gather`
+// (sr -> gather[sr] / gk) when that is given.  `gstride` moves the base by
+// group (stacked expert weights).
+//
+// Modes: BG_DENSE (one matrix); BG_GROUP_M (per expert, M = the expert's
+// assignment rows, walked through the expert tile list of 128-row tiles; C
+// rows are assignment rows); BG_GROUP_K (per expert, K = the expert's
+// assignment rows, one grid slice per expert; C moves by cgstride).
+// ---------------------------------------------------------------------------
+enum { BG_DENSE = 0, BG_GROUP_M = 1, BG_GROUP_K = 2 };
+
+struct BgOp {
+  const char* p;
+  int64_t ld;
+  int64_t gstride;
+  const int* gather;
+  int gk;
+  int grow;
+};
+
+struct BgArgs {
+  BgOp a, b;
+  char* c;
+  int64_t ldc, cgstride;
+  int M, N, K;
+  int accumulate, cbf16;
+  const int* offsets;
+  const int4* tiles;
+  const int* tile_count;
+};
+
+constexpr int kBgM = 128, kBgN = 128, kBgK = 32, kBgPitch = 80;  // LDS row: 32 bf16 + 16 B pad
+
+__device__ __forceinline__ unsigned short f2bf(float f) {
+  const bf16 h = (bf16)f;  // round to nearest even
+  return *reinterpret_cast<const unsigned short*>(&h);
+}
+
+// Loads 8 consecutive stored elements (along the contiguous dimension) as
+// bf16; `n` of them are valid (the rest are zero).
+template <int F32>
+__device__ __forceinline__ uint4 bg_load8(const char* p, int n, bool vec) {
+  if (F32) {
+    const float* f = reinterpret_cast<const float*>(p);
+    float v[8];
+    if (vec && n == 8) {
+      const float4 u = *reinterpret_cast<const float4*>(f);
+      const float4 w = *reinterpret_cast<const float4*>(f + 4);
+      v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w; v[4] = w.x; v[5] = w.y; v[6] = w.z; v[7] = w.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = i < n ? f[i] : 0.f;
+    }
+    uint4 o;
+    o.x = f2bf(v[0]) | ((unsigned)f2bf(v[1]) << 16);
+    o.y = f2bf(v[2]) | ((unsigned)f2bf(v[3]) << 16);
+    o.z = f2bf(v[4]) | ((unsigned)f2bf(v[5]) << 16);
+    o.w = f2bf(v[6]) | ((unsigned)f2bf(v[7]) << 16);
+    return o;
+  } else {
+    if (vec && n == 8) return *reinterpret_cast<const uint4*>(p);
+    const unsigned short* h = reinterpret_cast<const unsigned short*>(p);
+    unsigned short v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = i < n ? h[i] : (unsigned short)0;
+    return uint4{v[0] | ((unsigned)v[1] << 16), v[2] | ((unsigned)v[3] << 16), v[4] | ((unsigned)v[5] << 16),
+                 v[6] | ((unsigned)v[7] << 16)};
+  }
+}
+
+// One operand tile (128 rows x 32 k) of one k-tile into registers: 512
+// vectors of 8 elements, two per thread.  rows / kv: valid rows and k.
+template <int RC, int F32>
+struct BgTile {
+  uint4 v[2];
+  __device__ __forceinline__ void load(const BgOp& o, const char* base, int rowbase, int r0, int rows, int k0,
+                                       int kv, bool vec, int tid) {
+    constexpr int ES = F32 ? 4 : 2;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int vi = tid + 256 * q;
+      if (!RC) {
+        const int r = vi >> 2, kk = (vi & 3) * 8;
+        const int n = min(8, kv - kk);
+        if (r < rows && n > 0) {
+          int sr = r0 + r + (o.grow ? rowbase : 0);
+          if (o.gather) sr = o.gather[sr] / o.gk;
+          v[q] = bg_load8<F32>(base + ((int64_t)sr * o.ld + k0 + kk) * ES, n, vec);
+        } else {
+          v[q] = uint4{0u, 0u, 0u, 0u};
+        }
+      } else {
+        const int kk = vi >> 4, r8 = (vi & 15) * 8;
+        const int n = min(8, rows - r8);
+        if (kk < kv && n > 0) {
+          int sr = k0 + kk + (o.grow ? rowbase : 0);
+          if (o.gather) sr = o.gather[sr] / o.gk;
+          v[q] = bg_load8<F32>(base + ((int64_t)sr * o.ld + r0 + r8) * ES, n, vec);
+        } else {
+          v[q] = uint4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  }
+  // LDS image: row r at r * kBgPitch, k contiguous
+  __device__ __forceinline__ void store(char* s, int tid) const {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int vi = tid + 256 * q;
+      if (!RC) {
+        const int r = vi >> 2, kk = (vi & 3) * 8;
+        *reinterpret_cast<uint4*>(s + r * kBgPitch + kk * 2) = v[q];
+      } else {
+        const int kk = vi >> 4, r8 = (vi & 15) * 8;
+        const unsigned w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<unsigned short*>(s + (r8 + i) * kBgPitch + kk * 2) =
+              (unsigned short)(w[i >> 1] >> (16 * (i & 1)));
+      }
+    }
+  }
+};
+
+// 16-byte loads need the row pitch and the base 16-byte aligned.
+__device__ __forceinline__ bool bg_vec_ok(const char* base, int64_t ld, int es) {
+  return ((reinterpret_cast<uintptr_t>(base) & 15) == 0) && ((ld * es) % 16 == 0);
+}
+
+template <int MODE, int ARC, int AF32, int BRC, int BF32>
+__global__ __launch_bounds__(256) void bgemm_kernel(const BgArgs p) {
+  __shared__ __attribute__((aligned(16))) char sA[2][kBgM * kBgPitch];
+  __shared__ __attribute__((aligned(16))) char sB[2][kBgN * kBgPitch];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int e = 0, rowbase = 0, M = p.M, K = p.K, m0 = 0;
+  const int n0 = blockIdx.x * kBgN;
+  if (MODE == BG_DENSE) {
+    m0 = blockIdx.y * kBgM;
+  } else if (MODE == BG_GROUP_M) {
+    const int j = blockIdx.y;
+    if (j >= *p.tile_count) return;
+    const int4 te = p.tiles[j];
+    e = te.x;
+    rowbase = p.offsets[e];
+    M = p.offsets[e + 1] - rowbase;
+    m0 = (j - te.y) * kBgM;
+  } else {
+    e = blockIdx.z;
+    m0 = blockIdx.y * kBgM;
+    rowbase = p.offsets[e];
+    K = p.offsets[e + 1] - rowbase;
+  }
+  if (m0 >= M || n0 >= p.N) return;
+  const int rows_a = min(kBgM, M - m0), rows_b = min(kBgN, p.N - n0);
+  const char* abase = p.a.p + (int64_t)e * p.a.gstride * (AF32 ? 4 : 2);
+  const char* bbase = p.b.p + (int64_t)e * p.b.gstride * (BF32 ? 4 : 2);
+  const bool avec = bg_vec_ok(abase, p.a.ld, AF32 ? 4 : 2);
+  const bool bvec = bg_vec_ok(bbase, p.b.ld, BF32 ? 4 : 2);
+
+  const int wm = (wid & 1) * 64, wn = (wid >> 1) * 64;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  BgTile<ARC, AF32> ta;
+  BgTile<BRC, BF32> tb;
+  const int nk = (K + kBgK - 1) / kBgK;
+  auto load = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = kt * kBgK, kv = min(kBgK, K - k0);
+    ta.load(p.a, abase, rowbase, m0, rows_a, k0, kv, avec, tid);
+    tb.load(p.b, bbase, rowbase, n0, rows_b, k0, kv, bvec, tid);
+  };
+  if (nk > 0) {
+    load(0);
+    ta.store(sA[0], tid);
+    tb.store(sB[0], tid);
+  }
+  __syncthreads();
+  const int lr = lane & 31, kh = (lane >> 5) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(sA[cur] + (wm + i * 32 + lr) * kBgPitch + (ks * 16 + kh) * 2);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const bf16x8*>(sB[cur] + (wn + j * 32 + lr) * kBgPitch + (ks * 16 + kh) * 2);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      ta.store(sA[cur ^ 1], tid);
+      tb.store(sB[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  // lane l holds column n = l % 32 of each 32x32 block and rows
+  // 8 g + 4 (l / 32) + r (g, r < 4)
+  char* cbase = p.c + (int64_t)e * p.cgstride * (p.cbf16 ? 2 : 4);
+  const int crow0 = (MODE == BG_GROUP_M ? rowbase : 0) + m0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = wn + j * 32 + lr;
+      if (n >= rows_b) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = wm + i * 32 + g * 8 + (lane >> 5) * 4 + r;
+          if (m >= rows_a) continue;
+          const int64_t off = (int64_t)(crow0 + m) * p.ldc + n0 + n;
+          float v = acc[i][j][4 * g + r];
+          if (p.cbf16) {
+            reinterpret_cast<unsigned short*>(cbase)[off] = f2bf(v);
+          } else {
+            float* cp = reinterpret_cast<float*>(cbase) + off;
+            if (p.accumulate) v += *cp;
+            *cp = v;
+          }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Elementwise gradient kernels.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bw_sigmoid(float u) { return 1.f / (1.f + expf(-u)); }
+
+// SiTU-GLU on flat arrays: mode 0 writes a = silu(cap g) cap v; mode 1
+// writes dg, dv of a given da (may alias g and v: each element is read
+// before it is written by the same thread).
+__global__ __launch_bounds__(256) void bw_situ_kernel(int mode, const float* g, const float* v, const float* da,
+                                                      float* o1, float* o2, int64_t n, float cap, float inv_cap) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float gg = g[i], vv = v[i];
+  float cg = gg, cv = vv, dcg = 1.f, dcv = 1.f;
+  if (inv_cap > 0.f) {
+    const float tg = tanhf(gg * inv_cap), tv = tanhf(vv * inv_cap);
+    cg = cap * tg;
+    cv = cap * tv;
+    dcg = 1.f - tg * tg;
+    dcv = 1.f - tv * tv;
+  }
+  const float sg = bw_sigmoid(cg);
+  if (mode == 0) {
+    o1[i] = cg * sg * cv;
+  } else {
+    const float d = da[i];
+    o1[i] = d * cv * sg * (1.f + cg * (1.f - sg)) * dcg;
+    o2[i] = d * cg * sg * dcv;
+  }
+}
+
+// Block sum of one float per thread (256 threads); every thread gets it.
+__device__ __forceinline__ float bw_block_sum(float v, float* red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// Per token: c = sum_j w_tj O[pos(t, j)] (fp32, j ascending), r = (mean c^2 +
+// eps)^-1/2, n = gamma c r.  Writes c, n and r.
+__global__ __launch_bounds__(256) void bw_combine_norm_kernel(const float* O, const int32_t* pos, const float* w,
+                                                              const float* gamma, int L, int k, float eps, float* c,
+                                                              float* n, float* r) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  float ss = 0.f;
+  for (int l = threadIdx.x; l < L; l += 256) {
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) acc += w[t * k + j] * O[(int64_t)pos[t * k + j] * L + l];
+    c[t * L + l] = acc;
+    ss += acc * acc;
+  }
+  const float rr = 1.f / sqrtf(bw_block_sum(ss, red) / L + eps);
+  for (int l = threadIdx.x; l < L; l += 256) n[t * L + l] = gamma[l] * c[t * L + l] * rr;
+  if (threadIdx.x == 0) r[t] = rr;
+}
+
+// Per token: dc = r u - r^3 c (u . c) / L with u = gamma dn; then for each
+// slot j, dO[pos(t, j)] = w_tj dc and dw_tj = dc . O[pos(t, j)].  dc is
+// recomputed per element and slot rather than stored.
+__global__ __launch_bounds__(256) void bw_norm_combine_grad_kernel(const float* dn, const float* c, const float* r,
+                                                                   const float* gamma, const float* O,
+                                                                   const int32_t* pos, const float* w, int L, int k,
+                                                                   float* dO, float* dw) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  const float rr = r[t];
+  float uc = 0.f;
+  for (int l = threadIdx.x; l < L; l += 256) uc += gamma[l] * dn[t * L + l] * c[t * L + l];
+  const float coef = rr * rr * rr * bw_block_sum(uc, red) / L;
+  for (int j = 0; j < k; ++j) {
+    const int64_t a = pos[t * k + j];
+    const float wj = w[t * k + j];
+    float dot = 0.f;
+    for (int l = threadIdx.x; l < L; l += 256) {
+      const float dc = rr * gamma[l] * dn[t * L + l] - coef * c[t * L + l];
+      dO[a * L + l] = wj * dc;
+      dot += dc * O[a * L + l];
+    }
+    const float s = bw_block_sum(dot, red);
+    if (threadIdx.x == 0) dw[t * k + j] = s;
+  }
+}
+
+// dgamma partials: part[y, l] = sum over tokens t of chunk y of dn c r.
+__global__ __launch_bounds__(256) void bw_dgamma_part_kernel(const float* dn, const float* c, const float* r,
+                                                             int64_t T, int L, int64_t chunk, float* part) {
+  const int l = blockIdx.x * 256 + threadIdx.x;
+  if (l >= L) return;
+  const int64_t t0 = (int64_t)blockIdx.y * chunk, t1 = min(T, t0 + chunk);
+  float s = 0.f;
+  for (int64_t t = t0; t < t1; ++t) s += dn[t * L + l] * c[t * L + l] * r[t];
+  part[(int64_t)blockIdx.y * L + l] = s;
+}
+
+// Sum of `rows` partial rows [rows, L] into out[L] (rows in order).
+__global__ __launch_bounds__(256) void bw_sum_rows_kernel(const float* part, int rows, int L, float* out) {
+  const int l = blockIdx.x * 256 + threadIdx.x;
+  if (l >= L) return;
+  float s = 0.f;
+  for (int y = 0; y < rows; ++y) s += part[(int64_t)y * L + l];
+  out[l] = s;
+}
+
+// Router: per token, dlogit = ds s (1 - s) at the selected experts (0
+// elsewhere), ds_j = (dw_j - sum_j' dw_j' w_j') / S, S = sum of the selected
+// sigmoid scores, w_j = s_j / S.
+__global__ __launch_bounds__(256) void bw_route_grad_kernel(const float* logits, const int32_t* idx, const float* dw,
+                                                            int E, int k, float* dlogits) {
+  const int64_t t = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 256) dlogits[t * E + e] = 0.f;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float S = 0.f, dot = 0.f;
+    for (int j = 0; j < k; ++j) S += bw_sigmoid(logits[t * E + idx[t * k + j]]);
+    for (int j = 0; j < k; ++j) dot += dw[t * k + j] * bw_sigmoid(logits[t * E + idx[t * k + j]]) / S;
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      const float s = bw_sigmoid(logits[t * E + e]);
+      dlogits[t * E + e] = (dw[t * k + j] - dot) / S * s * (1.f - s);
+    }
+  }
+}
+
+// dz_t = sum_j dzrows[pos(t, j)] (j ascending); written, or added to out.
+__global__ __launch_bounds__(256) void bw_gather_sum_kernel(const float* rows, const int32_t* pos, int L, int k,
+                                                            float* out, int accumulate) {
+  const int64_t t = blockIdx.y;
+  const int l = blockIdx.x * 256 + threadIdx.x;
+  if (l >= L) return;
+  float s = 0.f;
+  for (int j = 0; j < k; ++j) s += rows[(int64_t)pos[t * k + j] * L + l];
+  if (accumulate) s += out[t * L + l];
+  out[t * L + l] = s;
+}
+
+// bf16 -> fp32 of n elements.
+__global__ __launch_bounds__(256) void bw_widen_kernel(const unsigned short* x, float* y, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) y[i] = __uint_as_float((unsigned)x[i] << 16);
+}
+
+}  // namespace lmoe

@@ -7,6 +7,7 @@
 
 #include <mutex>
 
+#include "backward.hpp"
 #include "gemm2.hpp"
 #include "kernels.hpp"
 #include "lmoe.h"
@@ -549,6 +550,88 @@ lmoe_status record(void* const* ev, int i, hipStream_t st) {
   return LMOE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Backward pass: workspace plan and launch helpers.
+// ---------------------------------------------------------------------------
+constexpr int kBwChunks = 64;  // token chunks of the dgamma reduction
+
+struct BPlan {
+  size_t logits, z, idx, w, bcounts, offsets, sorted, pos, tiles, tcount;
+  size_t G, V, A, dA, O, dO, c, n, dn, dz, r, dw, dl, gs, vs, hs, dhs, dgp, total;
+};
+
+BPlan bplan(const lmoe_shape* sh) {
+  BPlan p{};
+  const size_t T = (size_t)sh->T, tk = T * sh->k, sis = (size_t)sh->S * (sh->S ? sh->Is : 0);
+  const size_t nb = (T + kPermTokens - 1) / kPermTokens;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  p.logits = take(T * sh->E * 4);
+  p.z = take(T * sh->L * 2);
+  p.idx = take(tk * 4);
+  p.w = take(tk * 4);
+  p.bcounts = take(nb * sh->E * 4);
+  p.offsets = take((size_t)(sh->E + 1) * 4);
+  p.sorted = take(tk * 4);
+  p.pos = take(tk * 4);
+  p.tiles = take((size_t)max_tiles(sh, kBgM) * 16);
+  p.tcount = take(8);
+  p.G = take(tk * sh->I * 4);
+  p.V = take(tk * sh->I * 4);
+  p.A = take(tk * sh->I * 4);
+  p.dA = take(tk * sh->I * 4);
+  p.O = take(tk * sh->L * 4);
+  p.dO = take(tk * sh->L * 4);
+  p.c = take(T * sh->L * 4);
+  p.n = take(T * sh->L * 4);
+  p.dn = take(T * sh->L * 4);
+  p.dz = take(T * sh->L * 4);
+  p.r = take(T * 4);
+  p.dw = take(tk * 4);
+  p.dl = take(T * sh->E * 4);
+  p.gs = take(T * sis * 4);
+  p.vs = take(T * sis * 4);
+  p.hs = take(T * sis * 4);
+  p.dhs = take(T * sis * 4);
+  p.dgp = take((size_t)kBwChunks * sh->L * 4);
+  p.total = off;
+  return p;
+}
+
+BgOp bop(const void* p, int64_t ld, int64_t gstride = 0, const int* gather = nullptr, int gk = 1, int grow = 0) {
+  return BgOp{static_cast<const char*>(p), ld, gstride, gather, gk, grow};
+}
+
+template <int MODE, int ARC, int AF32, int BRC, int BF32>
+hipError_t bg(BgOp a, BgOp b, void* c, int64_t ldc, int M, int N, int K, int accumulate, hipStream_t st,
+              const lmoe_shape* sh, int cbf16 = 0, int64_t cgstride = 0, const int* offsets = nullptr,
+              const int4* tiles = nullptr, const int* tcount = nullptr) {
+  BgArgs p{a, b, static_cast<char*>(c), ldc, cgstride, M, N, K, accumulate, cbf16, offsets, tiles, tcount};
+  dim3 grid((unsigned)cdiv(N, kBgN), 1, 1);
+  if (MODE == BG_DENSE) grid.y = (unsigned)cdiv(M, kBgM);
+  else if (MODE == BG_GROUP_M) grid.y = (unsigned)max_tiles(sh, kBgM);
+  else {
+    grid.y = (unsigned)cdiv(M, kBgM);
+    grid.z = (unsigned)sh->E;
+  }
+  if (grid.x == 0 || grid.y == 0 || N <= 0) return hipSuccess;
+  hipLaunchKernelGGL((bgemm_kernel<MODE, ARC, AF32, BRC, BF32>), grid, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t bw_situ(int mode, float* g, float* v, const float* da, float* o1, float* o2, int64_t n, const lmoe_shape* sh,
+                   hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const float inv = isinf(sh->cap) ? 0.f : 1.f / sh->cap;
+  hipLaunchKernelGGL(bw_situ_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, mode, g, v, da, o1, o2, n,
+                     sh->cap, inv);
+  return hipGetLastError();
+}
+
 }  // namespace
 }  // namespace lmoe
 
@@ -769,6 +852,160 @@ lmoe_status lmoe_quantize_1x128(const void* x, int64_t R, int32_t C, void* q, fl
     return fail(LMOE_EINVAL, "x must be 16-byte, q 8-byte and scales 4-byte aligned");
   if (R * (int64_t)(C / 128) > (int64_t)INT32_MAX * 16) return fail(LMOE_EUNSUPPORTED, "too many blocks");
   LMOE_HIP(launch_quant_1x128(x, R, C, q, scales, static_cast<hipStream_t>(stream)), "1x128 quantisation");
+  return LMOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Backward pass.
+// ---------------------------------------------------------------------------
+size_t lmoe_backward_workspace_bytes(const lmoe_shape* sh) {
+  if (check_shape(sh) != LMOE_OK) return 0;
+  return bplan(sh).total;
+}
+
+lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const void* x, const void* dy,
+                          int32_t* topk_idx, const lmoe_grads* gr, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (lmoe_status s = check_shape(sh)) return s;
+  if (!(sh->act == LMOE_BF16 && sh->w_expert == LMOE_BF16) || sh->a8)
+    return fail(LMOE_EUNSUPPORTED, "the backward pass takes BF16 layers with BF16 expert weights (no a8)");
+  if (lmoe_status s = check_weights(sh, w, NEED_ROUTE | NEED_EXPERT | NEED_UP | NEED_NORM)) return s;
+  if (sh->T > 65535) return fail(LMOE_EUNSUPPORTED, "the backward pass takes at most 65535 tokens per call");
+  if (!w->w_gate || !w->w_value || !w->w_out) return fail(LMOE_EINVAL, "the backward reads row-major w_gate, w_value, w_out");
+  if (!gr) return fail(LMOE_EINVAL, "grads is NULL");
+  if ((!gr->dx && sh->T > 0) || !gr->dw_router || !gr->dw_gate || !gr->dw_value || !gr->dw_out || !gr->dgamma ||
+      (w->w_down && !gr->dw_down) || (w->w_up && !gr->dw_up) ||
+      (sh->S > 0 && (!gr->dws_gate || !gr->dws_value || !gr->dws_out)))
+    return fail(LMOE_EINVAL, "a gradient pointer is NULL");
+  const BPlan pl = bplan(sh);
+  if (ws_bytes < pl.total) return fail(LMOE_EWORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, pl.total);
+  if (!ws) return fail(LMOE_EINVAL, "ws is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(LMOE_EINVAL, "ws must be 256-byte aligned");
+  if (sh->T > 0 && (!x || !dy)) return fail(LMOE_EINVAL, "x and dy are required");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int T = (int)sh->T, H = sh->H, L = sh->L, E = sh->E, k = sh->k, I = sh->I, S = sh->S, Is = sh->Is;
+  const int tk = T * k, sis = S * Is;
+  float* logits = at<float>(ws, pl.logits);
+  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, pl.idx);
+  float* tw = at<float>(ws, pl.w);
+  int32_t* offsets = at<int32_t>(ws, pl.offsets);
+  int32_t* sorted = at<int32_t>(ws, pl.sorted);
+  int32_t* pos = at<int32_t>(ws, pl.pos);
+  int4* tiles = at<int4>(ws, pl.tiles);
+  int32_t* tc = at<int32_t>(ws, pl.tcount);
+  float *G = at<float>(ws, pl.G), *V = at<float>(ws, pl.V), *A = at<float>(ws, pl.A), *dA = at<float>(ws, pl.dA);
+  float *O = at<float>(ws, pl.O), *dO = at<float>(ws, pl.dO);
+  float *c = at<float>(ws, pl.c), *n = at<float>(ws, pl.n), *dn = at<float>(ws, pl.dn), *dz = at<float>(ws, pl.dz);
+  float *r = at<float>(ws, pl.r), *dw = at<float>(ws, pl.dw), *dl = at<float>(ws, pl.dl);
+  float *gs = at<float>(ws, pl.gs), *vs = at<float>(ws, pl.vs), *hs = at<float>(ws, pl.hs), *dhs = at<float>(ws, pl.dhs);
+  const void* zsrc = w->w_down ? at<void>(ws, pl.z) : x;
+
+  // --- forward, keeping what the gradients need ---------------------------
+  if (T > 0) {
+    LMOE_HIP((bg<BG_DENSE, 0, 0, 0, 0>(bop(x, H), bop(w->w_router, H), logits, E, T, E, H, 0, st, sh)), "router");
+    if (w->w_down)
+      LMOE_HIP((bg<BG_DENSE, 0, 0, 0, 0>(bop(x, H), bop(w->w_down, H), at<void>(ws, pl.z), L, T, L, H, 0, st, sh, 1)),
+               "latent down");
+    LMOE_HIP(launch_topk(logits, w->b_router, sh->T, E, k, idx, tw, st), "top-k");
+  }
+  LMOE_HIP(launch_permute(idx, sh->T, E, k, at<int32_t>(ws, pl.bcounts), offsets, sorted, pos, st), "permute");
+  LMOE_HIP(launch_tiles(offsets, E, kBgM, tiles, tc, 0, nullptr, nullptr, st), "tile list");
+  LMOE_HIP((bg<BG_GROUP_M, 0, 0, 0, 0>(bop(zsrc, L, 0, sorted, k, 1), bop(w->w_gate, L, (int64_t)I * L), G, I, 0, I, L, 0,
+                                       st, sh, 0, 0, offsets, tiles, tc)),
+           "expert gate");
+  LMOE_HIP((bg<BG_GROUP_M, 0, 0, 0, 0>(bop(zsrc, L, 0, sorted, k, 1), bop(w->w_value, L, (int64_t)I * L), V, I, 0, I, L, 0,
+                                       st, sh, 0, 0, offsets, tiles, tc)),
+           "expert value");
+  LMOE_HIP(bw_situ(0, G, V, nullptr, A, nullptr, (int64_t)tk * I, sh, st), "SiTU-GLU");
+  LMOE_HIP((bg<BG_GROUP_M, 0, 1, 0, 0>(bop(A, I, 0, nullptr, 1, 1), bop(w->w_out, I, (int64_t)L * I), O, L, 0, L, I, 0,
+                                       st, sh, 0, 0, offsets, tiles, tc)),
+           "expert down");
+  if (T > 0)
+    hipLaunchKernelGGL(bw_combine_norm_kernel, dim3(T), dim3(256), 0, st, O, pos, tw, w->gamma, L, k, sh->rms_eps, c, n, r);
+  LMOE_HIP(hipGetLastError(), "combine + norm");
+
+  // --- up-projection ------------------------------------------------------
+  if (w->w_up) {
+    LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dy, H), bop(w->w_up, L), dn, L, T, L, H, 0, st, sh)), "dn");
+    LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 1>(bop(dy, H), bop(n, L), gr->dw_up, L, H, L, T, 0, st, sh)), "dW_up");
+  } else if (T > 0) {
+    hipLaunchKernelGGL(bw_widen_kernel, dim3((unsigned)cdiv((int64_t)T * L, 256)), dim3(256), 0, st,
+                       static_cast<const unsigned short*>(dy), dn, (int64_t)T * L);
+    LMOE_HIP(hipGetLastError(), "dn");
+  }
+  // --- RMSNorm and combine ------------------------------------------------
+  if (T > 0)
+    hipLaunchKernelGGL(bw_norm_combine_grad_kernel, dim3(T), dim3(256), 0, st, dn, c, r, w->gamma, O, pos, tw, L, k, dO,
+                       dw);
+  LMOE_HIP(hipGetLastError(), "norm / combine gradient");
+  {
+    const int64_t chunk = cdiv(std::max<int64_t>(sh->T, 1), kBwChunks);
+    const int rows = (int)cdiv(std::max<int64_t>(sh->T, 1), chunk);
+    hipLaunchKernelGGL(bw_dgamma_part_kernel, dim3((unsigned)cdiv(L, 256), rows), dim3(256), 0, st, dn, c, r, sh->T, L,
+                       chunk, at<float>(ws, pl.dgp));
+    hipLaunchKernelGGL(bw_sum_rows_kernel, dim3((unsigned)cdiv(L, 256)), dim3(256), 0, st, at<float>(ws, pl.dgp), rows,
+                       L, gr->dgamma);
+    LMOE_HIP(hipGetLastError(), "dgamma");
+  }
+  // --- routed experts -----------------------------------------------------
+  LMOE_HIP((bg<BG_GROUP_M, 0, 1, 1, 0>(bop(dO, L, 0, nullptr, 1, 1), bop(w->w_out, I, (int64_t)L * I), dA, I, 0, I, L, 0,
+                                       st, sh, 0, 0, offsets, tiles, tc)),
+           "dA");
+  LMOE_HIP((bg<BG_GROUP_K, 1, 1, 1, 1>(bop(dO, L, 0, nullptr, 1, 1), bop(A, I, 0, nullptr, 1, 1), gr->dw_out, I, L, I, 0,
+                                       0, st, sh, 0, (int64_t)L * I, offsets)),
+           "dW_out");
+  LMOE_HIP(bw_situ(1, G, V, dA, G, V, (int64_t)tk * I, sh, st), "SiTU-GLU gradient");  // G, V now hold dG, dV
+  float* zr = O;  // O is no longer needed: latent gradient rows per assignment
+  LMOE_HIP((bg<BG_GROUP_M, 0, 1, 1, 0>(bop(G, I, 0, nullptr, 1, 1), bop(w->w_gate, L, (int64_t)I * L), zr, L, 0, L, I, 0,
+                                       st, sh, 0, 0, offsets, tiles, tc)),
+           "dz rows (gate)");
+  LMOE_HIP((bg<BG_GROUP_M, 0, 1, 1, 0>(bop(V, I, 0, nullptr, 1, 1), bop(w->w_value, L, (int64_t)I * L), zr, L, 0, L, I, 1,
+                                       st, sh, 0, 0, offsets, tiles, tc)),
+           "dz rows (value)");
+  LMOE_HIP((bg<BG_GROUP_K, 1, 1, 1, 0>(bop(G, I, 0, nullptr, 1, 1), bop(zsrc, L, 0, sorted, k, 1), gr->dw_gate, L, I, L,
+                                       0, 0, st, sh, 0, (int64_t)I * L, offsets)),
+           "dW_gate");
+  LMOE_HIP((bg<BG_GROUP_K, 1, 1, 1, 0>(bop(V, I, 0, nullptr, 1, 1), bop(zsrc, L, 0, sorted, k, 1), gr->dw_value, L, I, L,
+                                       0, 0, st, sh, 0, (int64_t)I * L, offsets)),
+           "dW_value");
+  // --- latent projection and dx --------------------------------------------
+  if (T > 0) {
+    hipLaunchKernelGGL(bw_gather_sum_kernel, dim3((unsigned)cdiv(L, 256), T), dim3(256), 0, st, zr, pos, L, k,
+                       w->w_down ? dz : gr->dx, 0);
+    LMOE_HIP(hipGetLastError(), "dz");
+  }
+  if (w->w_down) {
+    LMOE_HIP((bg<BG_DENSE, 0, 1, 1, 0>(bop(dz, L), bop(w->w_down, H), gr->dx, H, T, H, L, 0, st, sh)), "dx (latent)");
+    LMOE_HIP((bg<BG_DENSE, 1, 1, 1, 0>(bop(dz, L), bop(x, H), gr->dw_down, H, L, H, T, 0, st, sh)), "dW_down");
+  }
+  // --- router ---------------------------------------------------------------
+  if (T > 0) {
+    hipLaunchKernelGGL(bw_route_grad_kernel, dim3(T), dim3(256), 0, st, logits, idx, dw, E, k, dl);
+    LMOE_HIP(hipGetLastError(), "router gradient");
+  }
+  LMOE_HIP((bg<BG_DENSE, 0, 1, 1, 0>(bop(dl, E), bop(w->w_router, H), gr->dx, H, T, H, E, 1, st, sh)), "dx (router)");
+  LMOE_HIP((bg<BG_DENSE, 1, 1, 1, 0>(bop(dl, E), bop(x, H), gr->dw_router, H, E, H, T, 0, st, sh)), "dW_router");
+  // --- shared experts ---------------------------------------------------------
+  if (S > 0) {
+    LMOE_HIP((bg<BG_DENSE, 0, 0, 0, 0>(bop(x, H), bop(w->ws_gate, H), gs, sis, T, sis, H, 0, st, sh)), "shared gate");
+    LMOE_HIP((bg<BG_DENSE, 0, 0, 0, 0>(bop(x, H), bop(w->ws_value, H), vs, sis, T, sis, H, 0, st, sh)), "shared value");
+    LMOE_HIP(bw_situ(0, gs, vs, nullptr, hs, nullptr, (int64_t)T * sis, sh, st), "shared SiTU-GLU");
+    for (int s = 0; s < S; ++s) {
+      const char* wso = static_cast<const char*>(w->ws_out) + (size_t)s * H * Is * 2;
+      LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dy, H), bop(wso, Is), dhs + (size_t)s * Is, sis, T, Is, H, 0, st, sh)),
+               "shared dh");
+      LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 1>(bop(dy, H), bop(hs + (size_t)s * Is, sis), gr->dws_out + (size_t)s * H * Is, Is,
+                                         H, Is, T, 0, st, sh)),
+               "dWs_out");
+    }
+    LMOE_HIP(bw_situ(1, gs, vs, dhs, gs, vs, (int64_t)T * sis, sh, st), "shared SiTU-GLU gradient");
+    LMOE_HIP((bg<BG_DENSE, 0, 1, 1, 0>(bop(gs, sis), bop(w->ws_gate, H), gr->dx, H, T, H, sis, 1, st, sh)),
+             "dx (shared gate)");
+    LMOE_HIP((bg<BG_DENSE, 0, 1, 1, 0>(bop(vs, sis), bop(w->ws_value, H), gr->dx, H, T, H, sis, 1, st, sh)),
+             "dx (shared value)");
+    LMOE_HIP((bg<BG_DENSE, 1, 1, 1, 0>(bop(gs, sis), bop(x, H), gr->dws_gate, H, sis, H, T, 0, st, sh)), "dWs_gate");
+    LMOE_HIP((bg<BG_DENSE, 1, 1, 1, 0>(bop(vs, sis), bop(x, H), gr->dws_value, H, sis, H, T, 0, st, sh)), "dWs_value");
+  }
   return LMOE_OK;
 }
 

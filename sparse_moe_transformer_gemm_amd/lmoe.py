@@ -24,7 +24,8 @@ _TORCH = {F32: torch.float32, BF16: torch.bfloat16, F8E4M3: torch.float8_e4m3fn}
 
 EXPORTS = ("lmoe_validate", "lmoe_workspace_bytes", "lmoe_forward", "lmoe_route", "lmoe_permute",
            "lmoe_expert_gemm", "lmoe_combine_norm", "lmoe_up", "lmoe_router_logits", "lmoe_quantile_bias",
-           "lmoe_packed_bytes", "lmoe_pack_experts", "lmoe_quantize_1x128",
+           "lmoe_packed_bytes", "lmoe_pack_experts", "lmoe_quantize_1x128", "lmoe_backward",
+           "lmoe_backward_workspace_bytes",
            "lmoe_status_str", "lmoe_last_error")
 
 
@@ -47,6 +48,14 @@ _WEIGHT_FIELDS = ("w_router", "b_router", "w_down", "w_gate", "w_value", "w_out"
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _WEIGHT_FIELDS]
+
+
+GRAD_FIELDS = ("dx", "dw_router", "dw_down", "dw_gate", "dw_value", "dw_out", "dgamma", "dw_up", "dws_gate",
+               "dws_value", "dws_out")
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_FIELDS]
 
 
 _lib = None
@@ -77,6 +86,8 @@ def load_library(path: str = LIB_PATH):
         "lmoe_packed_bytes": (sz, [sp]),
         "lmoe_pack_experts": (ctypes.c_int, [sp, wp, vp, sz, vp]),
         "lmoe_quantize_1x128": (ctypes.c_int, [vp, ctypes.c_int64, ctypes.c_int32, vp, f32p, vp]),
+        "lmoe_backward_workspace_bytes": (sz, [sp]),
+        "lmoe_backward": (ctypes.c_int, [sp, wp, vp, vp, i32p, ctypes.POINTER(Grads), vp, sz, vp]),
         "lmoe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "lmoe_last_error": (ctypes.c_char_p, []),
     }
@@ -174,6 +185,43 @@ def quantize_1x128(x, q=None, scales=None, stream=None):
                                    _ptr(q, torch.float8_e4m3fn, "q"), _ptr(scales, torch.float32, "scales"),
                                    _stream(stream)))
     return q, scales
+
+
+def backward_workspace_bytes(sh: Shape) -> int:
+    load_library()
+    return int(_lib.lmoe_backward_workspace_bytes(ctypes.byref(sh)))
+
+
+def grad_shapes(sh: Shape, w: Weights) -> dict:
+    """Shapes of the fp32 gradients lmoe_backward writes for this layer."""
+    T, H, L, E, I, S, Is = sh.T, sh.H, sh.L, sh.E, sh.I, sh.S, sh.Is
+    out = {"dx": (T, H), "dw_router": (E, H), "dw_gate": (E, I, L), "dw_value": (E, I, L), "dw_out": (E, L, I),
+           "dgamma": (L,)}
+    if w.w_down:
+        out["dw_down"] = (L, H)
+    if w.w_up:
+        out["dw_up"] = (H, L)
+    if S > 0:
+        out.update(dws_gate=(S, Is, H), dws_value=(S, Is, H), dws_out=(S, H, Is))
+    return out
+
+
+def backward(sh: Shape, w: Weights, x, dy, grads=None, ws=None, stream=None):
+    """Gradients of sum(y * dy) for x and every weight (fp32 device tensors,
+    allocated when `grads` is None) and the selection the recomputed forward
+    took; see lmoe_backward in include/lmoe.h.  Returns (grads dict, idx)."""
+    lib = load_library()
+    dev = x.device
+    if grads is None:
+        grads = {n: torch.empty(shp, dtype=torch.float32, device=dev) for n, shp in grad_shapes(sh, w).items()}
+    g = Grads(**{n: _ptr(grads.get(n), torch.float32, n) for n in GRAD_FIELDS})
+    idx = torch.empty((sh.T, sh.k), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(backward_workspace_bytes(sh), 256), dtype=torch.uint8, device=dev)
+    _check(lib.lmoe_backward(ctypes.byref(sh), ctypes.byref(w), _ptr(x, _TORCH[sh.act], "x"),
+                             _ptr(dy, _TORCH[sh.act], "dy"), _ptr(idx, torch.int32, "topk_idx"), ctypes.byref(g),
+                             _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+    return grads, idx
 
 
 def packed_bytes(sh: Shape) -> int:

@@ -260,3 +260,28 @@ def test_quantize_1x128_rejects_before_any_gpu_call(lib):
     assert q(buf, 4, 128, buf, None, None) == 1
     assert q(ctypes.c_void_p(0x100008), 4, 128, buf, buf, None) == 1  # x not 16-byte aligned
     assert "aligned" in lmoe.last_error()
+
+
+def test_backward_rejects_before_any_gpu_call(lib):
+    sh = k3(T=64)
+    w = fake_weights(sh)
+    need = lmoe.backward_workspace_bytes(sh)
+    assert need > 0 and lmoe.backward_workspace_bytes(k3(T=8192)) > need
+    buf = ctypes.c_void_p(0x100000)
+    g = lmoe.Grads(**{n: 0x2000 + 0x100 * i for i, n in enumerate(lmoe.GRAD_FIELDS)})
+    ws = ctypes.c_void_p(0x200000)
+    bw = lib.lmoe_backward
+    assert bw(ctypes.byref(sh), ctypes.byref(w), buf, buf, None, ctypes.byref(g), ws, need - 1, None) == 3
+    assert bw(ctypes.byref(sh), ctypes.byref(w), buf, buf, None, None, ws, need, None) == 1
+    g2 = lmoe.Grads(**{n: 0x2000 + 0x100 * i for i, n in enumerate(lmoe.GRAD_FIELDS)})
+    g2.dw_out = None
+    assert bw(ctypes.byref(sh), ctypes.byref(w), buf, buf, None, ctypes.byref(g2), ws, need, None) == 1
+    assert bw(ctypes.byref(sh), ctypes.byref(w), None, buf, None, ctypes.byref(g), ws, need, None) == 1
+    f8 = k3(T=64, w_expert="f8")
+    assert bw(ctypes.byref(f8), ctypes.byref(fake_weights(f8)), buf, buf, None, ctypes.byref(g), ws, 1 << 40,
+              None) == 2
+    big = k3(T=70000)
+    assert bw(ctypes.byref(big), ctypes.byref(fake_weights(big)), buf, buf, None, ctypes.byref(g), ws, 1 << 45,
+              None) == 2
+    packed_only = fake_weights(sh, w_gate=None, w_value=None, w_out=None, packed=0x9000)
+    assert bw(ctypes.byref(sh), ctypes.byref(packed_only), buf, buf, None, ctypes.byref(g), ws, need, None) == 1
