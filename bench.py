@@ -60,6 +60,9 @@ def parse():
                     help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs of the layer and of the copy "
                          "calibration into profiles/traffic_<workload>.json, then exit")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--backward", action="store_true",
+                    help="time lmoe_backward (forward recompute + every gradient) instead of the forward; "
+                         "prints its own JSON line")
     return ap.parse_args()
 
 
@@ -167,6 +170,9 @@ def main():
         return
     lmoe.load_library()
     dev = torch.device("cuda:0")
+    if a.backward:
+        bench_backward(a, lmoe, dev)
+        return
     cfg = get_config(a.workload)
     print(f"# generating {cfg.name} inputs on the device", file=sys.stderr, flush=True)
     g = make_inputs(cfg, device=dev)
@@ -271,6 +277,139 @@ def main():
         out["cpu_baseline"], out["parity"] = cpu_baseline(cfg, g, idx, y, a.cpu_sample, dev)
 
     print(json.dumps(out), flush=True)
+
+
+def bench_backward(a, lmoe, dev):
+    """One step = one lmoe_backward call: the forward recomputed from x, then
+    the fp32 gradients of sum(y * dy) for x and every weight."""
+    import numpy as np
+    import torch
+
+    from synth import get_config, make_inputs
+
+    cfg = get_config(a.workload)
+    print(f"# generating {cfg.name} inputs on the device", file=sys.stderr, flush=True)
+    g = make_inputs(cfg, device=dev)
+    sh = lmoe.shape_of(cfg)
+    w = lmoe.make_weights(sh, g)
+    x = g["x"]
+    T = cfg.T
+    gen = torch.Generator(device=dev).manual_seed(77)
+    dy = torch.randn((T, cfg.H), generator=gen, device=dev).to(torch.bfloat16)
+    grads = {n: torch.empty(shp, dtype=torch.float32, device=dev) for n, shp in lmoe.grad_shapes(sh, w).items()}
+    ws = torch.empty(lmoe.backward_workspace_bytes(sh), dtype=torch.uint8, device=dev)
+    for _ in range(a.warmup):
+        _, idx = lmoe.backward(sh, w, x, dy, grads=grads, ws=ws)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    print(f"# timing {a.steps} backward steps after {a.warmup} warm-up", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(a.steps):
+        lmoe.backward(sh, w, x, dy, grads=grads, ws=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / a.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(lmoe.BWD_STAGES) + 1)] for _ in range(a.steps)]
+    for i in range(a.steps):
+        _, idx = lmoe.backward(sh, w, x, dy, grads=grads, ws=ws, events=evs[i])
+    torch.cuda.synchronize()
+    stages = {n: sum(e[s].elapsed_time(e[s + 1]) for e in evs) / a.steps for s, n in enumerate(lmoe.BWD_STAGES)}
+    fl = lmoe.backward_flops(sh, projections=not cfg.identity_proj, up=not cfg.identity_proj)
+    total = sum(fl.values())
+    tflops = total / (ms * 1e-3) / 1e12
+    ex_tf = fl["expert_grads"] / (stages["expert_grads"] * 1e-3) / 1e12
+    out = {
+        "metric": "latent-MoE layer backward tokens/s (forward recompute + fp32 gradients of x and every weight)",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations and dy, N(0,0.02) weights, K3 layer shape)",
+        "config": {"workload": cfg.name, "T": T, "H": cfg.H, "L": cfg.L, "E": cfg.E, "k": cfg.k, "I": cfg.I,
+                   "S": cfg.S, "Is": cfg.Is, "act": cfg.act, "w_expert": cfg.w_expert, "gradients": "fp32",
+                   "parallelism": "single GPU"},
+        "tflops": round(tflops, 2),
+        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "stage_gflop": {k: round(v / 1e9, 1) for k, v in fl.items()},
+        "roofline": {
+            "kernel": "routed expert gradient GEMMs (grouped dgrad + wgrad)",
+            "bound": "mfma",
+            "achieved": round(ex_tf, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(ex_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": fl["expert_grads"],
+            "avg_ms": round(stages["expert_grads"], 4),
+        },
+    }
+    if a.cpu_sample > 0:
+        out["cpu_baseline"], out["parity"] = cpu_baseline_backward(cfg, g, dy, idx, grads["dx"], a.cpu_sample, dev)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_backward(cfg, g, dy, idx, dx, n, dev):
+    """The oracle's backward on a seeded sample of the batch's tokens: its dx
+    rows are exact for those tokens (each token's dx depends on that token
+    alone), so they double as a parity check of the GPU's dx."""
+    import numpy as np
+    import torch
+
+    from oracle import lmoe_oracle as O
+    from synth import raw_numpy
+
+    cores = len(os.sched_getaffinity(0))
+    rows = np.sort(np.random.default_rng(54321).choice(cfg.T, size=min(n, cfg.T), replace=False))
+    rt = torch.as_tensor(rows, device=dev)
+    forced = idx[rt].cpu().numpy().astype(np.int64)
+    touched = sorted(set(forced.ravel().tolist()))
+
+    class Sparse:
+        """Expert stack on the host: the sample's experts, zeros elsewhere
+        (the sample's gradients never read the others)."""
+
+        def __init__(self, t):
+            self.t = t
+            self.cache = {e: raw_numpy(t[e]) for e in touched}
+
+        def __len__(self):
+            return self.t.shape[0]
+
+        def __getitem__(self, e):
+            e = int(e)
+            if e not in self.cache:
+                self.cache[e] = raw_numpy(self.t[e])
+            return self.cache[e]
+
+    inp = {}
+    for k, v in g.items():
+        if v is None:
+            inp[k] = None
+        elif k in ("w_gate", "w_value", "w_out"):
+            inp[k] = Sparse(v)
+        elif k == "x":
+            inp[k] = raw_numpy(v[rt])
+        else:
+            inp[k] = raw_numpy(v)
+    dy64 = O.bf16_bits_to_f64(raw_numpy(dy[rt]))
+    spec = dict(act=cfg.act, w_expert=cfg.w_expert, k=cfg.k, cap=cfg.cap, eps=cfg.eps)
+    print(f"# oracle backward: {len(rows)} tokens on {cores} host cores", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    ref = O.backward(inp, spec, dy64, forced_idx=forced, forced_tol=1e-5)
+    dt = time.perf_counter() - t0
+    got = dx[rt].double().cpu().numpy()
+    err = float((np.abs(got - ref["dx"]).max(1) / np.abs(ref["dx"]).max(1)).max())
+    base = {"value": round(len(rows) / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} seeded tokens of the {cfg.T}-token batch, backward (with its forward) in fp64 "
+                      f"numpy, {dt:.1f} s", "seconds": round(dt, 2)}
+    return base, {"rows": len(rows), "dx_max_row_rel_err": err, "tol": 2e-2, "ok": err <= 2e-2}
 
 
 def cpu_baseline(cfg, g, idx, y, n, dev):

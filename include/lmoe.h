@@ -266,6 +266,10 @@ lmoe_status lmoe_quantize_1x128(const void *x, int64_t R, int32_t C, void *q, fl
  *   dw_up [H, L] (not written when w_up is NULL); dws_gate, dws_value
  *   [S, Is, H], dws_out [S, H, Is] (not written when S == 0).
  * dy [T, H] is BF16.  topk_idx [T, k] receives the selection if not NULL.
+ * stage_events: NULL, or LMOE_NUM_BWD_STAGES + 1 hipEvent_t recorded on
+ * `stream` before the first stage and after each: forward recompute, up and
+ * norm/combine gradients, routed expert gradients, latent and router
+ * gradients, shared expert gradients.
  * The workspace holds lmoe_backward_workspace_bytes(shape) bytes (256-byte
  * aligned).  T <= 65535.  EUNSUPPORTED for other dtypes, for a8 and for larger
  * T; EINVAL for a missing
@@ -279,9 +283,11 @@ typedef struct {
   float *dw_up;
   float *dws_gate, *dws_value, *dws_out;
 } lmoe_grads;
+#define LMOE_NUM_BWD_STAGES 5
 size_t lmoe_backward_workspace_bytes(const lmoe_shape *shape);
 lmoe_status lmoe_backward(const lmoe_shape *shape, const lmoe_weights *w, const void *x, const void *dy,
-                          int32_t *topk_idx, const lmoe_grads *grads, void *ws, size_t ws_bytes, void *stream);
+                          int32_t *topk_idx, const lmoe_grads *grads, void *ws, size_t ws_bytes, void *stream,
+                          void *const *stage_events);
 
 /* Name of a status code; message of the calling thread's last failure.       */
 const char *lmoe_status_str(lmoe_status s);

@@ -864,7 +864,8 @@ size_t lmoe_backward_workspace_bytes(const lmoe_shape* sh) {
 }
 
 lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const void* x, const void* dy,
-                          int32_t* topk_idx, const lmoe_grads* gr, void* ws, size_t ws_bytes, void* stream) {
+                          int32_t* topk_idx, const lmoe_grads* gr, void* ws, size_t ws_bytes, void* stream,
+                          void* const* ev) {
   g_err[0] = 0;
   if (lmoe_status s = check_shape(sh)) return s;
   if (!(sh->act == LMOE_BF16 && sh->w_expert == LMOE_BF16) || sh->a8)
@@ -901,6 +902,7 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   const void* zsrc = w->w_down ? at<void>(ws, pl.z) : x;
 
   // --- forward, keeping what the gradients need ---------------------------
+  if (lmoe_status s = record(ev, 0, st)) return s;
   if (T > 0) {
     LMOE_HIP((bg<BG_DENSE, 0, 0, 0, 0>(bop(x, H), bop(w->w_router, H), logits, E, T, E, H, 0, st, sh)), "router");
     if (w->w_down)
@@ -924,6 +926,7 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
     hipLaunchKernelGGL(bw_combine_norm_kernel, dim3(T), dim3(256), 0, st, O, pos, tw, w->gamma, L, k, sh->rms_eps, c, n, r);
   LMOE_HIP(hipGetLastError(), "combine + norm");
 
+  if (lmoe_status s = record(ev, 1, st)) return s;
   // --- up-projection ------------------------------------------------------
   if (w->w_up) {
     LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dy, H), bop(w->w_up, L), dn, L, T, L, H, 0, st, sh)), "dn");
@@ -947,6 +950,7 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
                        L, gr->dgamma);
     LMOE_HIP(hipGetLastError(), "dgamma");
   }
+  if (lmoe_status s = record(ev, 2, st)) return s;
   // --- routed experts -----------------------------------------------------
   LMOE_HIP((bg<BG_GROUP_M, 0, 1, 1, 0>(bop(dO, L, 0, nullptr, 1, 1), bop(w->w_out, I, (int64_t)L * I), dA, I, 0, I, L, 0,
                                        st, sh, 0, 0, offsets, tiles, tc)),
@@ -968,6 +972,7 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   LMOE_HIP((bg<BG_GROUP_K, 1, 1, 1, 0>(bop(V, I, 0, nullptr, 1, 1), bop(zsrc, L, 0, sorted, k, 1), gr->dw_value, L, I, L,
                                        0, 0, st, sh, 0, (int64_t)I * L, offsets)),
            "dW_value");
+  if (lmoe_status s = record(ev, 3, st)) return s;
   // --- latent projection and dx --------------------------------------------
   if (T > 0) {
     hipLaunchKernelGGL(bw_gather_sum_kernel, dim3((unsigned)cdiv(L, 256), T), dim3(256), 0, st, zr, pos, L, k,
@@ -985,6 +990,7 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   }
   LMOE_HIP((bg<BG_DENSE, 0, 1, 1, 0>(bop(dl, E), bop(w->w_router, H), gr->dx, H, T, H, E, 1, st, sh)), "dx (router)");
   LMOE_HIP((bg<BG_DENSE, 1, 1, 1, 0>(bop(dl, E), bop(x, H), gr->dw_router, H, E, H, T, 0, st, sh)), "dW_router");
+  if (lmoe_status s = record(ev, 4, st)) return s;
   // --- shared experts ---------------------------------------------------------
   if (S > 0) {
     LMOE_HIP((bg<BG_DENSE, 0, 0, 0, 0>(bop(x, H), bop(w->ws_gate, H), gs, sis, T, sis, H, 0, st, sh)), "shared gate");
@@ -1006,6 +1012,7 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
     LMOE_HIP((bg<BG_DENSE, 1, 1, 1, 0>(bop(gs, sis), bop(x, H), gr->dws_gate, H, sis, H, T, 0, st, sh)), "dWs_gate");
     LMOE_HIP((bg<BG_DENSE, 1, 1, 1, 0>(bop(vs, sis), bop(x, H), gr->dws_value, H, sis, H, T, 0, st, sh)), "dWs_value");
   }
+  if (lmoe_status s = record(ev, 5, st)) return s;
   return LMOE_OK;
 }
 

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmoe.so"
 F32, BF16, F8E4M3 = 0, 1, 2
 NUM_STAGES = 7
 STAGES = ("route_gemm", "topk", "permute", "expert_gate_value", "expert_down", "combine_norm", "up")
+BWD_STAGES = ("forward_recompute", "up_norm_grads", "expert_grads", "latent_router_grads", "shared_grads")
 STATUS = {0: "LMOE_OK", 1: "LMOE_EINVAL", 2: "LMOE_EUNSUPPORTED", 3: "LMOE_EWORKSPACE", 4: "LMOE_EHIP"}
 DTYPE_CODE = {"f32": F32, "bf16": BF16, "f8": F8E4M3}
 _TORCH = {F32: torch.float32, BF16: torch.bfloat16, F8E4M3: torch.float8_e4m3fn}
@@ -87,7 +88,7 @@ def load_library(path: str = LIB_PATH):
         "lmoe_pack_experts": (ctypes.c_int, [sp, wp, vp, sz, vp]),
         "lmoe_quantize_1x128": (ctypes.c_int, [vp, ctypes.c_int64, ctypes.c_int32, vp, f32p, vp]),
         "lmoe_backward_workspace_bytes": (sz, [sp]),
-        "lmoe_backward": (ctypes.c_int, [sp, wp, vp, vp, i32p, ctypes.POINTER(Grads), vp, sz, vp]),
+        "lmoe_backward": (ctypes.c_int, [sp, wp, vp, vp, i32p, ctypes.POINTER(Grads), vp, sz, vp, vp]),
         "lmoe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "lmoe_last_error": (ctypes.c_char_p, []),
     }
@@ -206,10 +207,12 @@ def grad_shapes(sh: Shape, w: Weights) -> dict:
     return out
 
 
-def backward(sh: Shape, w: Weights, x, dy, grads=None, ws=None, stream=None):
+def backward(sh: Shape, w: Weights, x, dy, grads=None, ws=None, stream=None, events=None):
     """Gradients of sum(y * dy) for x and every weight (fp32 device tensors,
     allocated when `grads` is None) and the selection the recomputed forward
-    took; see lmoe_backward in include/lmoe.h.  Returns (grads dict, idx)."""
+    took; see lmoe_backward in include/lmoe.h.  Returns (grads dict, idx).
+    events: optional list of len(BWD_STAGES) + 1 torch.cuda.Event recorded
+    around the stages."""
     lib = load_library()
     dev = x.device
     if grads is None:
@@ -218,9 +221,17 @@ def backward(sh: Shape, w: Weights, x, dy, grads=None, ws=None, stream=None):
     idx = torch.empty((sh.T, sh.k), dtype=torch.int32, device=dev)
     if ws is None:
         ws = torch.empty(max(backward_workspace_bytes(sh), 256), dtype=torch.uint8, device=dev)
+    ev = None
+    if events is not None:
+        if len(events) != len(BWD_STAGES) + 1:
+            raise ValueError(f"events must hold {len(BWD_STAGES) + 1} torch.cuda.Event objects")
+        for e in events:
+            if not e.cuda_event:
+                e.record()  # creates the underlying event
+        ev = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
     _check(lib.lmoe_backward(ctypes.byref(sh), ctypes.byref(w), _ptr(x, _TORCH[sh.act], "x"),
                              _ptr(dy, _TORCH[sh.act], "dy"), _ptr(idx, torch.int32, "topk_idx"), ctypes.byref(g),
-                             _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+                             _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream), ev))
     return grads, idx
 
 
@@ -387,6 +398,25 @@ def layer_flops(sh: Shape, tokens=None, projections=True) -> float:
     proj = 2 * L * H if projections else 0
     per_tok = 2 * (E * H + k * 3 * L * I + S * 3 * H * Is) + 2 * proj
     return float(T) * per_tok
+
+
+def backward_flops(sh: Shape, projections=True, up=True) -> dict:
+    """Algorithmic FLOPs of one lmoe_backward call by stage (2 per
+    multiply-add): the forward recompute (router, down, expert gate/value/out),
+    dn and dW_up, the routed expert dgrads and wgrads (dA, dW_out, dz rows,
+    dW_gate, dW_value), the latent and router gradients, and the shared
+    experts (recompute, dgrads, wgrads)."""
+    T, H, L, E, k, I, S, Is = sh.T, sh.H, sh.L, sh.E, sh.k, sh.I, sh.S, sh.Is
+    p = 1 if projections else 0
+    u = 1 if up else 0
+    st = {
+        "forward_recompute": T * (2 * E * H + 2 * L * H * p + 2 * k * 3 * L * I),
+        "up_norm_grads": T * 4 * H * L * u,
+        "expert_grads": T * 12 * k * L * I,
+        "latent_router_grads": T * (4 * L * H * p + 4 * E * H),
+        "shared_grads": T * 16 * S * Is * H,
+    }
+    return {n: float(v) for n, v in st.items()}
 
 
 def expert_bytes(sh: Shape, touched: int, which="all") -> float:

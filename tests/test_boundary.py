@@ -271,17 +271,17 @@ def test_backward_rejects_before_any_gpu_call(lib):
     g = lmoe.Grads(**{n: 0x2000 + 0x100 * i for i, n in enumerate(lmoe.GRAD_FIELDS)})
     ws = ctypes.c_void_p(0x200000)
     bw = lib.lmoe_backward
-    assert bw(ctypes.byref(sh), ctypes.byref(w), buf, buf, None, ctypes.byref(g), ws, need - 1, None) == 3
-    assert bw(ctypes.byref(sh), ctypes.byref(w), buf, buf, None, None, ws, need, None) == 1
+    assert bw(ctypes.byref(sh), ctypes.byref(w), buf, buf, None, ctypes.byref(g), ws, need - 1, None, None) == 3
+    assert bw(ctypes.byref(sh), ctypes.byref(w), buf, buf, None, None, ws, need, None, None) == 1
     g2 = lmoe.Grads(**{n: 0x2000 + 0x100 * i for i, n in enumerate(lmoe.GRAD_FIELDS)})
     g2.dw_out = None
-    assert bw(ctypes.byref(sh), ctypes.byref(w), buf, buf, None, ctypes.byref(g2), ws, need, None) == 1
-    assert bw(ctypes.byref(sh), ctypes.byref(w), None, buf, None, ctypes.byref(g), ws, need, None) == 1
+    assert bw(ctypes.byref(sh), ctypes.byref(w), buf, buf, None, ctypes.byref(g2), ws, need, None, None) == 1
+    assert bw(ctypes.byref(sh), ctypes.byref(w), None, buf, None, ctypes.byref(g), ws, need, None, None) == 1
     f8 = k3(T=64, w_expert="f8")
     assert bw(ctypes.byref(f8), ctypes.byref(fake_weights(f8)), buf, buf, None, ctypes.byref(g), ws, 1 << 40,
-              None) == 2
+              None, None) == 2
     big = k3(T=70000)
     assert bw(ctypes.byref(big), ctypes.byref(fake_weights(big)), buf, buf, None, ctypes.byref(g), ws, 1 << 45,
-              None) == 2
+              None, None) == 2
     packed_only = fake_weights(sh, w_gate=None, w_value=None, w_out=None, packed=0x9000)
-    assert bw(ctypes.byref(sh), ctypes.byref(packed_only), buf, buf, None, ctypes.byref(g), ws, need, None) == 1
+    assert bw(ctypes.byref(sh), ctypes.byref(packed_only), buf, buf, None, ctypes.byref(g), ws, need, None, None) == 1

@@ -123,3 +123,50 @@ def test_comparison_layers(dev, k3w, name):
     finally:
         g.clear()
         torch.cuda.empty_cache()
+
+
+def test_k3_backward_t2048(dev, k3w):
+    """The K3 layer's backward at T = 2048: sampled dx rows against the
+    oracle (a token's dx depends on that token alone), and at full size the
+    property that the weight gradients of the batch are the sums of those of
+    its two halves (each token's selection is its own)."""
+    cfg = get_config("k3_prefill_t2048")
+    note(f"[k3 backward] {cfg.name}")
+    x = make_x(cfg, dev)
+    sh = lmoe.shape_of(cfg)
+    w = lmoe.make_weights(sh, k3w)
+    gen = torch.Generator(device=dev).manual_seed(78)
+    dy = torch.randn((cfg.T, cfg.H), generator=gen, device=dev).to(torch.bfloat16)
+    slices = {"dw_router": lambda t: t, "dw_down": lambda t: t, "dw_up": lambda t: t, "dgamma": lambda t: t,
+              "dws_gate": lambda t: t[:, :64], "dws_out": lambda t: t[:, :, :64],
+              "dw_gate": lambda t: t[:64:9], "dw_value": lambda t: t[5:200:13], "dw_out": lambda t: t[::97]}
+
+    def run(lo, hi):
+        s2 = lmoe.shape_of(cfg, T=hi - lo)
+        grads, idx = lmoe.backward(s2, w, x[lo:hi].contiguous(), dy[lo:hi].contiguous())
+        torch.cuda.synchronize()
+        out = {n: f(grads[n]).double().cpu() for n, f in slices.items()}
+        dx = grads["dx"].double().cpu()
+        del grads
+        torch.cuda.empty_cache()
+        return out, dx, idx
+
+    full, dx_full, idx = run(0, cfg.T)
+    a, dx_a, _ = run(0, cfg.T // 2)
+    b, dx_b, _ = run(cfg.T // 2, cfg.T)
+    for n in slices:
+        ref = full[n]
+        err = float((a[n] + b[n] - ref).abs().max() / ref.abs().max())
+        note(f"    {n:10s} halves vs whole: rel {err:.2e}")
+        assert err <= 1e-4, n
+    assert torch.equal(torch.cat([dx_a, dx_b]), dx_full)  # a token's dx is its own, bit for bit
+
+    rows = np.sort(np.random.default_rng(79).choice(cfg.T, size=4, replace=False))
+    rt = torch.as_tensor(rows, device=dev)
+    inp = lazy_inputs(k3w, None)
+    inp["x"] = raw_numpy(x[rt])
+    ref = O.backward(inp, spec_of(cfg), O.bf16_bits_to_f64(raw_numpy(dy[rt])),
+                     forced_idx=idx[rt].cpu().numpy().astype(np.int64), forced_tol=1e-5)
+    err = rowwise_rel_err(dx_full[torch.from_numpy(rows)].numpy(), ref["dx"])
+    note(f"    dx rows {rows.tolist()}: max row rel err {err:.3e}")
+    assert err <= 2e-2
