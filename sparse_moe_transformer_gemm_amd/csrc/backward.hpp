@@ -52,7 +52,14 @@ struct BgArgs {
   const int* tile_count;
 };
 
-constexpr int kBgM = 128, kBgN = 128, kBgK = 32, kBgPitch = 80;  // LDS row: 32 bf16 + 16 B pad
+#ifndef LMOE_BG_K
+#define LMOE_BG_K 32
+#endif
+constexpr int kBgM = 128, kBgN = 128, kBgK = LMOE_BG_K;
+constexpr int kBgPitch = kBgK * 2 + 16;       // LDS row: the k-tile in bf16 + 16 B pad
+constexpr int kBgRcPitch = (kBgM + 8) * 2;    // row-contiguous tiles: one k per LDS row, 128 rows + pad
+constexpr int kBgTileBytes = kBgM * kBgPitch > kBgK * kBgRcPitch ? kBgM * kBgPitch : kBgK * kBgRcPitch;
+constexpr int kBgVec = kBgM * kBgK / 8 / 256;  // 8-element vectors per thread per operand tile
 
 __device__ __forceinline__ unsigned short f2bf(float f) {
   const bf16 h = (bf16)f;  // round to nearest even
@@ -91,19 +98,19 @@ __device__ __forceinline__ uint4 bg_load8(const char* p, int n, bool vec) {
   }
 }
 
-// One operand tile (128 rows x 32 k) of one k-tile into registers: 512
-// vectors of 8 elements, two per thread.  rows / kv: valid rows and k.
+// One operand tile (128 rows x kBgK) of one k-tile into registers, kBgVec
+// vectors of 8 elements per thread.  rows / kv: valid rows and k.
 template <int RC, int F32>
 struct BgTile {
-  uint4 v[2];
+  uint4 v[kBgVec];
   __device__ __forceinline__ void load(const BgOp& o, const char* base, int rowbase, int r0, int rows, int k0,
                                        int kv, bool vec, int tid) {
-    constexpr int ES = F32 ? 4 : 2;
+    constexpr int ES = F32 ? 4 : 2, VPR = kBgK / 8;  // vectors per k-contiguous row
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kBgVec; ++q) {
       const int vi = tid + 256 * q;
       if (!RC) {
-        const int r = vi >> 2, kk = (vi & 3) * 8;
+        const int r = vi / VPR, kk = (vi % VPR) * 8;
         const int n = min(8, kv - kk);
         if (r < rows && n > 0) {
           int sr = r0 + r + (o.grow ? rowbase : 0);
@@ -125,25 +132,48 @@ struct BgTile {
       }
     }
   }
-  // LDS image: row r at r * kBgPitch, k contiguous
+  // LDS image.  k-contiguous operands: row r at r * kBgPitch, k contiguous.
+  // Row-contiguous operands keep their layout: k at k * kBgRcPitch, rows
+  // contiguous (the fragments are read with transposing LDS reads).
   __device__ __forceinline__ void store(char* s, int tid) const {
+    constexpr int VPR = kBgK / 8;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kBgVec; ++q) {
       const int vi = tid + 256 * q;
       if (!RC) {
-        const int r = vi >> 2, kk = (vi & 3) * 8;
+        const int r = vi / VPR, kk = (vi % VPR) * 8;
         *reinterpret_cast<uint4*>(s + r * kBgPitch + kk * 2) = v[q];
       } else {
         const int kk = vi >> 4, r8 = (vi & 15) * 8;
-        const unsigned w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<unsigned short*>(s + (r8 + i) * kBgPitch + kk * 2) =
-              (unsigned short)(w[i >> 1] >> (16 * (i & 1)));
+        *reinterpret_cast<uint4*>(s + kk * kBgRcPitch + r8 * 2) = v[q];
       }
     }
   }
 };
+
+typedef short bgv4 __attribute__((ext_vector_type(4)));
+
+// MFMA fragment of rows r0 .. r0 + 31 at k-step ks: lane l holds the 8
+// consecutive k (8 (l / 32) .. + 7 within the step) of row r0 + l % 32.
+// Row-contiguous tiles are read with ds_read_b64_tr_b16: in each 16-lane
+// group, lane i receives element i % 4 of the 4-element loads of lanes
+// 4 j + i / 4 (j = 0..3), so lane q of group G points at k-row
+// 8 (G / 2) + q / 4 and rows r0 + 16 (G % 2) + 4 (q % 4) .. + 3; a second read
+// 4 k-rows further gives the other 4 k.
+template <int RC>
+__device__ __forceinline__ bf16x8 bg_frag(const char* s, int r0, int ks, int lane) {
+  if (!RC) {
+    return *reinterpret_cast<const bf16x8*>(s + (r0 + (lane & 31)) * kBgPitch + (ks * 16 + (lane >> 5) * 8) * 2);
+  } else {
+    const int G = lane >> 4, q = lane & 15;
+    const char* p = s + (ks * 16 + 8 * (G >> 1) + (q >> 2)) * kBgRcPitch + (r0 + 16 * (G & 1) + 4 * (q & 3)) * 2;
+    typedef __attribute__((address_space(3))) bgv4 lds_v4;
+    const bgv4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p));
+    const bgv4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p + 4 * kBgRcPitch));
+    const short v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return *reinterpret_cast<const bf16x8*>(v);
+  }
+}
 
 // 16-byte loads need the row pitch and the base 16-byte aligned.
 __device__ __forceinline__ bool bg_vec_ok(const char* base, int64_t ld, int es) {
@@ -152,8 +182,8 @@ __device__ __forceinline__ bool bg_vec_ok(const char* base, int64_t ld, int es) 
 
 template <int MODE, int ARC, int AF32, int BRC, int BF32>
 __global__ __launch_bounds__(256) void bgemm_kernel(const BgArgs p) {
-  __shared__ __attribute__((aligned(16))) char sA[2][kBgM * kBgPitch];
-  __shared__ __attribute__((aligned(16))) char sB[2][kBgN * kBgPitch];
+  __shared__ __attribute__((aligned(16))) char sA[2][kBgTileBytes];
+  __shared__ __attribute__((aligned(16))) char sB[2][kBgTileBytes];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int e = 0, rowbase = 0, M = p.M, K = p.K, m0 = 0;
   const int n0 = blockIdx.x * kBgN;
@@ -203,19 +233,17 @@ __global__ __launch_bounds__(256) void bgemm_kernel(const BgArgs p) {
     tb.store(sB[0], tid);
   }
   __syncthreads();
-  const int lr = lane & 31, kh = (lane >> 5) * 8;
+  const int lr = lane & 31;
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) load(kt + 1);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < kBgK / 16; ++ks) {
       bf16x8 a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(sA[cur] + (wm + i * 32 + lr) * kBgPitch + (ks * 16 + kh) * 2);
+      for (int i = 0; i < 2; ++i) a[i] = bg_frag<ARC>(sA[cur], wm + i * 32, ks, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(sB[cur] + (wn + j * 32 + lr) * kBgPitch + (ks * 16 + kh) * 2);
+      for (int j = 0; j < 2; ++j) b[j] = bg_frag<BRC>(sB[cur], wn + j * 32, ks, lane);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
