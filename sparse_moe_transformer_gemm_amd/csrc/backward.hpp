@@ -291,10 +291,11 @@ __global__ __launch_bounds__(256) void bgemm_kernel(const BgArgs p) {
 __device__ __forceinline__ float bw_sigmoid(float u) { return 1.f / (1.f + expf(-u)); }
 
 // SiTU-GLU on flat arrays: mode 0 writes a = silu(cap g) cap v; mode 1
-// writes dg, dv of a given da (may alias g and v: each element is read
-// before it is written by the same thread).
+// writes dg, dv of a given da.  Outputs are bf16 (the next GEMM's operand
+// precision).
 __global__ __launch_bounds__(256) void bw_situ_kernel(int mode, const float* g, const float* v, const float* da,
-                                                      float* o1, float* o2, int64_t n, float cap, float inv_cap) {
+                                                      unsigned short* o1, unsigned short* o2, int64_t n, float cap,
+                                                      float inv_cap) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   const float gg = g[i], vv = v[i];
@@ -308,11 +309,11 @@ __global__ __launch_bounds__(256) void bw_situ_kernel(int mode, const float* g, 
   }
   const float sg = bw_sigmoid(cg);
   if (mode == 0) {
-    o1[i] = cg * sg * cv;
+    o1[i] = f2bf(cg * sg * cv);
   } else {
     const float d = da[i];
-    o1[i] = d * cv * sg * (1.f + cg * (1.f - sg)) * dcg;
-    o2[i] = d * cg * sg * dcv;
+    o1[i] = f2bf(d * cv * sg * (1.f + cg * (1.f - sg)) * dcg);
+    o2[i] = f2bf(d * cg * sg * dcv);
   }
 }
 
@@ -327,10 +328,10 @@ __device__ __forceinline__ float bw_block_sum(float v, float* red) {
 }
 
 // Per token: c = sum_j w_tj O[pos(t, j)] (fp32, j ascending), r = (mean c^2 +
-// eps)^-1/2, n = gamma c r.  Writes c, n and r.
+// eps)^-1/2, n = gamma c r.  Writes c (fp32), n (bf16) and r.
 __global__ __launch_bounds__(256) void bw_combine_norm_kernel(const float* O, const int32_t* pos, const float* w,
                                                               const float* gamma, int L, int k, float eps, float* c,
-                                                              float* n, float* r) {
+                                                              unsigned short* n, float* r) {
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
   float ss = 0.f;
@@ -341,17 +342,17 @@ __global__ __launch_bounds__(256) void bw_combine_norm_kernel(const float* O, co
     ss += acc * acc;
   }
   const float rr = 1.f / sqrtf(bw_block_sum(ss, red) / L + eps);
-  for (int l = threadIdx.x; l < L; l += 256) n[t * L + l] = gamma[l] * c[t * L + l] * rr;
+  for (int l = threadIdx.x; l < L; l += 256) n[t * L + l] = f2bf(gamma[l] * c[t * L + l] * rr);
   if (threadIdx.x == 0) r[t] = rr;
 }
 
 // Per token: dc = r u - r^3 c (u . c) / L with u = gamma dn; then for each
-// slot j, dO[pos(t, j)] = w_tj dc and dw_tj = dc . O[pos(t, j)].  dc is
-// recomputed per element and slot rather than stored.
+// slot j, dO[pos(t, j)] = w_tj dc (bf16) and dw_tj = dc . O[pos(t, j)] (fp32
+// dc).  dc is recomputed per element and slot rather than stored.
 __global__ __launch_bounds__(256) void bw_norm_combine_grad_kernel(const float* dn, const float* c, const float* r,
                                                                    const float* gamma, const float* O,
                                                                    const int32_t* pos, const float* w, int L, int k,
-                                                                   float* dO, float* dw) {
+                                                                   unsigned short* dO, float* dw) {
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
   const float rr = r[t];
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(256) void bw_norm_combine_grad_kernel(const float* 
     float dot = 0.f;
     for (int l = threadIdx.x; l < L; l += 256) {
       const float dc = rr * gamma[l] * dn[t * L + l] - coef * c[t * L + l];
-      dO[a * L + l] = wj * dc;
+      dO[a * L + l] = f2bf(wj * dc);
       dot += dc * O[a * L + l];
     }
     const float s = bw_block_sum(dot, red);
@@ -412,16 +413,17 @@ __global__ __launch_bounds__(256) void bw_route_grad_kernel(const float* logits,
   }
 }
 
-// dz_t = sum_j dzrows[pos(t, j)] (j ascending); written, or added to out.
+// dz_t = sum_j dzrows[pos(t, j)] (j ascending, fp32); written as fp32 to
+// out32, or as bf16 to out16 (the next GEMM's operand).
 __global__ __launch_bounds__(256) void bw_gather_sum_kernel(const float* rows, const int32_t* pos, int L, int k,
-                                                            float* out, int accumulate) {
+                                                            float* out32, unsigned short* out16) {
   const int64_t t = blockIdx.y;
   const int l = blockIdx.x * 256 + threadIdx.x;
   if (l >= L) return;
   float s = 0.f;
   for (int j = 0; j < k; ++j) s += rows[(int64_t)pos[t * k + j] * L + l];
-  if (accumulate) s += out[t * L + l];
-  out[t * L + l] = s;
+  if (out16) out16[t * L + l] = f2bf(s);
+  else out32[t * L + l] = s;
 }
 
 // bf16 -> fp32 of n elements.

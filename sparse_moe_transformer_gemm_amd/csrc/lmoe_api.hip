@@ -557,7 +557,7 @@ constexpr int kBwChunks = 64;  // token chunks of the dgamma reduction
 
 struct BPlan {
   size_t logits, z, idx, w, bcounts, offsets, sorted, pos, tiles, tcount;
-  size_t G, V, A, dA, O, dO, c, n, dn, dz, r, dw, dl, gs, vs, hs, dhs, dgp, total;
+  size_t G, V, A, dA, dG, dV, O, dO, c, n, dn, dz, r, dw, dl, gs, vs, hs, dhs, dgs, dvs, dgp, total;
 };
 
 BPlan bplan(const lmoe_shape* sh) {
@@ -580,23 +580,28 @@ BPlan bplan(const lmoe_shape* sh) {
   p.pos = take(tk * 4);
   p.tiles = take((size_t)max_tiles(sh, kBgM) * 16);
   p.tcount = take(8);
+  // fp32: GEMM outputs and what elementwise gradients read; bf16: GEMM inputs
   p.G = take(tk * sh->I * 4);
   p.V = take(tk * sh->I * 4);
-  p.A = take(tk * sh->I * 4);
+  p.A = take(tk * sh->I * 2);
   p.dA = take(tk * sh->I * 4);
+  p.dG = take(tk * sh->I * 2);
+  p.dV = take(tk * sh->I * 2);
   p.O = take(tk * sh->L * 4);
-  p.dO = take(tk * sh->L * 4);
+  p.dO = take(tk * sh->L * 2);
   p.c = take(T * sh->L * 4);
-  p.n = take(T * sh->L * 4);
+  p.n = take(T * sh->L * 2);
   p.dn = take(T * sh->L * 4);
-  p.dz = take(T * sh->L * 4);
+  p.dz = take(T * sh->L * 2);
   p.r = take(T * 4);
   p.dw = take(tk * 4);
   p.dl = take(T * sh->E * 4);
   p.gs = take(T * sis * 4);
   p.vs = take(T * sis * 4);
-  p.hs = take(T * sis * 4);
+  p.hs = take(T * sis * 2);
   p.dhs = take(T * sis * 4);
+  p.dgs = take(T * sis * 2);
+  p.dvs = take(T * sis * 2);
   p.dgp = take((size_t)kBwChunks * sh->L * 4);
   p.total = off;
   return p;
@@ -623,12 +628,12 @@ hipError_t bg(BgOp a, BgOp b, void* c, int64_t ldc, int M, int N, int K, int acc
   return hipGetLastError();
 }
 
-hipError_t bw_situ(int mode, float* g, float* v, const float* da, float* o1, float* o2, int64_t n, const lmoe_shape* sh,
-                   hipStream_t st) {
+hipError_t bw_situ(int mode, const float* g, const float* v, const float* da, void* o1, void* o2, int64_t n,
+                   const lmoe_shape* sh, hipStream_t st) {
   if (n == 0) return hipSuccess;
   const float inv = isinf(sh->cap) ? 0.f : 1.f / sh->cap;
-  hipLaunchKernelGGL(bw_situ_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, mode, g, v, da, o1, o2, n,
-                     sh->cap, inv);
+  hipLaunchKernelGGL(bw_situ_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, mode, g, v, da,
+                     static_cast<unsigned short*>(o1), static_cast<unsigned short*>(o2), n, sh->cap, inv);
   return hipGetLastError();
 }
 
@@ -894,11 +899,12 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   int32_t* pos = at<int32_t>(ws, pl.pos);
   int4* tiles = at<int4>(ws, pl.tiles);
   int32_t* tc = at<int32_t>(ws, pl.tcount);
-  float *G = at<float>(ws, pl.G), *V = at<float>(ws, pl.V), *A = at<float>(ws, pl.A), *dA = at<float>(ws, pl.dA);
-  float *O = at<float>(ws, pl.O), *dO = at<float>(ws, pl.dO);
-  float *c = at<float>(ws, pl.c), *n = at<float>(ws, pl.n), *dn = at<float>(ws, pl.dn), *dz = at<float>(ws, pl.dz);
-  float *r = at<float>(ws, pl.r), *dw = at<float>(ws, pl.dw), *dl = at<float>(ws, pl.dl);
-  float *gs = at<float>(ws, pl.gs), *vs = at<float>(ws, pl.vs), *hs = at<float>(ws, pl.hs), *dhs = at<float>(ws, pl.dhs);
+  float *G = at<float>(ws, pl.G), *V = at<float>(ws, pl.V), *dA = at<float>(ws, pl.dA), *O = at<float>(ws, pl.O);
+  float *c = at<float>(ws, pl.c), *dn = at<float>(ws, pl.dn), *r = at<float>(ws, pl.r), *dw = at<float>(ws, pl.dw);
+  float *dl = at<float>(ws, pl.dl), *gs = at<float>(ws, pl.gs), *vs = at<float>(ws, pl.vs), *dhs = at<float>(ws, pl.dhs);
+  unsigned short *A = at<unsigned short>(ws, pl.A), *dG = at<unsigned short>(ws, pl.dG), *dV = at<unsigned short>(ws, pl.dV);
+  unsigned short *dO = at<unsigned short>(ws, pl.dO), *n = at<unsigned short>(ws, pl.n), *dz = at<unsigned short>(ws, pl.dz);
+  unsigned short *hs = at<unsigned short>(ws, pl.hs), *dgs = at<unsigned short>(ws, pl.dgs), *dvs = at<unsigned short>(ws, pl.dvs);
   const void* zsrc = w->w_down ? at<void>(ws, pl.z) : x;
 
   // --- forward, keeping what the gradients need ---------------------------
@@ -919,7 +925,7 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
                                        st, sh, 0, 0, offsets, tiles, tc)),
            "expert value");
   LMOE_HIP(bw_situ(0, G, V, nullptr, A, nullptr, (int64_t)tk * I, sh, st), "SiTU-GLU");
-  LMOE_HIP((bg<BG_GROUP_M, 0, 1, 0, 0>(bop(A, I, 0, nullptr, 1, 1), bop(w->w_out, I, (int64_t)L * I), O, L, 0, L, I, 0,
+  LMOE_HIP((bg<BG_GROUP_M, 0, 0, 0, 0>(bop(A, I, 0, nullptr, 1, 1), bop(w->w_out, I, (int64_t)L * I), O, L, 0, L, I, 0,
                                        st, sh, 0, 0, offsets, tiles, tc)),
            "expert down");
   if (T > 0)
@@ -930,7 +936,7 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   // --- up-projection ------------------------------------------------------
   if (w->w_up) {
     LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dy, H), bop(w->w_up, L), dn, L, T, L, H, 0, st, sh)), "dn");
-    LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 1>(bop(dy, H), bop(n, L), gr->dw_up, L, H, L, T, 0, st, sh)), "dW_up");
+    LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dy, H), bop(n, L), gr->dw_up, L, H, L, T, 0, st, sh)), "dW_up");
   } else if (T > 0) {
     hipLaunchKernelGGL(bw_widen_kernel, dim3((unsigned)cdiv((int64_t)T * L, 256)), dim3(256), 0, st,
                        static_cast<const unsigned short*>(dy), dn, (int64_t)T * L);
@@ -952,36 +958,36 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   }
   if (lmoe_status s = record(ev, 2, st)) return s;
   // --- routed experts -----------------------------------------------------
-  LMOE_HIP((bg<BG_GROUP_M, 0, 1, 1, 0>(bop(dO, L, 0, nullptr, 1, 1), bop(w->w_out, I, (int64_t)L * I), dA, I, 0, I, L, 0,
+  LMOE_HIP((bg<BG_GROUP_M, 0, 0, 1, 0>(bop(dO, L, 0, nullptr, 1, 1), bop(w->w_out, I, (int64_t)L * I), dA, I, 0, I, L, 0,
                                        st, sh, 0, 0, offsets, tiles, tc)),
            "dA");
-  LMOE_HIP((bg<BG_GROUP_K, 1, 1, 1, 1>(bop(dO, L, 0, nullptr, 1, 1), bop(A, I, 0, nullptr, 1, 1), gr->dw_out, I, L, I, 0,
+  LMOE_HIP((bg<BG_GROUP_K, 1, 0, 1, 0>(bop(dO, L, 0, nullptr, 1, 1), bop(A, I, 0, nullptr, 1, 1), gr->dw_out, I, L, I, 0,
                                        0, st, sh, 0, (int64_t)L * I, offsets)),
            "dW_out");
-  LMOE_HIP(bw_situ(1, G, V, dA, G, V, (int64_t)tk * I, sh, st), "SiTU-GLU gradient");  // G, V now hold dG, dV
+  LMOE_HIP(bw_situ(1, G, V, dA, dG, dV, (int64_t)tk * I, sh, st), "SiTU-GLU gradient");
   float* zr = O;  // O is no longer needed: latent gradient rows per assignment
-  LMOE_HIP((bg<BG_GROUP_M, 0, 1, 1, 0>(bop(G, I, 0, nullptr, 1, 1), bop(w->w_gate, L, (int64_t)I * L), zr, L, 0, L, I, 0,
+  LMOE_HIP((bg<BG_GROUP_M, 0, 0, 1, 0>(bop(dG, I, 0, nullptr, 1, 1), bop(w->w_gate, L, (int64_t)I * L), zr, L, 0, L, I, 0,
                                        st, sh, 0, 0, offsets, tiles, tc)),
            "dz rows (gate)");
-  LMOE_HIP((bg<BG_GROUP_M, 0, 1, 1, 0>(bop(V, I, 0, nullptr, 1, 1), bop(w->w_value, L, (int64_t)I * L), zr, L, 0, L, I, 1,
+  LMOE_HIP((bg<BG_GROUP_M, 0, 0, 1, 0>(bop(dV, I, 0, nullptr, 1, 1), bop(w->w_value, L, (int64_t)I * L), zr, L, 0, L, I, 1,
                                        st, sh, 0, 0, offsets, tiles, tc)),
            "dz rows (value)");
-  LMOE_HIP((bg<BG_GROUP_K, 1, 1, 1, 0>(bop(G, I, 0, nullptr, 1, 1), bop(zsrc, L, 0, sorted, k, 1), gr->dw_gate, L, I, L,
+  LMOE_HIP((bg<BG_GROUP_K, 1, 0, 1, 0>(bop(dG, I, 0, nullptr, 1, 1), bop(zsrc, L, 0, sorted, k, 1), gr->dw_gate, L, I, L,
                                        0, 0, st, sh, 0, (int64_t)I * L, offsets)),
            "dW_gate");
-  LMOE_HIP((bg<BG_GROUP_K, 1, 1, 1, 0>(bop(V, I, 0, nullptr, 1, 1), bop(zsrc, L, 0, sorted, k, 1), gr->dw_value, L, I, L,
+  LMOE_HIP((bg<BG_GROUP_K, 1, 0, 1, 0>(bop(dV, I, 0, nullptr, 1, 1), bop(zsrc, L, 0, sorted, k, 1), gr->dw_value, L, I, L,
                                        0, 0, st, sh, 0, (int64_t)I * L, offsets)),
            "dW_value");
   if (lmoe_status s = record(ev, 3, st)) return s;
   // --- latent projection and dx --------------------------------------------
   if (T > 0) {
     hipLaunchKernelGGL(bw_gather_sum_kernel, dim3((unsigned)cdiv(L, 256), T), dim3(256), 0, st, zr, pos, L, k,
-                       w->w_down ? dz : gr->dx, 0);
+                       w->w_down ? nullptr : gr->dx, w->w_down ? dz : nullptr);
     LMOE_HIP(hipGetLastError(), "dz");
   }
   if (w->w_down) {
-    LMOE_HIP((bg<BG_DENSE, 0, 1, 1, 0>(bop(dz, L), bop(w->w_down, H), gr->dx, H, T, H, L, 0, st, sh)), "dx (latent)");
-    LMOE_HIP((bg<BG_DENSE, 1, 1, 1, 0>(bop(dz, L), bop(x, H), gr->dw_down, H, L, H, T, 0, st, sh)), "dW_down");
+    LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dz, L), bop(w->w_down, H), gr->dx, H, T, H, L, 0, st, sh)), "dx (latent)");
+    LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dz, L), bop(x, H), gr->dw_down, H, L, H, T, 0, st, sh)), "dW_down");
   }
   // --- router ---------------------------------------------------------------
   if (T > 0) {
@@ -1000,17 +1006,17 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
       const char* wso = static_cast<const char*>(w->ws_out) + (size_t)s * H * Is * 2;
       LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dy, H), bop(wso, Is), dhs + (size_t)s * Is, sis, T, Is, H, 0, st, sh)),
                "shared dh");
-      LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 1>(bop(dy, H), bop(hs + (size_t)s * Is, sis), gr->dws_out + (size_t)s * H * Is, Is,
+      LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dy, H), bop(hs + (size_t)s * Is, sis), gr->dws_out + (size_t)s * H * Is, Is,
                                          H, Is, T, 0, st, sh)),
                "dWs_out");
     }
-    LMOE_HIP(bw_situ(1, gs, vs, dhs, gs, vs, (int64_t)T * sis, sh, st), "shared SiTU-GLU gradient");
-    LMOE_HIP((bg<BG_DENSE, 0, 1, 1, 0>(bop(gs, sis), bop(w->ws_gate, H), gr->dx, H, T, H, sis, 1, st, sh)),
+    LMOE_HIP(bw_situ(1, gs, vs, dhs, dgs, dvs, (int64_t)T * sis, sh, st), "shared SiTU-GLU gradient");
+    LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dgs, sis), bop(w->ws_gate, H), gr->dx, H, T, H, sis, 1, st, sh)),
              "dx (shared gate)");
-    LMOE_HIP((bg<BG_DENSE, 0, 1, 1, 0>(bop(vs, sis), bop(w->ws_value, H), gr->dx, H, T, H, sis, 1, st, sh)),
+    LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dvs, sis), bop(w->ws_value, H), gr->dx, H, T, H, sis, 1, st, sh)),
              "dx (shared value)");
-    LMOE_HIP((bg<BG_DENSE, 1, 1, 1, 0>(bop(gs, sis), bop(x, H), gr->dws_gate, H, sis, H, T, 0, st, sh)), "dWs_gate");
-    LMOE_HIP((bg<BG_DENSE, 1, 1, 1, 0>(bop(vs, sis), bop(x, H), gr->dws_value, H, sis, H, T, 0, st, sh)), "dWs_value");
+    LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dgs, sis), bop(x, H), gr->dws_gate, H, sis, H, T, 0, st, sh)), "dWs_gate");
+    LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dvs, sis), bop(x, H), gr->dws_value, H, sis, H, T, 0, st, sh)), "dWs_value");
   }
   if (lmoe_status s = record(ev, 5, st)) return s;
   return LMOE_OK;
