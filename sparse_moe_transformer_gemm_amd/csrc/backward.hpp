@@ -329,7 +329,10 @@ __device__ __forceinline__ float bw_block_sum(float v, float* red) {
 
 // Per token: c = sum_j w_tj O[pos(t, j)] (fp32, j ascending), r = (mean c^2 +
 // eps)^-1/2, n = gamma c r.  Writes c (fp32), n (bf16) and r.
-__global__ __launch_bounds__(256) void bw_combine_norm_kernel(const float* O, const int32_t* pos, const float* w,
+__device__ __forceinline__ float bf2f(unsigned short h) { return __uint_as_float((unsigned)h << 16); }
+
+// (O is the expert output rows in bf16, as the forward stores them.)
+__global__ __launch_bounds__(256) void bw_combine_norm_kernel(const unsigned short* O, const int32_t* pos, const float* w,
                                                               const float* gamma, int L, int k, float eps, float* c,
                                                               unsigned short* n, float* r) {
   __shared__ float red[4];
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(256) void bw_combine_norm_kernel(const float* O, co
   float ss = 0.f;
   for (int l = threadIdx.x; l < L; l += 256) {
     float acc = 0.f;
-    for (int j = 0; j < k; ++j) acc += w[t * k + j] * O[(int64_t)pos[t * k + j] * L + l];
+    for (int j = 0; j < k; ++j) acc += w[t * k + j] * bf2f(O[(int64_t)pos[t * k + j] * L + l]);
     c[t * L + l] = acc;
     ss += acc * acc;
   }
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(256) void bw_combine_norm_kernel(const float* O, co
 // slot j, dO[pos(t, j)] = w_tj dc (bf16) and dw_tj = dc . O[pos(t, j)] (fp32
 // dc).  dc is recomputed per element and slot rather than stored.
 __global__ __launch_bounds__(256) void bw_norm_combine_grad_kernel(const float* dn, const float* c, const float* r,
-                                                                   const float* gamma, const float* O,
+                                                                   const float* gamma, const unsigned short* O,
                                                                    const int32_t* pos, const float* w, int L, int k,
                                                                    unsigned short* dO, float* dw) {
   __shared__ float red[4];
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(256) void bw_norm_combine_grad_kernel(const float* 
     for (int l = threadIdx.x; l < L; l += 256) {
       const float dc = rr * gamma[l] * dn[t * L + l] - coef * c[t * L + l];
       dO[a * L + l] = f2bf(wj * dc);
-      dot += dc * O[a * L + l];
+      dot += dc * bf2f(O[a * L + l]);
     }
     const float s = bw_block_sum(dot, red);
     if (threadIdx.x == 0) dw[t * k + j] = s;

@@ -265,7 +265,9 @@ struct ExpertTiles {
   }
 };
 
-template <class Cfg, typename CT>
+// RAW = 1: the epilogue stores the gate and value pre-activations (fp32,
+// graw / vraw [T*k, I] in assignment order) instead of their SiTU-GLU.
+template <class Cfg, typename CT, int RAW = 0>
 struct ExpertGVProb {
   ExpertTiles<Cfg> et;
   const char* z;      // [T, ldz]
@@ -276,6 +278,8 @@ struct ExpertGVProb {
   const float* sg;    // [E, I/128, L/128]
   const float* sv;
   char* act;          // [T*k, I]
+  float* graw;        // RAW: [T*k, I]
+  float* vraw;
   const char* wpk;    // packed gate/value blocks (see lmoe_pack_experts) or NULL
   const float* xs;    // W8A8: z block scales in expert order, [L/128, ldxs]
   int64_t ldxs;
@@ -675,16 +679,29 @@ __device__ __forceinline__ void UpProb<Cfg, CT>::epilogue(const State& st, const
   });
 }
 
-template <class Cfg, typename CT>
+template <class Cfg, typename CT, int RAW>
 template <class Acc>
-__device__ __forceinline__ void ExpertGVProb<Cfg, CT>::epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const {
+__device__ __forceinline__ void ExpertGVProb<Cfg, CT, RAW>::epilogue(const State& st, const Acc& acc, int wf0, int wt0,
+                                                                     int lane) const {
   for_glu<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int ul, int tl) __attribute__((always_inline)) {
     if (tl < st.rows) {
-      float v[4];
+      if constexpr (RAW) {
+        float gv[4], vv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = situ_glu(acc[i][j][4 * g + r], acc[i + 1][j][4 * g + r], cap, inv_cap);
-      CT* row = reinterpret_cast<CT*>(act) + (int64_t)(st.m0 + tl) * I;
-      store4<CT>(row, st.ft * (Cfg::BF / 2) + ul, v, I, true);
+        for (int r = 0; r < 4; ++r) {
+          gv[r] = acc[i][j][4 * g + r];
+          vv[r] = acc[i + 1][j][4 * g + r];
+        }
+        const int64_t o = (int64_t)(st.m0 + tl) * I;
+        store4<float>(graw + o, st.ft * (Cfg::BF / 2) + ul, gv, I, true);
+        store4<float>(vraw + o, st.ft * (Cfg::BF / 2) + ul, vv, I, true);
+      } else {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = situ_glu(acc[i][j][4 * g + r], acc[i + 1][j][4 * g + r], cap, inv_cap);
+        CT* row = reinterpret_cast<CT*>(act) + (int64_t)(st.m0 + tl) * I;
+        store4<CT>(row, st.ft * (Cfg::BF / 2) + ul, v, I, true);
+      }
     }
   });
 }

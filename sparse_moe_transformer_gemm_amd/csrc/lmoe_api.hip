@@ -426,6 +426,31 @@ hipError_t expert_down(const Ctx& c, const void* act, const int32_t* offsets, co
   return launch_gemm<Cfg, CT>(p, pad8(max_tiles(sh, Cfg::BT) * p.et.nft), c.st);
 }
 
+// Gate and value pre-activations (fp32, assignment order) for the backward's
+// recompute, with the forward's persistent bf16 expert GEMM.
+hipError_t expert_gv_raw(const Ctx& c, const void* z, const int32_t* offsets, const int32_t* sorted,
+                         const int4* tiles, const int32_t* tcount, float* g, float* v) {
+  using Cfg = T2ExpertGV;
+  const lmoe_shape* sh = c.sh;
+  ExpertGVProb<Cfg, bf16, 1> p{};
+  p.et.offsets = offsets;
+  p.et.tiles = tiles;
+  p.et.tile_count = tcount;
+  p.et.nft = (int)cdiv(sh->I, Cfg::BF / 2);
+  p.z = static_cast<const char*>(z);
+  p.ldz = sh->L;
+  p.sorted = sorted;
+  p.wg = static_cast<const char*>(c.w->w_gate);
+  p.wv = static_cast<const char*>(c.w->w_value);
+  p.graw = g;
+  p.vraw = v;
+  p.wpk = c.pk_gv();
+  p.I = sh->I;
+  p.L = sh->L;
+  p.k = sh->k;
+  return launch_gemm<Cfg, bf16>(p, pad8(max_tiles(sh, Cfg::BT) * p.et.nft), c.st);
+}
+
 // W8A8 gate/value: z (or x) quantised per token, its row scales put in expert
 // order, then the e4m3 x e4m3 GEMM with the SiTU-GLU epilogue (bf16 act).
 hipError_t expert_gv_a8(const Ctx& c, const Plan& pl, void* ws, const void* z, const int32_t* offsets,
@@ -556,8 +581,8 @@ lmoe_status record(void* const* ev, int i, hipStream_t st) {
 constexpr int kBwChunks = 64;  // token chunks of the dgamma reduction
 
 struct BPlan {
-  size_t logits, z, idx, w, bcounts, offsets, sorted, pos, tiles, tcount;
-  size_t G, V, A, dA, dG, dV, O, dO, c, n, dn, dz, r, dw, dl, gs, vs, hs, dhs, dgs, dvs, dgp, total;
+  size_t logits, z, idx, w, bcounts, offsets, sorted, pos, tiles, tcount, tiles2, tcount2;
+  size_t G, V, A, dA, dG, dV, O, zr, dO, c, n, dn, dz, r, dw, dl, gs, vs, hs, dhs, dgs, dvs, dgp, total;
 };
 
 BPlan bplan(const lmoe_shape* sh) {
@@ -580,6 +605,8 @@ BPlan bplan(const lmoe_shape* sh) {
   p.pos = take(tk * 4);
   p.tiles = take((size_t)max_tiles(sh, kBgM) * 16);
   p.tcount = take(8);
+  p.tiles2 = take((size_t)max_tiles(sh, T2ExpertGV::BT) * 16);  // the persistent expert GEMMs' tiles
+  p.tcount2 = take(8);
   // fp32: GEMM outputs and what elementwise gradients read; bf16: GEMM inputs
   p.G = take(tk * sh->I * 4);
   p.V = take(tk * sh->I * 4);
@@ -587,7 +614,8 @@ BPlan bplan(const lmoe_shape* sh) {
   p.dA = take(tk * sh->I * 4);
   p.dG = take(tk * sh->I * 2);
   p.dV = take(tk * sh->I * 2);
-  p.O = take(tk * sh->L * 4);
+  p.O = take(tk * sh->L * 2);
+  p.zr = take(tk * sh->L * 4);
   p.dO = take(tk * sh->L * 2);
   p.c = take(T * sh->L * 4);
   p.n = take(T * sh->L * 2);
@@ -899,11 +927,13 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   int32_t* pos = at<int32_t>(ws, pl.pos);
   int4* tiles = at<int4>(ws, pl.tiles);
   int32_t* tc = at<int32_t>(ws, pl.tcount);
-  float *G = at<float>(ws, pl.G), *V = at<float>(ws, pl.V), *dA = at<float>(ws, pl.dA), *O = at<float>(ws, pl.O);
+  float *G = at<float>(ws, pl.G), *V = at<float>(ws, pl.V), *dA = at<float>(ws, pl.dA), *zr = at<float>(ws, pl.zr);
   float *c = at<float>(ws, pl.c), *dn = at<float>(ws, pl.dn), *r = at<float>(ws, pl.r), *dw = at<float>(ws, pl.dw);
   float *dl = at<float>(ws, pl.dl), *gs = at<float>(ws, pl.gs), *vs = at<float>(ws, pl.vs), *dhs = at<float>(ws, pl.dhs);
   unsigned short *A = at<unsigned short>(ws, pl.A), *dG = at<unsigned short>(ws, pl.dG), *dV = at<unsigned short>(ws, pl.dV);
   unsigned short *dO = at<unsigned short>(ws, pl.dO), *n = at<unsigned short>(ws, pl.n), *dz = at<unsigned short>(ws, pl.dz);
+  unsigned short* O = at<unsigned short>(ws, pl.O);
+  const Ctx cx{sh, w, st};
   unsigned short *hs = at<unsigned short>(ws, pl.hs), *dgs = at<unsigned short>(ws, pl.dgs), *dvs = at<unsigned short>(ws, pl.dvs);
   const void* zsrc = w->w_down ? at<void>(ws, pl.z) : x;
 
@@ -917,17 +947,16 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
     LMOE_HIP(launch_topk(logits, w->b_router, sh->T, E, k, idx, tw, st), "top-k");
   }
   LMOE_HIP(launch_permute(idx, sh->T, E, k, at<int32_t>(ws, pl.bcounts), offsets, sorted, pos, st), "permute");
-  LMOE_HIP(launch_tiles(offsets, E, kBgM, tiles, tc, 0, nullptr, nullptr, st), "tile list");
-  LMOE_HIP((bg<BG_GROUP_M, 0, 0, 0, 0>(bop(zsrc, L, 0, sorted, k, 1), bop(w->w_gate, L, (int64_t)I * L), G, I, 0, I, L, 0,
-                                       st, sh, 0, 0, offsets, tiles, tc)),
-           "expert gate");
-  LMOE_HIP((bg<BG_GROUP_M, 0, 0, 0, 0>(bop(zsrc, L, 0, sorted, k, 1), bop(w->w_value, L, (int64_t)I * L), V, I, 0, I, L, 0,
-                                       st, sh, 0, 0, offsets, tiles, tc)),
-           "expert value");
-  LMOE_HIP(bw_situ(0, G, V, nullptr, A, nullptr, (int64_t)tk * I, sh, st), "SiTU-GLU");
-  LMOE_HIP((bg<BG_GROUP_M, 0, 0, 0, 0>(bop(A, I, 0, nullptr, 1, 1), bop(w->w_out, I, (int64_t)L * I), O, L, 0, L, I, 0,
-                                       st, sh, 0, 0, offsets, tiles, tc)),
-           "expert down");
+  int4* tiles2 = at<int4>(ws, pl.tiles2);
+  int32_t* tc2 = at<int32_t>(ws, pl.tcount2);
+  LMOE_HIP(launch_tiles(offsets, E, kBgM, tiles, tc, T2ExpertGV::BT, tiles2, tc2, st), "tile lists");
+  // the routed experts as the forward computes them (O in bf16), keeping the
+  // gate and value pre-activations
+  if (T > 0) {
+    LMOE_HIP(expert_gv_raw(cx, zsrc, offsets, sorted, tiles2, tc2, G, V), "expert gate/value");
+    LMOE_HIP(bw_situ(0, G, V, nullptr, A, nullptr, (int64_t)tk * I, sh, st), "SiTU-GLU");
+    LMOE_HIP((expert_down<T2ExpertDn, bf16>(cx, A, offsets, tiles2, tc2, O)), "expert down");
+  }
   if (T > 0)
     hipLaunchKernelGGL(bw_combine_norm_kernel, dim3(T), dim3(256), 0, st, O, pos, tw, w->gamma, L, k, sh->rms_eps, c, n, r);
   LMOE_HIP(hipGetLastError(), "combine + norm");
@@ -965,7 +994,6 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
                                        0, st, sh, 0, (int64_t)L * I, offsets)),
            "dW_out");
   LMOE_HIP(bw_situ(1, G, V, dA, dG, dV, (int64_t)tk * I, sh, st), "SiTU-GLU gradient");
-  float* zr = O;  // O is no longer needed: latent gradient rows per assignment
   LMOE_HIP((bg<BG_GROUP_M, 0, 0, 1, 0>(bop(dG, I, 0, nullptr, 1, 1), bop(w->w_gate, L, (int64_t)I * L), zr, L, 0, L, I, 0,
                                        st, sh, 0, 0, offsets, tiles, tc)),
            "dz rows (gate)");
