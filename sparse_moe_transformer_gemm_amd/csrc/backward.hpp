@@ -239,15 +239,22 @@ __global__ __launch_bounds__(256) void bgemm_kernel(const BgArgs p) {
     if (kt + 1 < nk) load(kt + 1);
 #pragma unroll
     for (int ks = 0; ks < kBgK / 16; ++ks) {
+      // 32-row blocks with no valid row (an expert's last, partial row
+      // tile; a tile past N) are skipped, reads and MFMAs alike: the test is
+      // uniform across the wave
       bf16x8 a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = bg_frag<ARC>(sA[cur], wm + i * 32, ks, lane);
+      for (int i = 0; i < 2; ++i)
+        if (wm + i * 32 < rows_a) a[i] = bg_frag<ARC>(sA[cur], wm + i * 32, ks, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = bg_frag<BRC>(sB[cur], wn + j * 32, ks, lane);
+      for (int j = 0; j < 2; ++j)
+        if (wn + j * 32 < rows_b) b[j] = bg_frag<BRC>(sB[cur], wn + j * 32, ks, lane);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j)
+          if (wm + i * 32 < rows_a && wn + j * 32 < rows_b)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < nk) {
       ta.store(sA[cur ^ 1], tid);
