@@ -60,6 +60,9 @@ def parse():
                     help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs of the layer and of the copy "
                          "calibration into profiles/traffic_<workload>.json, then exit")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--quantile", action="store_true",
+                    help="time the Quantile Balancing threshold solve (lmoe_quantile_bias) on the workload's "
+                         "router-logit shape; prints its own JSON line")
     ap.add_argument("--backward", action="store_true",
                     help="time lmoe_backward (forward recompute + every gradient) instead of the forward; "
                          "prints its own JSON line")
@@ -172,6 +175,9 @@ def main():
     dev = torch.device("cuda:0")
     if a.backward:
         bench_backward(a, lmoe, dev)
+        return
+    if a.quantile:
+        bench_quantile(a, lmoe, dev)
         return
     cfg = get_config(a.workload)
     print(f"# generating {cfg.name} inputs on the device", file=sys.stderr, flush=True)
@@ -352,6 +358,77 @@ def bench_backward(a, lmoe, dev):
     }
     if a.cpu_sample > 0:
         out["cpu_baseline"], out["parity"] = cpu_baseline_backward(cfg, g, dy, idx, grads["dx"], a.cpu_sample, dev)
+    print(json.dumps(out), flush=True)
+
+
+def bench_quantile(a, lmoe, dev):
+    """One step = one lmoe_quantile_bias call: the per-expert (1 - k/E)
+    quantile of the batch's sigmoid scores from fp32 router logits [T, E]
+    already in HBM (a skewed router: per-expert offsets of +-4)."""
+    import numpy as np
+    import torch
+
+    from oracle import lmoe_oracle as O
+    from synth import get_config
+    from synth.inputs import make_router_logits
+
+    cfg = get_config(a.workload)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    lg_host = make_router_logits(T, E, seed=13, spread=4.0)
+    lg = torch.from_numpy(lg_host).to(dev)
+    sh = lmoe.shape_of(cfg)
+    bias = torch.empty(E, dtype=torch.float32, device=dev)
+    ws = lmoe.alloc_workspace(sh, dev)
+    for _ in range(a.warmup):
+        lmoe.quantile_bias(sh, lg, out=bias, ws=ws)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(a.steps):
+        lmoe.quantile_bias(sh, lg, out=bias, ws=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / a.steps
+    # algorithmic bytes: the logits read once, the bias written once
+    nbytes = T * E * 4 + E * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "Quantile Balancing threshold solve, tokens/s (per-expert quantile of the batch's router scores)",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0, 1.7^2) router logits with per-expert offsets of +-4)",
+        "config": {"workload": f"quantile_bias_T{T}_E{E}_k{k}", "T": T, "E": E, "k": k,
+                   "parallelism": "single GPU"},
+        "roofline": {
+            "kernel": "qb_keys_kernel + qb_select_kernel",
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": nbytes,
+            "avg_ms": round(ms, 5),
+        },
+    }
+    if a.cpu_sample > 0:
+        cores = len(os.sched_getaffinity(0))
+        t0c = time.perf_counter()
+        ref = O.quantile_bias(lg_host.astype(np.float64), k)
+        dt = time.perf_counter() - t0c
+        err = float(np.abs(bias.cpu().numpy().astype(np.float64) - ref).max())
+        out["cpu_baseline"] = {"value": round(T / dt, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                               "sample": f"the whole {T}-token batch (numpy sort per expert, fp64), {dt:.2f} s",
+                               "seconds": round(dt, 3)}
+        out["parity"] = {"max_abs_err": err, "tol": 1e-6, "ok": err <= 1e-6}
     print(json.dumps(out), flush=True)
 
 

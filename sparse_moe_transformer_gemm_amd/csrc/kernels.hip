@@ -320,47 +320,84 @@ __global__ __launch_bounds__(256) void qb_keys_kernel(const float* logits, int64
   }
 }
 
-// One work-group per expert: the two order statistics by radix selection
-// (4 passes of 8 bits, most significant first) over the expert's keys.
+// Keys of an expert held in LDS by the select kernel (64 KB); longer batches
+// are read from global memory in every pass.
+constexpr int64_t kQbLdsKeys = 16384;
+
+// Inclusive sum over the 256 threads of a work-group (4 waves).
+__device__ __forceinline__ uint32_t qb_block_scan(uint32_t v, uint32_t* wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t u = __shfl_up(v, d);
+    if (lane >= d) v += u;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) v += wsum[i];
+  return v;
+}
+
+// One work-group per expert: the lower order statistic s_(lo) by radix
+// selection (4 passes of 8 bits, most significant first) over the expert's
+// keys, held in LDS; then s_(lo+1), which is the same key when enough keys
+// tie with it and otherwise the smallest key above it (one more pass).
 __global__ __launch_bounds__(256) void qb_select_kernel(const uint32_t* keys, int64_t T, int E, int k, float* bias) {
+  extern __shared__ uint32_t sk[];
   __shared__ uint32_t hist[256];
+  __shared__ uint32_t wsum[4];
   __shared__ int64_t rank_s;
-  __shared__ uint32_t bin_s;
+  __shared__ uint32_t bin_s, min_s[4];
   const int tid = threadIdx.x;
   const int e = blockIdx.x;
   const uint32_t* col = keys + (int64_t)e * T;
+  const bool inl = T <= kQbLdsKeys;
+  if (inl)
+    for (int64_t t = tid; t < T; t += 256) sk[t] = col[t];
   const double h = (double)(T - 1) * (1.0 - (double)k / (double)E);
   const int64_t lo = (int64_t)floor(h);
   const int64_t hi = lo + 1 < T ? lo + 1 : T - 1;
-  uint32_t kv[2];
-  for (int which = 0; which < 2; ++which) {
-    int64_t r = which ? hi : lo;  // 0-based rank among the keys matching the prefix
-    uint32_t prefix = 0, mask = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
-      __syncthreads();
-      for (int64_t t = tid; t < T; t += 256) {
-        const uint32_t v = col[t];
-        if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int64_t cum = 0;
-        int b = 0;
-        while (b < 255 && cum + (int64_t)hist[b] <= r) cum += hist[b++];
-        rank_s = r - cum;
-        bin_s = (uint32_t)b;
-      }
-      __syncthreads();
-      prefix |= bin_s << shift;
-      mask |= 255u << shift;
-      r = rank_s;
-      __syncthreads();
+  int64_t r = lo;  // 0-based rank among the keys that match the prefix
+  uint32_t prefix = 0, mask = 0, ties = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    for (int64_t t = tid; t < T; t += 256) {
+      const uint32_t v = inl ? sk[t] : col[t];
+      if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & 255u], 1u);
     }
-    kv[which] = prefix;
+    __syncthreads();
+    const uint32_t c = hist[tid];
+    const uint32_t incl = qb_block_scan(c, wsum);
+    const uint32_t excl = incl - c;
+    if ((int64_t)excl <= r && r < (int64_t)incl) {
+      bin_s = (uint32_t)tid;
+      rank_s = r - (int64_t)excl;
+    }
+    __syncthreads();
+    prefix |= bin_s << shift;
+    mask |= 255u << shift;
+    r = rank_s;
+    ties = hist[bin_s];  // after the last pass: the keys equal to s_(lo)
+    __syncthreads();
+  }
+  const uint32_t klo = prefix;
+  uint32_t khi = klo;
+  if (hi != lo && r + 1 >= (int64_t)ties) {
+    // s_(lo+1) is the smallest key above s_(lo)
+    uint32_t m = 0xffffffffu;
+    for (int64_t t = tid; t < T; t += 256) {
+      const uint32_t v = inl ? sk[t] : col[t];
+      if (v > klo && v < m) m = v;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) m = min(m, (uint32_t)__shfl_xor(m, d));
+    if ((tid & 63) == 0) min_s[tid >> 6] = m;
+    __syncthreads();
+    khi = min(min(min_s[0], min_s[1]), min(min_s[2], min_s[3]));
   }
   if (tid == 0) {
-    const double xl = key2f(kv[0]), xh = key2f(kv[1]);
+    const double xl = key2f(klo), xh = key2f(khi);
     bias[e] = (float)(-(xl + (h - (double)lo) * (xh - xl)));
   }
 }
@@ -372,7 +409,8 @@ hipError_t launch_quantile_bias(const float* logits, int64_t T, int E, int k, ui
                      logits, T, E, keys);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(qb_select_kernel, dim3((unsigned)E), dim3(256), 0, st, keys, T, E, k, bias);
+  const size_t lds = T <= kQbLdsKeys ? (size_t)T * 4 : 0;
+  hipLaunchKernelGGL(qb_select_kernel, dim3((unsigned)E), dim3(256), lds, st, keys, T, E, k, bias);
   return hipGetLastError();
 }
 
