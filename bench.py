@@ -323,7 +323,20 @@ def bench_backward(a, lmoe, dev):
     fl = lmoe.backward_flops(sh, projections=not cfg.identity_proj, up=not cfg.identity_proj)
     total = sum(fl.values())
     tflops = total / (ms * 1e-3) / 1e12
-    ex_tf = fl["expert_grads"] / (stages["expert_grads"] * 1e-3) / 1e12
+    # the dominant stage, routed expert gradients: HBM-bound at K3 shape (the
+    # fp32 gradients of every expert are written: t_HBM > t_MFMA)
+    ex_s = stages["expert_grads"] * 1e-3
+    ex_bytes = lmoe.backward_expert_bytes(sh)
+    t_hbm = ex_bytes / (PEAK_HBM_GBS * 1e9)
+    t_mfma = fl["expert_grads"] / (PEAK_BF16_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(ex_bytes / ex_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(t_hbm / ex_s, 4), "bytes_per_launch": ex_bytes}
+    else:
+        roof = {"bound": "mfma", "achieved": round(fl["expert_grads"] / ex_s / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(t_mfma / ex_s, 4)}
+    roof.update(flops_per_launch=fl["expert_grads"], mfma_tflops=round(fl["expert_grads"] / ex_s / 1e12, 1),
+                t_hbm_ms=round(t_hbm * 1e3, 3), t_mfma_ms=round(t_mfma * 1e3, 3))
     out = {
         "metric": "latent-MoE layer backward tokens/s (forward recompute + fp32 gradients of x and every weight)",
         "value": round(T / (ms * 1e-3), 1),
@@ -344,17 +357,8 @@ def bench_backward(a, lmoe, dev):
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "stage_gflop": {k: round(v / 1e9, 1) for k, v in fl.items()},
-        "roofline": {
-            "kernel": "routed expert gradient GEMMs (grouped dgrad + wgrad)",
-            "bound": "mfma",
-            "achieved": round(ex_tf, 1),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(ex_tf / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
-            "flops_per_launch": fl["expert_grads"],
-            "avg_ms": round(stages["expert_grads"], 4),
-        },
+        "roofline": dict({"kernel": "routed expert gradient stage (grouped dgrads + wgrads)", "traffic": None,
+                          "avg_ms": round(stages["expert_grads"], 4)}, **roof),
     }
     if a.cpu_sample > 0:
         out["cpu_baseline"], out["parity"] = cpu_baseline_backward(cfg, g, dy, idx, grads["dx"], a.cpu_sample, dev)

@@ -419,6 +419,21 @@ def backward_flops(sh: Shape, projections=True, up=True) -> dict:
     return {n: float(v) for n, v in st.items()}
 
 
+def backward_expert_bytes(sh: Shape) -> float:
+    """Algorithmic HBM bytes of lmoe_backward's routed-expert gradient stage:
+    the bf16 gate, value and out weights of every expert read once (the
+    dgrads), the fp32 gate, value and out gradients of every expert written
+    once (experts no token chose get zeros), and each activation written or
+    read once: dO (bf16), A (bf16), dA (fp32), G and V (fp32), dG and dV
+    (bf16), the latent gradient rows (fp32) and z (bf16)."""
+    T, L, E, k, I = sh.T, sh.L, sh.E, sh.k, sh.I
+    tk = T * k
+    weights = 3 * E * I * L * 2
+    grads = 3 * E * I * L * 4
+    acts = tk * (L * 2 + I * 2 + I * 4 + 2 * I * 4 + 2 * I * 2 + L * 4) + T * L * 2
+    return float(weights + grads + acts)
+
+
 def expert_bytes(sh: Shape, touched: int, which="all") -> float:
     """Weight bytes of `touched` routed experts: gate+value, down, or all."""
     wb = {F32: 4, BF16: 2, F8E4M3: 1}[sh.w_expert]
