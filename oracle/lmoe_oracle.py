@@ -1,4 +1,6 @@
-"""CPU fp64 oracle of one Stable Latent MoE layer forward pass.
+"""CPU fp64 oracle of one Stable Latent MoE layer: the forward pass (bf16,
+fp32, e4m3 expert weights, W8A8 routed experts), the Quantile Balancing
+thresholds and the backward pass.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call
 this module: only tests/, the smoke check in __graft_entry__ and the
@@ -26,12 +28,18 @@ Readings taken where the pages are silent (each is a documented choice):
   * shared experts run at full width on x, use the same SiTU-GLU, have
     weight 1 and are added after the up-projection;
   * no capacity limit (no token is dropped), no biases in the linears, and
-    the residual add is outside the layer.
+    the residual add is outside the layer;
+  * W8A8: the routed experts' activations, as stored in the activation dtype,
+    are quantised per row per 128 columns to e4m3fn (scale amax / 448);
+  * Quantile Balancing: expert e's threshold is the (1 - k/E) quantile of its
+    batch scores (linear interpolation), and its bias is minus that;
+  * backward: the gradient of sum(y * dy); the selection and its bias carry
+    none, the router's flows through the renormalised combine weights.
 
 Parity pins: every function here is pinned by tests/test_oracle.py against
-library routines (torch/scipy), closed forms, invariants or brute force; the
-chosen readings above are conventions and are pinned only through those
-properties.
+library routines (torch/scipy, torch.autograd for the gradients), closed
+forms, invariants, finite differences or brute force; the chosen readings
+above are conventions and are pinned only through those properties.
 """
 
 import numpy as np
