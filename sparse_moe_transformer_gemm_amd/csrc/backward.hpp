@@ -180,11 +180,13 @@ __device__ __forceinline__ bool bg_vec_ok(const char* base, int64_t ld, int es) 
   return ((reinterpret_cast<uintptr_t>(base) & 15) == 0) && ((ld * es) % 16 == 0);
 }
 
-// The grouped wgrads (a few k-tiles per work-group) are latency-bound: they
-// ask for 4 waves per SIMD, which fits them in 128 registers; the other
-// modes would spill at that occupancy.
+// The grouped modes (per-expert wgrads with a few k-tiles per work-group, and
+// the row-tiled dgrads over each expert's rows) are latency-bound: they ask
+// for 4 waves per SIMD, i.e. at most 128 registers. The dgrads spill a few
+// registers at that bound and are still faster (measured); the dense mode keeps
+// its full register budget.
 template <int MODE, int ARC, int AF32, int BRC, int BF32>
-__global__ __launch_bounds__(256, MODE == BG_GROUP_K ? 4 : 1) void bgemm_kernel(const BgArgs p) {
+__global__ __launch_bounds__(256, MODE != BG_DENSE ? 4 : 1) void bgemm_kernel(const BgArgs p) {
   __shared__ __attribute__((aligned(16))) char sA[2][kBgTileBytes];
   __shared__ __attribute__((aligned(16))) char sB[2][kBgTileBytes];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
