@@ -85,6 +85,7 @@ struct NSeg {
 
 template <class Cfg, typename CT>
 struct DenseXProb {
+  static constexpr bool kDenseRows = true;  // rows past T: loaded from row 0, never stored
   const char* x;
   int64_t T;
   int K;              // H
@@ -174,6 +175,7 @@ struct KSeg {
 
 template <class Cfg, typename CT>
 struct UpProb {
+  static constexpr bool kDenseRows = true;  // rows past T: never stored
   int64_t T;
   int N;              // H
   int nks, nft, ntt, padded;
