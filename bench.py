@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="time lmoe_backward (forward recompute + every gradient) instead of the forward; "
                          "prints its own JSON line")
+    ap.add_argument("--library-gemms", action="store_true",
+                    help="context only: time torch's bf16 GEMMs (hipBLASLt) at the T=8192 layer's dense and "
+                         "uniform-load expert shapes; prints its own JSON line")
     return ap.parse_args()
 
 
@@ -178,6 +181,9 @@ def main():
         return
     if a.quantile:
         bench_quantile(a, lmoe, dev)
+        return
+    if a.library_gemms:
+        bench_library_gemms(a)
         return
     cfg = get_config(a.workload)
     print(f"# generating {cfg.name} inputs on the device", file=sys.stderr, flush=True)
@@ -363,6 +369,51 @@ def bench_backward(a, lmoe, dev):
     if a.cpu_sample > 0:
         out["cpu_baseline"], out["parity"] = cpu_baseline_backward(cfg, g, dy, idx, grads["dx"], a.cpu_sample, dev)
     print(json.dumps(out), flush=True)
+
+
+def bench_library_gemms(a):
+    """Context for the GEMM kernels' efficiency, not part of the layer: torch's
+    bf16 products (hipBLASLt on ROCm) at the T=8192 K3 shapes.  Dense: route
+    GEMM (x [8192, 7168] against the stacked router, W_dn and shared gate/value
+    weights, 8576 rows) and up GEMM (K = 3584 + 2048, 7168 rows), weights
+    [N, K] as the layer stores them.  Experts: a batched product with a
+    uniform 146 rows per expert (the mean load), which the grouped GEMMs
+    handle with ragged rows instead."""
+    import torch
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev).manual_seed(0)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    out = {"metric": "library bf16 GEMM times at the K3 T=8192 shapes (context)", "unit": "ms", "dense": {},
+           "batched_experts": {}}
+    for name, (M, K, N) in {"route": (8192, 7168, 8576), "up": (8192, 5632, 7168)}.items():
+        A = torch.randn(M, K, device=dev, dtype=bf, generator=g)
+        W = torch.randn(N, K, device=dev, dtype=bf, generator=g)
+        ms = timed(lambda: torch.nn.functional.linear(A, W), 10)
+        out["dense"][name] = {"M": M, "K": K, "N": N, "ms": round(ms, 4), "tflops": round(2 * M * K * N / ms / 1e9, 1)}
+        del A, W
+    for name, (E, M, K, N) in {"gate_value": (896, 146, 3584, 2048), "down": (896, 146, 1024, 3584)}.items():
+        A = torch.randn(E, M, K, device=dev, dtype=bf, generator=g)
+        B = torch.randn(E, K, N, device=dev, dtype=bf, generator=g)
+        ms = timed(lambda: torch.bmm(A, B), 5)
+        byt = E * K * N * 2 + E * M * (K + N) * 2
+        out["batched_experts"][name] = {"E": E, "rows": M, "K": K, "N": N, "ms": round(ms, 4),
+                                        "gbs": round(byt / ms / 1e6, 1)}
+        del A, B
+        torch.cuda.empty_cache()
+    print(json.dumps(out))
 
 
 def bench_quantile(a, lmoe, dev):

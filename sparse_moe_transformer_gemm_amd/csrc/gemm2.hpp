@@ -246,9 +246,8 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
 // double-buffered across the four 16-wide k-steps so the LDS reads of step
 // ks+1 overlap the MFMAs of step ks.  Token blocks j >= tiv (rows all past
 // the valid ones) are skipped, loads and MFMAs alike; the test is uniform
-// across the wave.  (A branch-free variant of this loop for full tiles was
-// measured to run the 256x256 dense GEMMs about 3x slower on MI355X, and to
-// slow the kernels launched after them, so it is not used.)
+// across the wave.  Dense GEMMs, whose extra token rows are never stored,
+// use the unconditional mma_ktile_full below instead.
 template <int FI, int TI, bool DB = true>
 __device__ __forceinline__ void mma_ktile(f32x16 (&acc)[FI][TI], const char* sW, const char* sX, int wf0, int wt0,
                                           int lane, int tiv) {
