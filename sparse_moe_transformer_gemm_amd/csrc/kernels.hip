@@ -236,18 +236,35 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(const CT* __restrict_
   for (int c = 0; c < MAXC; ++c)
 #pragma unroll
     for (int i = 0; i < EPC; ++i) acc[c][i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int p = pos[t * k + j];
-    if (p < 0) continue;
-    const float wj = w[t * k + j];
-    const CT* row = O + (int64_t)p * L;
+  // rows of JB assignments are loaded together (more loads in flight per
+  // thread), then added in ascending j; a missing row (pos < 0) adds nothing
+  constexpr int JB = 16 / MAXC;
+  for (int j0 = 0; j0 < k; j0 += JB) {
+    vec_t v[JB][MAXC];
+    float wj[JB];
+    bool ok[JB];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-      const int ch = tid + c * 256;
-      if (ch < nch) {
-        const vec_t v = *reinterpret_cast<const vec_t*>(row + ch * EPC);
+    for (int u = 0; u < JB; ++u) {
+      const int p = j0 + u < k ? pos[t * k + j0 + u] : -1;
+      ok[u] = p >= 0;
+      wj[u] = ok[u] ? w[t * k + j0 + u] : 0.f;
+      const CT* row = O + (int64_t)(ok[u] ? p : 0) * L;
 #pragma unroll
-        for (int i = 0; i < EPC; ++i) acc[c][i] += wj * to_f32(v[i]);
+      for (int c = 0; c < MAXC; ++c) {
+        const int ch = tid + c * 256;
+        if (ok[u] && ch < nch) v[u][c] = *reinterpret_cast<const vec_t*>(row + ch * EPC);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < JB; ++u) {
+      if (!ok[u]) continue;
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) {
+        const int ch = tid + c * 256;
+        if (ch < nch) {
+#pragma unroll
+          for (int i = 0; i < EPC; ++i) acc[c][i] += wj[u] * to_f32(v[u][c][i]);
+        }
       }
     }
   }
@@ -275,7 +292,10 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(const CT* __restrict_
 hipError_t launch_combine_norm(bool bf16_act, const void* O, const int32_t* pos, const float* w, const float* gamma,
                                int64_t T, int L, int k, float eps, void* n, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  if (bf16_act)
+  if (bf16_act && L <= 2 * 256 * 8)
+    hipLaunchKernelGGL((combine_norm_kernel<bf16, 2>), dim3((unsigned)T), dim3(256), 0, st, (const bf16*)O, pos, w,
+                       gamma, L, k, eps, (bf16*)n);
+  else if (bf16_act)
     hipLaunchKernelGGL((combine_norm_kernel<bf16, 4>), dim3((unsigned)T), dim3(256), 0, st, (const bf16*)O, pos, w,
                        gamma, L, k, eps, (bf16*)n);
   else
