@@ -258,8 +258,13 @@ __global__ __launch_bounds__(256, MODE != BG_DENSE ? 4 : 1) void bgemm_kernel(co
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          if (wm + i * 32 < rows_a && wn + j * 32 < rows_b)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          if (wm + i * 32 < rows_a && wn + j * 32 < rows_b) {
+            // dense mode: transposed blocks, for row-vector stores (below)
+            if constexpr (MODE == BG_DENSE)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          }
     }
     if (kt + 1 < nk) {
       ta.store(sA[cur ^ 1], tid);
@@ -268,10 +273,63 @@ __global__ __launch_bounds__(256, MODE != BG_DENSE ? 4 : 1) void bgemm_kernel(co
     __syncthreads();
   }
 
-  // lane l holds column n = l % 32 of each 32x32 block and rows
-  // 8 g + 4 (l / 32) + r (g, r < 4)
   char* cbase = p.c + (int64_t)e * p.cgstride * (p.cbf16 ? 2 : 4);
   const int crow0 = (MODE == BG_GROUP_M ? rowbase : 0) + m0;
+  if constexpr (MODE == BG_DENSE) {
+    // acc[i][j] is the transposed 32x32 block: lane l holds row m = l % 32 of
+    // C and its columns 8 g + 4 (l / 32) + r (g, r < 4), so each g is four
+    // consecutive elements of one C row, stored as one 16-byte (fp32) or
+    // 8-byte (bf16) vector where aligned and wholly inside the tile.  (The
+    // grouped modes measured slower this way and keep the layout below.)
+    const bool cvec = (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(cbase) & (p.cbf16 ? 7 : 15)) == 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int m = wm + i * 32 + lr;
+        if (m >= rows_a || wn + j * 32 >= rows_b) continue;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = wn + j * 32 + g * 8 + (lane >> 5) * 4;
+          if (n >= rows_b) continue;
+          const int64_t off = (int64_t)(crow0 + m) * p.ldc + n0 + n;
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r];
+          if (p.cbf16) {
+            unsigned short* cp = reinterpret_cast<unsigned short*>(cbase) + off;
+            if (cvec && n + 3 < rows_b) {
+              *reinterpret_cast<uint2*>(cp) =
+                  uint2{f2bf(v[0]) | ((unsigned)f2bf(v[1]) << 16), f2bf(v[2]) | ((unsigned)f2bf(v[3]) << 16)};
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (n + r < rows_b) cp[r] = f2bf(v[r]);
+            }
+          } else {
+            float* cp = reinterpret_cast<float*>(cbase) + off;
+            if (cvec && n + 3 < rows_b) {
+              float4 o = {v[0], v[1], v[2], v[3]};
+              if (p.accumulate) {
+                const float4 c = *reinterpret_cast<const float4*>(cp);
+                o.x += c.x;
+                o.y += c.y;
+                o.z += c.z;
+                o.w += c.w;
+              }
+              *reinterpret_cast<float4*>(cp) = o;
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (n + r < rows_b) cp[r] = p.accumulate ? cp[r] + v[r] : v[r];
+            }
+          }
+        }
+      }
+    return;
+  }
+  // lane l holds column n = l % 32 of each 32x32 block and rows
+  // 8 g + 4 (l / 32) + r (g, r < 4)
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
