@@ -15,11 +15,41 @@
 namespace lmoe {
 
 // ---------------------------------------------------------------------------
-// Top-k: one wavefront per token.  Lane l holds experts l, l+64, ...; each of
-// the k rounds takes the lane-local best (largest s + b, lower index on equal
-// values), reduces it across the wave with the same order, and retires the
-// winner.  All selection state stays in registers.
+// Top-k: one wavefront per token.  Lane l holds experts l, l+64, ... as one
+// 64-bit key each: the order-preserving image of the biased score s + b in
+// the high word and the complement of the expert index in the low word, so
+// the largest key is the largest score, lower index first on equal scores.
+// NaN and -inf scores rank as -FLT_MAX: below every real expert, above
+// padding and retired entries (key 0).  Each of the k rounds takes the
+// wave's largest key with DPP steps inside each 16-lane row and scalar reads
+// across the four rows, then retires the winner; all state stays in
+// registers and no round needs an LDS round trip.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t topk_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t topk_dpp(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Largest key over the wave, the same value in every lane.
+__device__ __forceinline__ uint64_t topk_wave_max(uint64_t v) {
+  v = topk_max(v, topk_dpp<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
+  v = topk_max(v, topk_dpp<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
+  v = topk_max(v, topk_dpp<0x141>(v));  // row_half_mirror: the other quad of 8
+  v = topk_max(v, topk_dpp<0x140>(v));  // row_mirror: the other half of 16
+  uint64_t r = 0;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, row * 16);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), row * 16);
+    r = topk_max(r, ((uint64_t)hi << 32) | lo);
+  }
+  return r;
+}
+
 template <int NPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
                                                    int64_t T, int E, int k, int32_t* __restrict__ idx,
@@ -28,41 +58,46 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + t * E;
-  float key[NPL], sc[NPL];
+  uint64_t key[NPL];
+  float sc[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
       const float s = 1.f / (1.f + expf(-row[e]));
       float v = s + bias[e];
-      // NaN and -inf rank below every real expert but above padding / retired ones.
       v = (v == v) ? fmaxf(v, -FLT_MAX) : -FLT_MAX;
-      key[i] = v;
+      uint32_t b = __float_as_uint(v);
+      b = b == 0x80000000u ? 0u : b;  // -0 ranks as +0 (equal scores)
+      const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+      key[i] = ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)e;
       sc[i] = s;
     } else {
-      key[i] = -INFINITY;
+      key[i] = 0;
       sc[i] = 0.f;
     }
   }
   int my_e = 0;
   float my_s = 0.f, ssum = 0.f;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY, bs = 0.f;
-    int be = INT_MAX;
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) best = topk_max(best, key[i]);
+    best = topk_wave_max(best);
+    const int be = (int)~(uint32_t)best;  // uniform across the wave
+    const int wl = be & 63, wi = be >> 6;
+    float s_w = 0.f;
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
-      if (key[i] > bv) { bv = key[i]; be = lane + 64 * i; bs = sc[i]; }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oe = __shfl_xor(be, o);
-      const float os = __shfl_xor(bs, o);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; bs = os; }
+      if (i == wi) {
+        s_w = sc[i];
+        if (lane == wl) key[i] = 0;
+      }
+    const float bs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_w), wl));
+    if (lane == j) {
+      my_e = be;
+      my_s = bs;
     }
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-      if (lane + 64 * i == be) key[i] = -INFINITY;
-    if (lane == j) { my_e = be; my_s = bs; }
     ssum += bs;
   }
   if (lane < k) {

@@ -447,3 +447,35 @@ def test_quantize_1x128_rejects(dev):
         lmoe.quantize_1x128(x[:, :200].contiguous())
     q, sc = lmoe.quantize_1x128(x[:0])
     assert q.shape == (0, 256) and sc.shape == (2, 0)
+
+
+@pytest.mark.gpu
+def test_topk_exact_ties_and_infinite_bias(dev):
+    """Identical router rows give every expert the same logit, so the biased
+    scores tie exactly wherever the bias does: the selection must run by bias
+    descending, then expert index ascending, with -inf biases last, and every
+    selected weight is 1/k.  Checked against the oracle's selection rule
+    (a library sort on (-score, index)) applied to the biases alone."""
+    cfg = get_config("small_bf16")
+    note(f"[top-k ties] {cfg.name}")
+    t, g = make_case(cfg, dev)
+    E, k = cfg.E, cfg.k
+    g = dict(g)
+    g["w_router"] = g["w_router"][:1].expand(E, -1).contiguous()
+    # two experts at the top level, four tied at the next, the rest lower or -inf
+    levels = np.full(E, -0.5)
+    levels[[7, 3]] = 0.25
+    levels[[20, 9, 1, 5]] = 0.0
+    levels[[0, 2, 4, 6, 11]] = -np.inf
+    g["b_router"] = torch.tensor(levels, dtype=torch.float32, device=dev)
+    sh, w = _weights(cfg, g)
+    logits = lmoe.router_logits(sh, w, g["x"])
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    assert (lg == lg[:, :1]).all(), "identical router rows give identical logits"
+    idx, tw, _ = lmoe.route(sh, w, g["x"])
+    torch.cuda.synchronize()
+    want, _ = O.select_topk(np.broadcast_to(levels, (cfg.T, E)).astype(np.float64), k)
+    assert k == 4 and list(want[0]) == [3, 7, 1, 5]
+    np.testing.assert_array_equal(idx.cpu().numpy(), want)
+    np.testing.assert_allclose(tw.cpu().numpy(), 1.0 / k, rtol=1e-6)
