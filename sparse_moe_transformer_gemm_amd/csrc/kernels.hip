@@ -242,6 +242,70 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__
   if (bt_b > 0) write_tiles(e, E, c, bt_b, tiles_b, cnt_b, lds);
 }
 
+// Permute and tile list of a batch of at most kPermTokens tokens in one
+// work-group (decode-sized batches): the same marks, ranks, scans and tile
+// entries as perm_count + perm_scan + perm_scatter + tiles_kernel with a
+// single token group, in one launch instead of four.
+__global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __restrict__ idx, int64_t T, int E, int k,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
+                                                             int bt, int4* __restrict__ tiles,
+                                                             int32_t* __restrict__ cnt) {
+  extern __shared__ unsigned long long mask[];  // E x 4 words: tokens 64 w .. 64 w + 63 of expert e at e * 4 + w
+  __shared__ int soff[1024];
+  __shared__ int lds[1024 / 64 + 1];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * 4; i += 1024) mask[i] = 0ull;
+  __syncthreads();
+  const bool tok = tid < kPermTokens && tid < T;
+  const int w = tid >> 6;
+  const unsigned long long bit = 1ull << (tid & 63);
+  uint64_t dup = 0;
+  if (tok) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(int64_t)tid * k + j];
+      if (e < 0 || e >= E) { dup |= 1ull << j; continue; }
+      const unsigned long long old = atomicOr(&mask[e * 4 + w], bit);
+      if (old & bit) dup |= 1ull << j;  // repeat of an expert already listed for this token
+    }
+  }
+  __syncthreads();
+  // expert tid: its count, then the exclusive scan over experts
+  const int c = tid < E ? __popcll(mask[tid * 4]) + __popcll(mask[tid * 4 + 1]) + __popcll(mask[tid * 4 + 2]) +
+                              __popcll(mask[tid * 4 + 3])
+                        : 0;
+  int total;
+  const int ex = block_exclusive_scan<1024>(c, lds, &total);
+  if (tid < E) {
+    offsets[tid] = ex;
+    soff[tid] = ex;
+  }
+  if (tid == 0) offsets[E] = total;
+  __syncthreads();
+  if (tok) {
+    const unsigned long long below = bit - 1ull;
+    for (int j = 0; j < k; ++j) {
+      const int64_t a = (int64_t)tid * k + j;
+      if (dup >> j & 1ull) { pos[a] = -1; continue; }
+      const int e = idx[a];
+      int rank = __popcll(mask[e * 4 + w] & below);
+      for (int q = 0; q < w; ++q) rank += __popcll(mask[e * 4 + q]);
+      const int dst = soff[e] + rank;
+      sorted[dst] = (int32_t)a;
+      pos[a] = dst;
+    }
+  }
+  write_tiles(tid, E, c, bt, tiles, cnt, lds);
+}
+
+hipError_t launch_permute_small(const int32_t* idx, int64_t T, int E, int k, int32_t* offsets, int32_t* sorted,
+                                int32_t* pos, int bt, int4* tiles, int32_t* cnt, hipStream_t st) {
+  const size_t lds = (size_t)E * 4 * sizeof(unsigned long long);
+  hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), lds, st, idx, T, E, k, offsets, sorted, pos, bt,
+                     tiles, cnt);
+  return hipGetLastError();
+}
+
 hipError_t launch_tiles(const int32_t* offsets, int E, int bt_a, int4* tiles_a, int32_t* cnt_a, int bt_b,
                         int4* tiles_b, int32_t* cnt_b, hipStream_t st) {
   hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(1024), 0, st, offsets, E, bt_a, tiles_a, cnt_a, bt_b, tiles_b,

@@ -15,6 +15,11 @@ hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E,
 hipError_t launch_permute(const int32_t* idx, int64_t T, int E, int k, int32_t* bcounts, int32_t* offsets,
                           int32_t* sorted, int32_t* pos, hipStream_t st);
 
+// launch_permute and launch_tiles (one list, token-tile height bt) in one
+// work-group, for T <= kPermTokens and E <= 1024; the same results.
+hipError_t launch_permute_small(const int32_t* idx, int64_t T, int E, int k, int32_t* offsets, int32_t* sorted,
+                                int32_t* pos, int bt, int4* tiles, int32_t* cnt, hipStream_t st);
+
 // Tile lists of the expert GEMMs for token-tile heights bt_a and bt_b (0: skip b).
 hipError_t launch_tiles(const int32_t* offsets, int E, int bt_a, int4* tiles_a, int32_t* cnt_a, int bt_b,
                         int4* tiles_b, int32_t* cnt_b, hipStream_t st);

@@ -819,11 +819,17 @@ lmoe_status lmoe_forward(const lmoe_shape* sh, const lmoe_weights* w, const void
   if (lmoe_status s = record(ev, 1, c.st)) return s;
   LMOE_HIP(launch_topk(logits, w->b_router, sh->T, sh->E, sh->k, idx, tw, c.st), "top-k");
   if (lmoe_status s = record(ev, 2, c.st)) return s;
-  LMOE_HIP(launch_permute(idx, sh->T, sh->E, sh->k, at<int32_t>(ws, pl.bcounts), offsets, sorted, pos, c.st),
-           "permute");
-  LMOE_HIP(launch_tiles(offsets, sh->E, expert_bt(sh), at<int4>(ws, pl.tiles_a), at<int32_t>(ws, pl.tcount), 0,
-                        nullptr, nullptr, c.st),
-           "tile list");
+  if (sh->T <= kPermTokens) {
+    LMOE_HIP(launch_permute_small(idx, sh->T, sh->E, sh->k, offsets, sorted, pos, expert_bt(sh),
+                                  at<int4>(ws, pl.tiles_a), at<int32_t>(ws, pl.tcount), c.st),
+             "permute + tile list");
+  } else {
+    LMOE_HIP(launch_permute(idx, sh->T, sh->E, sh->k, at<int32_t>(ws, pl.bcounts), offsets, sorted, pos, c.st),
+             "permute");
+    LMOE_HIP(launch_tiles(offsets, sh->E, expert_bt(sh), at<int4>(ws, pl.tiles_a), at<int32_t>(ws, pl.tcount), 0,
+                          nullptr, nullptr, c.st),
+             "tile list");
+  }
   if (lmoe_status s = record(ev, 3, c.st)) return s;
   const void* zin = z ? z : x;
   const int4* tiles = at<int4>(ws, pl.tiles_a);
