@@ -56,11 +56,13 @@ def test_forward_small(dev, name):
         assert np.abs(forced["z"] @ O.decode(inp["w_gate"][0], "f32").T).max() > 300
 
 
-@pytest.mark.parametrize("name,T", [("small_bf16", 20), ("small_bf16", 300), ("small_bf16", 700),
+@pytest.mark.parametrize("name,T", [("small_bf16", 20), ("small_bf16", 256), ("small_bf16", 257),
+                                    ("small_bf16", 300), ("small_bf16", 700),
                                     ("small_bf16", 2000), ("small_fp8", 700), ("small_fp8", 2000),
                                     ("small_w8a8", 20), ("small_w8a8", 2000)])
 def test_forward_tile_variants(dev, name, T):
-    """Token counts that select each kernel tile: thin / dense x- and up-GEMMs,
+    """Token counts that select each kernel tile: thin / dense x- and up-GEMMs
+    (and the one-group / multi-group permute) on either side of T = 256,
     small / mid / big expert token tiles (experts with 1-3, ~50, ~330 rows);
     with e4m3 expert weights, the register-staged tiles at T=300 and the
     LDS-DMA tiles that widen codes at the fragment load from T=700 on; W8A8
