@@ -29,8 +29,9 @@ Readings taken where the pages are silent (each is a documented choice):
     weight 1 and are added after the up-projection;
   * no capacity limit (no token is dropped), no biases in the linears, and
     the residual add is outside the layer;
-  * W8A8: the routed experts' activations, as stored in the activation dtype,
-    are quantised per row per 128 columns to e4m3fn (scale amax / 448);
+  * W8A8: the routed experts' activations (z, and each expert's SiTU-GLU
+    output), as the layer computes them, are quantised per row per 128
+    columns to e4m3fn (scale amax / 448, the decisions taken in fp32);
   * Quantile Balancing: expert e's threshold is the (1 - k/E) quantile of its
     batch scores (linear interpolation), and its bias is minus that;
   * backward: the gradient of sum(y * dy); the selection and its bias carry
@@ -159,21 +160,13 @@ def bf16_round(v):
     return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
 
 
-def round_to_act(v, act):
-    """An activation as the layer's activation dtype holds it."""
-    if act == "bf16":
-        return bf16_round(v)
-    if act == "f32":
-        return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
-    return np.asarray(v, dtype=np.float64)
-
-
-def fp8_activations(v, act="f64"):
-    """The values a W8A8 expert GEMM multiplies: the activation as stored in
-    the layer's activation dtype, quantised 1x128, decoded.  (The quantiser
-    reads the stored tensor, so its code decisions are taken on the stored
-    values.)"""
-    return dequant_rows(*quantize_1x128(round_to_act(v, act)))
+def fp8_activations(v):
+    """The values a W8A8 expert GEMM multiplies: the activation as the layer
+    computes it, quantised 1x128 (code decisions in fp32, quantize_1x128),
+    decoded.  No intermediate storage rounding is modelled: the pages name
+    only the BF16/FP8 dynamic-range problem (P3 merged summary), so the
+    quantiser reads the exact activation."""
+    return dequant_rows(*quantize_1x128(v))
 
 
 def matrix(stack, scales, idx, tag):
@@ -323,14 +316,13 @@ def permute(idx, E):
     return offsets, sorted_, pos
 
 
-def expert_ffn(zrows, wg, wv, wo, c, a8=False, act="f64"):
+def expert_ffn(zrows, wg, wv, wo, c, a8=False):
     """One routed expert on its latent rows: gated FFN with gate and value
     branches (P2 stabilizer passage) and the SiTU-GLU activation.  With a8
-    (W8A8) the SiTU-GLU output, stored in the act dtype, is quantised 1x128
-    before the down GEMM; the caller passes rows already quantised for the
-    gate/value GEMM."""
+    (W8A8) the SiTU-GLU output is quantised 1x128 before the down GEMM; the
+    caller passes rows already quantised for the gate/value GEMM."""
     a = situ_glu(zrows @ wg.T, zrows @ wv.T, c)
-    return a, (fp8_activations(a, act) if a8 else a) @ wo.T
+    return a, (fp8_activations(a) if a8 else a) @ wo.T
 
 
 def combine(O, pos, w):
@@ -374,8 +366,7 @@ def forward(inp, spec, forced_idx=None, forced_tol=1e-3):
     s_out, gamma, w_up, ws_gate, ws_value, ws_out, ss_gate, ss_value, ss_out
     (expert stacks may be any indexable over experts).  `spec` gives act,
     w_expert, k, cap, eps and optionally a8 (W8A8 routed experts: their
-    activations, as stored in the act dtype, quantised 1x128 to e4m3fn, see
-    quantize_1x128).  Returns
+    activations quantised 1x128 to e4m3fn, see fp8_activations).  Returns
     every intermediate as float64/int64 (A before any quantisation).
 
     Steps: route on x; z = latent down-projection of x; tokens grouped by
@@ -403,7 +394,7 @@ def forward(inp, spec, forced_idx=None, forced_tol=1e-3):
     z = latent_down(x, w_down)
     L = z.shape[1]
     # W8A8: each token's latent row is quantised once, whatever expert reads it
-    zx = fp8_activations(z, act) if a8 else z
+    zx = fp8_activations(z) if a8 else z
     offsets, sorted_, pos = permute(idx, E)
     I = None
     A = None
@@ -416,7 +407,7 @@ def forward(inp, spec, forced_idx=None, forced_tol=1e-3):
         wg = matrix(inp["w_gate"], inp.get("s_gate"), e, wt)
         wv = matrix(inp["w_value"], inp.get("s_value"), e, wt)
         wo = matrix(inp["w_out"], inp.get("s_out"), e, wt)
-        a, o = expert_ffn(zx[toks], wg, wv, wo, c, a8, act)
+        a, o = expert_ffn(zx[toks], wg, wv, wo, c, a8)
         if A is None:
             I = a.shape[1]
             A = np.zeros((T * k, I))

@@ -550,37 +550,30 @@ def pin_bf16_round():
     assert np.array_equal(O.bf16_round(v.astype(np.float64)), want)
     ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 1 + 2.0 ** -8 + 2.0 ** -40])
     assert list(O.bf16_round(ties)) == [1.0, 1 + 2.0 ** -6, -1.0, 1 + 2.0 ** -7]
-    assert O.round_to_act(np.array([1 + 2.0 ** -30]), "f32")[0] == 1.0
-    assert O.round_to_act(np.array([1 + 2.0 ** -30]), "f64")[0] == 1 + 2.0 ** -30
 
 
-def pin_a8_quantises_the_stored_activation():
-    """A bf16 layer's W8A8 path quantises z as the bf16 tensor holds it: the
-    quantiser applied to z itself and to its bf16 rounding differ on some
-    blocks of this layer, and the forward follows the rounded one."""
+def pin_a8_quantises_the_exact_activation():
+    """W8A8 quantises the routed experts' inputs as the layer computes them:
+    z = x W_dn^T and the SiTU-GLU output, unrounded.  One expert, W_o = I,
+    identity up-projection, no shared expert: the layer is RMSNorm of the
+    quantised SiTU-GLU output of the quantised z, written here with numpy and
+    the pinned quantiser.  A copy rounded to bf16 before quantising takes
+    other codes on this layer, so that reading would fail here."""
     inp, spec = _a8_layer(87, T=6, E=1, k=1, S=0)
-    inp["w_down"] = inp["w_up"] = None
+    inp["w_up"] = None
     inp["w_out"] = np.eye(128)[None]
-    x = inp["x"] + 2.0 ** -9 * np.sign(inp["x"])  # values near bf16 rounding ties
-    inp["x"] = x
-    spec = dict(spec, act="bf16")
-    inp_bf = dict(inp, x=O.bf16_round(x))
-    to_bits = lambda a: (torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
-                         .astype(np.uint16))
-    got = O.forward(dict(inp, x=to_bits(O.bf16_round(x))), spec)["y"]
-    ref = O.forward(dict(inp_bf, x=to_bits(inp_bf["x"])), spec)["y"]
-    close(got, ref, rtol=0, atol=0)
-    zq_direct = O.dequant_rows(*O.quantize_1x128(x))
-    zq_stored = O.dequant_rows(*O.quantize_1x128(O.bf16_round(x)))
-    assert not np.array_equal(zq_direct, zq_stored)
-    g = zq_stored @ inp["w_gate"][0].T
-    vv = zq_stored @ inp["w_value"][0].T
-    capg, capv = 100 * np.tanh(g / 100), 100 * np.tanh(vv / 100)
-    a = O.bf16_round(capg / (1 + np.exp(-capg)) * capv)
-    aq = O.dequant_rows(*O.quantize_1x128(a))
     gamma = inp["gamma"].astype(np.float64)
+    z = inp["x"] @ inp["w_down"].T
+    zq = O.dequant_rows(*O.quantize_1x128(z))
+    g = zq @ inp["w_gate"][0].T
+    vv = zq @ inp["w_value"][0].T
+    capg, capv = 100 * np.tanh(g / 100), 100 * np.tanh(vv / 100)
+    a = capg / (1 + np.exp(-capg)) * capv
+    aq = O.dequant_rows(*O.quantize_1x128(a))
     want = gamma * aq / np.sqrt(np.mean(aq * aq, axis=1, keepdims=True) + spec["eps"])
-    close(got, want, rtol=1e-10, atol=1e-12)
+    close(O.forward(inp, spec)["y"], want, rtol=1e-10, atol=1e-12)
+    assert not np.array_equal(zq, O.dequant_rows(*O.quantize_1x128(O.bf16_round(z))))
+    assert not np.array_equal(aq, O.dequant_rows(*O.quantize_1x128(O.bf16_round(a))))
 
 
 def _a8_layer(seed, T=7, **kw):
@@ -856,15 +849,15 @@ def _mut_quantize_e4m3_max_240(v):
     return O.e4m3fn_encode(b / scale[:, :, None]).reshape(R, C), scale
 
 
-def _mut_fp8_activations_skipped(v, act="f64"):
+def _mut_fp8_activations_skipped(v):
     return np.asarray(v, dtype=np.float64)
 
 
-def _mut_fp8_activations_unrounded(v, act="f64"):
-    return O.dequant_rows(*O.quantize_1x128(v))
+def _mut_fp8_activations_rounded_bf16(v):
+    return O.dequant_rows(*O.quantize_1x128(O.bf16_round(v)))
 
 
-def _mut_expert_ffn_a_not_quantised(zrows, wg, wv, wo, c, a8=False, act="f64"):
+def _mut_expert_ffn_a_not_quantised(zrows, wg, wv, wo, c, a8=False):
     a = O.situ_glu(zrows @ wg.T, zrows @ wv.T, c)
     return a, a @ wo.T
 
@@ -911,7 +904,7 @@ MUTANTS = {
     "route_grad": [_mut_route_grad_unrenormalised],
     "e4m3fn_encode": [_mut_encode_truncates],
     "quantize_1x128": [_mut_quantize_per_row, _mut_quantize_e4m3_max_240],
-    "fp8_activations": [_mut_fp8_activations_skipped, _mut_fp8_activations_unrounded],
+    "fp8_activations": [_mut_fp8_activations_skipped, _mut_fp8_activations_rounded_bf16],
     "bf16_round": [_mut_bf16_round_truncates],
     "expert_ffn": [_mut_expert_ffn_a_not_quantised],
     "situ_glu": [_mut_value_uncapped, _mut_gate_value_swapped],
