@@ -45,8 +45,11 @@
  *     LMOE_EWORKSPACE) and launch failures (LMOE_EHIP).  A fault inside a kernel
  *     surfaces at the caller's next synchronisation.  lmoe_last_error() returns a
  *     message for the calling thread's last failure.  No C++ exception crosses
- *     the ABI.  The library holds no mutable global state: calls on different
- *     streams are independent if their workspaces differ.
+ *     the ABI.  Per call the library keeps no state outside the caller's
+ *     workspace: calls on different streams are independent if their
+ *     workspaces differ.  Process-wide it caches, once per device, host-side
+ *     facts (the compute-unit count, kernel launch attributes), each written
+ *     once under a once-flag.
  */
 #ifndef LMOE_H
 #define LMOE_H
@@ -95,7 +98,9 @@ typedef struct {
   int32_t a8;             /* 0: the routed experts multiply act-dtype activations
                              (W8A16 with F8E4M3 weights).  1: W8A8 -- z and the
                              SiTU-GLU output are quantised per token per 128
-                             columns to e4m3fn (see lmoe_quantize_1x128) and the
+                             columns to e4m3fn (see lmoe_quantize_1x128), from
+                             their fp32 values as the GEMMs accumulate them
+                             (lmoe_expert_gemm: from z as given), and the
                              routed expert GEMMs multiply e4m3 by e4m3, with fp32
                              accumulation and the block scales applied once per
                              128 columns.  Needs act BF16 and w_expert F8E4M3

@@ -34,6 +34,7 @@ struct TileCfg {
   static constexpr int LDS = 2 * (BF + BT) * kPitch;
   static constexpr bool kDma = false;
   static constexpr int kKind = 1;
+  static constexpr int XF8 = 0;  // tokens are never e4m3 here
   static_assert(FW % 64 == 0, "a wave covers whole gate/value pairs");
   static_assert(TW % 32 == 0 && CW >= 1 && CX >= 1, "tile shape");
   static_assert((BF * 8) % NT == 0 && (BT * 8) % NT == 0, "chunk split");
@@ -269,6 +270,7 @@ struct ExpertTiles {
 
 // RAW = 1: the epilogue stores the gate and value pre-activations (fp32,
 // graw / vraw [T*k, I] in assignment order) instead of their SiTU-GLU.
+// RAW = 2: the SiTU-GLU output is stored in fp32 (W8A8: the quantiser's input).
 template <class Cfg, typename CT, int RAW = 0>
 struct ExpertGVProb {
   ExpertTiles<Cfg> et;
@@ -279,8 +281,8 @@ struct ExpertGVProb {
   const char* wv;
   const float* sg;    // [E, I/128, L/128]
   const float* sv;
-  char* act;          // [T*k, I]
-  float* graw;        // RAW: [T*k, I]
+  char* act;          // [T*k, I] act dtype (fp32 with RAW = 2)
+  float* graw;        // RAW = 1: [T*k, I]
   float* vraw;
   const char* wpk;    // packed gate/value blocks (see lmoe_pack_experts) or NULL
   const float* xs;    // W8A8: z block scales in expert order, [L/128, ldxs]
@@ -687,7 +689,7 @@ __device__ __forceinline__ void ExpertGVProb<Cfg, CT, RAW>::epilogue(const State
                                                                      int lane) const {
   for_glu<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int ul, int tl) __attribute__((always_inline)) {
     if (tl < st.rows) {
-      if constexpr (RAW) {
+      if constexpr (RAW == 1) {
         float gv[4], vv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -701,8 +703,9 @@ __device__ __forceinline__ void ExpertGVProb<Cfg, CT, RAW>::epilogue(const State
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = situ_glu(acc[i][j][4 * g + r], acc[i + 1][j][4 * g + r], cap, inv_cap);
-        CT* row = reinterpret_cast<CT*>(act) + (int64_t)(st.m0 + tl) * I;
-        store4<CT>(row, st.ft * (Cfg::BF / 2) + ul, v, I, true);
+        typedef std::conditional_t<RAW == 2, float, CT> OT;
+        OT* row = reinterpret_cast<OT*>(act) + (int64_t)(st.m0 + tl) * I;
+        store4<OT>(row, st.ft * (Cfg::BF / 2) + ul, v, I, true);
       }
     }
   });

@@ -41,6 +41,7 @@ struct Tile2 {
   static constexpr int LDS = STAGES * STAGE_BYTES;
   static constexpr bool kDma = true;
   static constexpr int kKind = 2;
+  static constexpr int XF8 = 0;  // tokens are never e4m3 here
   static_assert(FW % 64 == 0 && TW % 32 == 0, "wave tile");
   static_assert((QW + QX) % NW == 0, "DMA instructions split evenly over the waves");
   static_assert(STAGES >= 2 && NQ * (STAGES - 2) <= 63, "vmcnt range");

@@ -539,9 +539,27 @@ hipError_t launch_quantile_bias(const float* logits, int64_t T, int E, int k, ui
 // rounded fp32 division, then the hardware conversion, which rounds to
 // nearest even.  Every |x / scale| <= 448 up to one rounding of the quotient,
 // which the conversion rounds back to 448.  Sixteen lanes share one block,
-// eight bf16 each: one 16-byte load and one 8-byte store per lane.
+// eight values each (bf16: one 16-byte load; fp32: two), one 8-byte store.
+// The fp32 form reads the layer's own activations as the GEMMs accumulated
+// them, so the code decisions see no intermediate rounding.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __restrict__ x, int64_t R, int C,
+__device__ __forceinline__ void load8(const uint16_t* p, float (&f)[8]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&f)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  f[0] = a.x, f[1] = a.y, f[2] = a.z, f[3] = a.w, f[4] = b.x, f[5] = b.y, f[6] = b.z, f[7] = b.w;
+}
+
+template <typename In>
+__global__ __launch_bounds__(256) void quant_1x128_kernel(const In* __restrict__ x, int64_t R, int C,
                                                           uint8_t* __restrict__ q, float* __restrict__ sc) {
   const int nb = C >> 7;
   const int64_t unit = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (row, block)
@@ -550,14 +568,8 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __rest
   const int b = (int)(unit - r * nb);
   const int sub = threadIdx.x & 15;
   const int64_t off = r * C + b * 128 + sub * 8;
-  const uint4 v = *reinterpret_cast<const uint4*>(x + off);
-  const unsigned w[4] = {v.x, v.y, v.z, v.w};
   float f[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
+  load8(x + off, f);
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
@@ -571,18 +583,20 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __rest
   *reinterpret_cast<uint2*>(q + off) = uint2{(unsigned)lo, (unsigned)hi};
   if (sub == 0) sc[(int64_t)b * R + r] = s;
 }
-
-hipError_t launch_quant_1x128(const void* x, int64_t R, int C, void* q, float* sc, hipStream_t st) {
+hipError_t launch_quant_1x128(const void* x, bool x_f32, int64_t R, int C, void* q, float* sc, hipStream_t st) {
   const int64_t units = R * (C / 128);
   if (units == 0) return hipSuccess;
   const int64_t blocks = (units + 15) / 16;
   if (blocks > INT_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quant_1x128_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(x), R, C, static_cast<uint8_t*>(q), sc);
+  if (x_f32)
+    hipLaunchKernelGGL(quant_1x128_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<const float*>(x), R, C, static_cast<uint8_t*>(q), sc);
+  else
+    hipLaunchKernelGGL(quant_1x128_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(x), R, C, static_cast<uint8_t*>(q), sc);
   return hipGetLastError();
 }
 
-// Row scales in expert order: out[b * tk + a] = s_tok[b * T + sorted[a] / k].
 __global__ __launch_bounds__(256) void gather_scales_kernel(const float* __restrict__ s_tok, int64_t T, int nb,
                                                             const int32_t* __restrict__ sorted, int64_t tk, int k,
                                                             float* __restrict__ out) {

@@ -32,10 +32,10 @@ hipError_t launch_combine_norm(bool bf16, const void* O, const int32_t* pos, con
 hipError_t launch_quantile_bias(const float* logits, int64_t T, int E, int k, uint32_t* keys, float* bias,
                                 hipStream_t st);
 
-// W8A8 activations: bf16 x[R, C] (C a multiple of 128, row stride C) ->
-// e4m3fn codes q[R, C] and fp32 scales sc[C/128, R] (scale = amax / 448 per
-// row per 128 columns; code = e4m3fn(x / scale)).
-hipError_t launch_quant_1x128(const void* x, int64_t R, int C, void* q, float* sc, hipStream_t st);
+// W8A8 activations: x[R, C] (bf16, or fp32 when x_f32; C a multiple of 128,
+// row stride C) -> e4m3fn codes q[R, C] and fp32 scales sc[C/128, R]
+// (scale = amax / 448 per row per 128 columns; code = e4m3fn(x / scale)).
+hipError_t launch_quant_1x128(const void* x, bool x_f32, int64_t R, int C, void* q, float* sc, hipStream_t st);
 
 // out[b, a] = s_tok[b, sorted[a] / k] for b < nb, a < T * k (row scales of
 // the token rows in expert order).

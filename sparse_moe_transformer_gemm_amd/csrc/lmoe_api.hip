@@ -154,7 +154,8 @@ int64_t max_tiles(const lmoe_shape* sh, int bt) {
 
 struct Plan {
   size_t logits, z, hs, n, idx, w, bcounts, offsets, sorted, pos, tiles_a, tiles_b, tcount, act, out;
-  size_t zq, zs_tok, zs, aq, as;  // W8A8 only: e4m3 z, its scales by token and in expert order; e4m3 act, scales
+  size_t zf, zq, zs_tok, zs, aq, as;  // W8A8 only: fp32 z; e4m3 z, its scales by token and in expert order;
+                                      // e4m3 act, its scales
   size_t shared_bf16;              // e4m3 shared experts decoded to bf16 (gate, value, out)
   size_t total;
 };
@@ -183,10 +184,11 @@ Plan plan(const lmoe_shape* sh) {
   p.tiles_a = take((size_t)max_tiles(sh, expert_bt(sh)) * 16);
   p.tiles_b = take(16);
   p.tcount = take(8);
-  p.act = take(tk * sh->I * es);
+  p.act = take(tk * sh->I * (sh->a8 ? 4 : es));  // W8A8: fp32 for the quantiser
   p.out = take(tk * sh->L * es);
   if (sh->w_expert == LMOE_F8E4M3 && sh->S > 0) p.shared_bf16 = take((size_t)3 * sh->S * sh->Is * sh->H * 2);
   if (sh->a8) {
+    p.zf = take(T * sh->L * 4);
     p.zq = take(T * sh->L);
     p.zs_tok = take(T * (sh->L / 128) * 4);
     p.zs = take(tk * (sh->L / 128) * 4);
@@ -213,21 +215,33 @@ lmoe_status check_ws(const lmoe_shape* sh, const void* ws, size_t ws_bytes) {
 // ---------------------------------------------------------------------------
 // GEMM launches.
 // ---------------------------------------------------------------------------
-// Work-groups of a persistent GEMM: one per compute unit (their LDS use
-// leaves room for one group per CU), a multiple of the XCD count.
+// Host-side values cached per device on first use (each entry written once,
+// under its own once_flag): the compute-unit count and the kernels' LDS
+// attribute.  Devices past kMaxDevices are queried on every call instead.
+constexpr int kMaxDevices = 64;
+int current_device() {
+  int d = -1;
+  return hipGetDevice(&d) == hipSuccess ? d : -1;
+}
+
+int cu_count(int dev) {
+  int cus = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
+}
+
+// Work-groups of a persistent GEMM: one per compute unit of the current
+// device (their LDS use leaves room for one group per CU), a multiple of the
+// XCD count.
 int persistent_grid() {
-  static std::once_flag once;
-  static int n = 0;
-  std::call_once(once, [] {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-      n = cus;
-    else
-      n = 256;
-    n = (n + kXcds - 1) / kXcds * kXcds;
-  });
-  return n;
+  static std::once_flag once[kMaxDevices];
+  static int n[kMaxDevices];
+  const int dev = current_device();
+  auto count = [](int d) { return (cu_count(d) + kXcds - 1) / kXcds * kXcds; };
+  if (dev < 0 || dev >= kMaxDevices) return count(dev);
+  std::call_once(once[dev], [&] { n[dev] = count(dev); });
+  return n[dev];
 }
 
 template <class Cfg, typename CT, class Prob>
@@ -240,13 +254,21 @@ hipError_t launch_gemm(const Prob& p, int64_t grid, hipStream_t st) {
   } else if constexpr (Cfg::kKind == 3) kern = gemm3_kernel<Cfg, Prob>;
   else if constexpr (Cfg::kKind == 2) kern = gemm2_kernel<Cfg, Prob>;
   else kern = gemm_kernel<Cfg, CT, Prob>;
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [&] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+  auto set_attr = [&] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                Cfg::LDS);
-  });
-  if (attr != hipSuccess) return attr;
+  };
+  static std::once_flag once[kMaxDevices];
+  static hipError_t attr[kMaxDevices];
+  const int dev = current_device();
+  hipError_t a;
+  if (dev < 0 || dev >= kMaxDevices) {
+    a = set_attr();
+  } else {
+    std::call_once(once[dev], [&] { attr[dev] = set_attr(); });
+    a = attr[dev];
+  }
+  if (a != hipSuccess) return a;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::LDS, st, p);
   return hipGetLastError();
 }
@@ -273,8 +295,10 @@ struct Ctx {
 
 // x-GEMM: any of router logits (fp32 [T, E]), latent z ([T, L]) and the shared
 // experts' SiTU-GLU activations (hs [T, S*Is]) from one pass over x.
+// z_f32: z is written in fp32 (the W8A8 quantiser's input) instead of the
+// act dtype.
 template <class Cfg, typename CT>
-hipError_t xgemm(const Ctx& c, const void* x, float* logits, void* z, void* hs) {
+hipError_t xgemm(const Ctx& c, const void* x, float* logits, void* z, void* hs, bool z_f32 = false) {
   const lmoe_shape* sh = c.sh;
   DenseXProb<Cfg, CT> p{};
   p.x = static_cast<const char*>(x);
@@ -302,7 +326,7 @@ hipError_t xgemm(const Ctx& c, const void* x, float* logits, void* z, void* hs) 
     s.out = static_cast<char*>(z);
     s.ldo = sh->L;
     s.rows = sh->L;
-    s.kind = EPI_STORE;
+    s.kind = z_f32 ? EPI_F32 : EPI_STORE;
     s.vec = 1;
     s.ft0 = ft;
     ft += (int)cdiv(sh->L, Cfg::BF);
@@ -371,12 +395,13 @@ hipError_t upgemm(const Ctx& c, const void* n, const void* hs, void* y) {
   return launch_gemm<Cfg, CT>(p, p.padded, c.st);
 }
 
-// xs: W8A8 row scales (z then holds e4m3 codes), [L/128, T*k] in expert order.
+// xs: W8A8 row scales (z then holds e4m3 codes), [L/128, T*k] in expert
+// order; act is then written in fp32.
 template <class Cfg, typename CT>
 hipError_t expert_gv(const Ctx& c, const void* z, const int32_t* offsets, const int32_t* sorted,
                      const int4* tiles, const int32_t* tcount, void* act, const float* xs = nullptr) {
   const lmoe_shape* sh = c.sh;
-  ExpertGVProb<Cfg, CT> p{};
+  ExpertGVProb<Cfg, CT, Cfg::XF8 ? 2 : 0> p{};
   p.et.offsets = offsets;
   p.et.tiles = tiles;
   p.et.tile_count = tcount;
@@ -451,23 +476,27 @@ hipError_t expert_gv_raw(const Ctx& c, const void* z, const int32_t* offsets, co
   return launch_gemm<Cfg, bf16>(p, pad8(max_tiles(sh, Cfg::BT) * p.et.nft), c.st);
 }
 
-// W8A8 gate/value: z (or x) quantised per token, its row scales put in expert
-// order, then the e4m3 x e4m3 GEMM with the SiTU-GLU epilogue (bf16 act).
-hipError_t expert_gv_a8(const Ctx& c, const Plan& pl, void* ws, const void* z, const int32_t* offsets,
+// W8A8 gate/value: z (or x) quantised per token -- from fp32 when z_f32 --,
+// its row scales put in expert order, then the e4m3 x e4m3 GEMM with the
+// SiTU-GLU epilogue writing fp32 act.
+hipError_t expert_gv_a8(const Ctx& c, const Plan& pl, void* ws, const void* z, bool z_f32, const int32_t* offsets,
                         const int32_t* sorted, const int4* tiles, const int32_t* tcount, void* act) {
   const lmoe_shape* sh = c.sh;
-  hipError_t e = launch_quant_1x128(z, sh->T, sh->L, at<void>(ws, pl.zq), at<float>(ws, pl.zs_tok), c.st);
+  hipError_t e =
+      launch_quant_1x128(z, z_f32, sh->T, sh->L, at<void>(ws, pl.zq), at<float>(ws, pl.zs_tok), c.st);
   if (e != hipSuccess) return e;
   e = launch_gather_scales(at<float>(ws, pl.zs_tok), sh->T, sh->L / 128, sorted, sh->k, at<float>(ws, pl.zs), c.st);
   if (e != hipSuccess) return e;
   return expert_gv<T2ExpertGVA8, bf16>(c, at<void>(ws, pl.zq), offsets, sorted, tiles, tcount, act,
                                        at<float>(ws, pl.zs));
 }
-// W8A8 down: the SiTU-GLU output quantised per row, then the e4m3 x e4m3 GEMM.
+// W8A8 down: the fp32 SiTU-GLU output quantised per row, then the e4m3 x
+// e4m3 GEMM.
 hipError_t expert_down_a8(const Ctx& c, const Plan& pl, void* ws, const void* act, const int32_t* offsets,
                           const int4* tiles, const int32_t* tcount, void* out) {
   const lmoe_shape* sh = c.sh;
-  hipError_t e = launch_quant_1x128(act, sh->T * sh->k, sh->I, at<void>(ws, pl.aq), at<float>(ws, pl.as), c.st);
+  hipError_t e =
+      launch_quant_1x128(act, true, sh->T * sh->k, sh->I, at<void>(ws, pl.aq), at<float>(ws, pl.as), c.st);
   if (e != hipSuccess) return e;
   return expert_down<T2ExpertDnA8, bf16>(c, at<void>(ws, pl.aq), offsets, tiles, tcount, out, at<float>(ws, pl.as));
 }
@@ -511,12 +540,14 @@ hipError_t dense_view(const Ctx& c, const Plan& pl, void* ws, DenseView& v) {
 
 // Dispatch on (dtype, tile).
 template <typename CT>
-hipError_t xgemm_any(const Ctx& c, const void* x, float* logits, void* z, void* hs) {
+hipError_t xgemm_any(const Ctx& c, const void* x, float* logits, void* z, void* hs, bool z_f32 = false) {
   if constexpr (sizeof(CT) == 2) {
     if (!(hs && is_f8(c.sh)))
-      return dense_small(c.sh) ? xgemm<T2Thin, CT>(c, x, logits, z, hs) : xgemm<T2Dense, CT>(c, x, logits, z, hs);
+      return dense_small(c.sh) ? xgemm<T2Thin, CT>(c, x, logits, z, hs, z_f32)
+                               : xgemm<T2Dense, CT>(c, x, logits, z, hs, z_f32);
   }
-  return dense_small(c.sh) ? xgemm<CfgSmall, CT>(c, x, logits, z, hs) : xgemm<CfgBig, CT>(c, x, logits, z, hs);
+  return dense_small(c.sh) ? xgemm<CfgSmall, CT>(c, x, logits, z, hs, z_f32)
+                           : xgemm<CfgBig, CT>(c, x, logits, z, hs, z_f32);
 }
 template <typename CT>
 hipError_t upgemm_any(const Ctx& c, const void* n, const void* hs, void* y) {
@@ -746,7 +777,7 @@ lmoe_status lmoe_expert_gemm(const lmoe_shape* sh, const lmoe_weights* w, const 
   int32_t* tc = at<int32_t>(ws, pl.tcount);
   if (use_a8(sh)) {
     LMOE_HIP(launch_tiles(offsets, sh->E, expert_bt(sh), tiles, tc, 0, nullptr, nullptr, c.st), "tile list");
-    LMOE_HIP(expert_gv_a8(c, pl, ws, z, offsets, sorted, tiles, tc, act), "expert gate/value GEMM");
+    LMOE_HIP(expert_gv_a8(c, pl, ws, z, false, offsets, sorted, tiles, tc, act), "expert gate/value GEMM");
     LMOE_HIP(expert_down_a8(c, pl, ws, act, offsets, tiles, tc, expert_out), "expert down GEMM");
     return LMOE_OK;
   }
@@ -800,7 +831,9 @@ lmoe_status lmoe_forward(const lmoe_shape* sh, const lmoe_weights* w, const void
   const Plan pl = plan(sh);
   const bool bf = bf16_act(sh);
   float* logits = at<float>(ws, pl.logits);
-  void* z = w->w_down ? at<void>(ws, pl.z) : nullptr;
+  // W8A8: z goes to the quantiser in fp32
+  const bool zf = use_a8(sh) && w->w_down;
+  void* z = w->w_down ? at<void>(ws, zf ? pl.zf : pl.z) : nullptr;
   void* hs = sh->S > 0 ? at<void>(ws, pl.hs) : nullptr;
   void* n = at<void>(ws, pl.n);
   int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, pl.idx);
@@ -815,7 +848,7 @@ lmoe_status lmoe_forward(const lmoe_shape* sh, const lmoe_weights* w, const void
   DenseView dv;
   LMOE_HIP(dense_view(c, pl, ws, dv), "shared expert decode");
   const Ctx cd{&dv.sh, &dv.w, c.st};  // route and up GEMMs
-  LMOE_HIP(bf ? xgemm_any<bf16>(cd, x, logits, z, hs) : xgemm_any<float>(cd, x, logits, z, hs), "route GEMM");
+  LMOE_HIP(bf ? xgemm_any<bf16>(cd, x, logits, z, hs, zf) : xgemm_any<float>(cd, x, logits, z, hs), "route GEMM");
   if (lmoe_status s = record(ev, 1, c.st)) return s;
   LMOE_HIP(launch_topk(logits, w->b_router, sh->T, sh->E, sh->k, idx, tw, c.st), "top-k");
   if (lmoe_status s = record(ev, 2, c.st)) return s;
@@ -834,7 +867,7 @@ lmoe_status lmoe_forward(const lmoe_shape* sh, const lmoe_weights* w, const void
   const void* zin = z ? z : x;
   const int4* tiles = at<int4>(ws, pl.tiles_a);
   const int32_t* tc = at<int32_t>(ws, pl.tcount);
-  LMOE_HIP(use_a8(sh) ? expert_gv_a8(c, pl, ws, zin, offsets, sorted, tiles, tc, act)
+  LMOE_HIP(use_a8(sh) ? expert_gv_a8(c, pl, ws, zin, zf, offsets, sorted, tiles, tc, act)
            : bf      ? expert_gv_any<bf16>(c, zin, offsets, sorted, tiles, tc, act)
                      : expert_gv_any<float>(c, zin, offsets, sorted, tiles, tc, act),
            "expert gate/value GEMM");
@@ -890,7 +923,7 @@ lmoe_status lmoe_quantize_1x128(const void* x, int64_t R, int32_t C, void* q, fl
       (reinterpret_cast<uintptr_t>(scales) & 3))
     return fail(LMOE_EINVAL, "x must be 16-byte, q 8-byte and scales 4-byte aligned");
   if (R * (int64_t)(C / 128) > (int64_t)INT32_MAX * 16) return fail(LMOE_EUNSUPPORTED, "too many blocks");
-  LMOE_HIP(launch_quant_1x128(x, R, C, q, scales, static_cast<hipStream_t>(stream)), "1x128 quantisation");
+  LMOE_HIP(launch_quant_1x128(x, false, R, C, q, scales, static_cast<hipStream_t>(stream)), "1x128 quantisation");
   return LMOE_OK;
 }
 
