@@ -55,6 +55,10 @@ _LIST = [
     # Small bf16 / fp8 layers that span several tiles with ragged tails.
     LayerConfig("small_bf16", T=333, H=512, L=256, E=24, k=4, S=2, I=192, Is=128,
                 act="bf16", w_expert="bf16", seed=3),
+    # small_bf16 with x scaled so that the routed and the shared experts' gate
+    # and value pre-activations run far past the cap in the bf16 kernels.
+    LayerConfig("small_situ_stress_bf16", T=333, H=512, L=256, E=24, k=4, S=2, I=192, Is=128,
+                act="bf16", w_expert="bf16", seed=8, x_scale=4000.0),
     LayerConfig("small_fp8", T=301, H=512, L=256, E=20, k=4, S=2, I=256, Is=128,
                 act="bf16", w_expert="f8", seed=4),
     LayerConfig("small_w8a8", T=301, H=512, L=256, E=20, k=4, S=2, I=256, Is=128,

@@ -285,3 +285,4 @@ def test_backward_rejects_before_any_gpu_call(lib):
               None, None) == 2
     packed_only = fake_weights(sh, w_gate=None, w_value=None, w_out=None, packed=0x9000)
     assert bw(ctypes.byref(sh), ctypes.byref(packed_only), buf, buf, None, ctypes.byref(g), ws, need, None, None) == 1
+

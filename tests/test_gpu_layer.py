@@ -20,8 +20,18 @@ pytestmark = pytest.mark.gpu
 
 lmoe = pytest.importorskip("sparse_moe_transformer_gemm_amd.lmoe")
 
-SMALL = ["tiny_f32", "tiny_situ_stress", "small_bf16", "small_fp8", "small_w8a8", "small_identity_bf16",
-         "small_full_k"]
+SMALL = ["tiny_f32", "tiny_situ_stress", "small_bf16", "small_situ_stress_bf16", "small_fp8", "small_w8a8",
+         "small_identity_bf16", "small_full_k"]
+
+
+def _saturates(inp, cfg, z64=None):
+    """The largest |gate| pre-activation of the routed experts (on z64, or on
+    the layer's own z) and of the shared experts, in fp64."""
+    x = O.decode(inp["x"], cfg.act)
+    z = z64 if z64 is not None else (x if inp["w_down"] is None else x @ O.decode(inp["w_down"], cfg.act).T)
+    routed = np.abs(z @ O.decode(inp["w_gate"][0], cfg.w_expert).T).max()
+    shared = np.abs(x @ O.decode(inp["ws_gate"][0], cfg.act).T).max() if inp.get("ws_gate") is not None else 0.0
+    return routed, shared
 
 
 @pytest.fixture(scope="module")
@@ -51,14 +61,17 @@ def test_forward_small(dev, name):
     err = rowwise_rel_err(to_f64(y), forced["y"])
     note(f"    max row rel err {err:.3e} (tol {tol_of(cfg)})")
     assert err <= tol_of(cfg)
-    if name == "tiny_situ_stress":
-        # the stress input really drives gate and value past the cap
-        assert np.abs(forced["z"] @ O.decode(inp["w_gate"][0], "f32").T).max() > 300
+    if cfg.x_scale > 1:
+        # the stress input really drives the gate pre-activations past the cap
+        routed, shared = _saturates(inp, cfg)
+        note(f"    max |gate| pre-activation: routed {routed:.0f}, shared {shared:.0f} (cap {cfg.cap})")
+        assert routed > 3 * cfg.cap and shared > 3 * cfg.cap
 
 
 @pytest.mark.parametrize("name,T", [("small_bf16", 20), ("small_bf16", 256), ("small_bf16", 257),
                                     ("small_bf16", 300), ("small_bf16", 700),
-                                    ("small_bf16", 2000), ("small_fp8", 700), ("small_fp8", 2000),
+                                    ("small_bf16", 2000), ("small_situ_stress_bf16", 20),
+                                    ("small_situ_stress_bf16", 2000), ("small_fp8", 700), ("small_fp8", 2000),
                                     ("small_w8a8", 20), ("small_w8a8", 2000)])
 def test_forward_tile_variants(dev, name, T):
     """Token counts that select each kernel tile: thin / dense x- and up-GEMMs
@@ -165,26 +178,34 @@ def _oracle_experts(inp, cfg, z64, idx):
         wg = O.matrix(inp["w_gate"], inp.get("s_gate"), e, cfg.w_expert)
         wv = O.matrix(inp["w_value"], inp.get("s_value"), e, cfg.w_expert)
         wo = O.matrix(inp["w_out"], inp.get("s_out"), e, cfg.w_expert)
-        zx = O.fp8_activations(z64, cfg.act) if cfg.a8 else z64
-        out[lo:hi] = O.expert_ffn(zx[srt[lo:hi] // cfg.k], wg, wv, wo, cfg.cap, cfg.a8, cfg.act)[1]
+        zx = O.fp8_activations(z64) if cfg.a8 else z64
+        out[lo:hi] = O.expert_ffn(zx[srt[lo:hi] // cfg.k], wg, wv, wo, cfg.cap, cfg.a8)[1]
     return out, off, srt
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "tiny_situ_stress", "small_bf16", "small_fp8", "small_w8a8",
-                                  "small_full_k"])
-def test_expert_gemm(dev, name):
-    cfg = get_config(name)
-    note(f"[expert_gemm] {name}")
+@pytest.mark.parametrize("name,T", [("tiny_f32", None), ("tiny_situ_stress", None), ("small_bf16", None),
+                                    ("small_situ_stress_bf16", None), ("small_situ_stress_bf16", 2000),
+                                    ("small_fp8", None), ("small_w8a8", None), ("small_full_k", None)])
+def test_expert_gemm(dev, name, T):
+    """Latent rows scaled by 1000 where the config is a stress case: |gate| and
+    |value| then run far past the cap in the SiTU-GLU epilogue (T = 2000
+    reaches the 256-row persistent tiles)."""
+    cfg = get_config(name) if T is None else replace(get_config(name), T=T, name=f"{name}_T{T}")
+    note(f"[expert_gemm] {cfg.name}")
     t, g = make_case(cfg, dev)
     sh, w = _weights(cfg, g)
     inp = host_inputs(t)
     # latent rows: seeded, scaled like the stress case when it applies
     gen = torch.Generator().manual_seed(123)
-    z = torch.randn((cfg.T, cfg.L), generator=gen) * (300.0 if cfg.x_scale > 1 else 1.0)
+    z = torch.randn((cfg.T, cfg.L), generator=gen) * (1000.0 if cfg.x_scale > 1 else 1.0)
     z = z.to(g["x"].dtype)
     rng = np.random.default_rng(9)
     idx = np.stack([rng.choice(cfg.E, cfg.k, replace=False) for _ in range(cfg.T)]).astype(np.int64)
     ref, off, srt = _oracle_experts(inp, cfg, to_f64(z), idx)
+    if cfg.x_scale > 1:
+        routed, _ = _saturates(inp, cfg, to_f64(z))
+        note(f"    max |gate| pre-activation {routed:.0f} (cap {cfg.cap})")
+        assert routed > 3 * cfg.cap
     out = lmoe.expert_gemm(sh, w, z.to(dev), torch.from_numpy(off.astype(np.int32)).to(dev),
                            torch.from_numpy(srt.astype(np.int32)).to(dev))
     torch.cuda.synchronize()
