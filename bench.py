@@ -50,7 +50,9 @@ def parse():
     ap.add_argument("--workload", default="k3_t8192")
     ap.add_argument("--decode-workload", default="k3_decode_t64")
     ap.add_argument("--decode-steps", type=int, default=50)
-    ap.add_argument("--cpu-sample", type=int, default=48, help="tokens the oracle runs for cpu_baseline (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens the oracle runs for cpu_baseline (0: skip)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the secondary lines (Zipf-skewed router at T=16384, e4m3 expert weights at T=8192)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--pack", action="store_true",
                     help="pack the routed expert weights once (lmoe_pack_experts) and time the layer on them")
@@ -127,6 +129,58 @@ def measured_traffic(workload, kernel):
         return None
     k = t["kernels"][kernel]
     return k["fetch_bytes"] + k["write_bytes"]
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (amdsmi) from a host thread while the
+    layer runs; reports the samples' median, minimum and maximum in MHz."""
+
+    def __init__(self, period_s=0.01):
+        import threading
+        self.period, self.samples, self.error = period_s, [], None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read()
+        except Exception as e:  # no amdsmi or no permission: the field says why
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        info = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
+        for key in ("clk", "cur_clk"):
+            if key in info:
+                return float(info[key])
+        raise KeyError(f"no current clock among {sorted(info)}")
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.error is None:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"mhz_median": None, "error": self.error or "no samples"}
+        v = sorted(self.samples)
+        return {"mhz_median": v[len(v) // 2], "mhz_min": v[0], "mhz_max": v[-1], "samples": len(v),
+                "source": "amdsmi GFX clock, sampled every 10 ms during the layer loop"}
 
 
 def timed_loop(lmoe, sh, w, x, y, idx, tw, ws, steps, warmup, per_stage):
@@ -215,14 +269,18 @@ def main():
     tok_s = T / (ms * 1e-3)
 
     # dominant kernel: expert gate/value GEMM.  Algorithmic bytes per launch =
-    # gate+value weights of the touched experts + latent rows read once +
-    # SiTU-GLU activations written once.
+    # the gate and value weights of the touched experts (one expert's unit is
+    # 2 * I * L elements); the latent rows it reads and the SiTU-GLU
+    # activations it writes are intermediates, reported beside the roofline.
     es = 2 if cfg.act == "bf16" else 4
-    gv_bytes = lmoe.expert_bytes(sh, touched, "gv") + T * cfg.L * es + T * cfg.k * cfg.I * es
+    gv_bytes = lmoe.expert_bytes(sh, touched, "gv")
+    gv_inter = T * cfg.L * es + T * cfg.k * cfg.I * es
     gv_ms = stages["expert_gate_value"]
     gv_gbs = gv_bytes / (gv_ms * 1e-3) / 1e9
-    dn_bytes = lmoe.expert_bytes(sh, touched, "down") + T * cfg.k * cfg.I * es + T * cfg.k * cfg.L * es
+    dn_bytes = lmoe.expert_bytes(sh, touched, "down")
     layer_bytes = lmoe.expert_bytes(sh, touched) + lmoe.dense_bytes(sh, projections=proj) + 2 * T * cfg.H * es
+    with ClockSampler() as clk:
+        timed_loop(lmoe, sh, w, x, y, idx, tw, ws, max(50, a.steps), 0, per_stage=False)
 
     out = {
         "metric": METRIC,
@@ -257,10 +315,17 @@ def main():
             "frac": round(gv_gbs / PEAK_HBM_GBS, 4),
             "traffic": measured_traffic(cfg.name, "expert_gate_value"),
             "bytes_per_launch": gv_bytes,
+            "bytes_unit": "gate + value weights of one touched expert, 2*I*L*2 B",
+            "units_per_launch": touched,
             "avg_ms": round(gv_ms, 4),
+            "intermediate_bytes": gv_inter,
+            "intermediates": "latent rows read once (T*L) + SiTU-GLU activations written once (T*k*I), not in "
+                             "achieved",
         },
-        "expert_down": {"avg_ms": round(stages["expert_down"], 4),
-                        "gbs": round(dn_bytes / (stages["expert_down"] * 1e-3) / 1e9, 1)},
+        "expert_down": {"avg_ms": round(stages["expert_down"], 4), "weight_bytes": dn_bytes,
+                        "gbs": round(dn_bytes / (stages["expert_down"] * 1e-3) / 1e9, 1),
+                        "frac": round(dn_bytes / (stages["expert_down"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "gpu_clock": clk.summary(),
     }
 
     if not a.no_decode:
@@ -285,10 +350,59 @@ def main():
         }
         del dws
 
+    if not a.no_secondary:
+        out["secondary"] = secondary_lines(a, lmoe, dev, g)
+
     if a.cpu_sample > 0:
         out["cpu_baseline"], out["parity"] = cpu_baseline(cfg, g, idx, y, a.cpu_sample, dev)
 
     print(json.dumps(out), flush=True)
+
+
+def secondary_lines(a, lmoe, dev, g_bf16):
+    """Two more workloads of the same layer, timed like the headline: the
+    Zipf-skewed router at T=16384 (bf16 weights, bias b_e = r_e^-1.1) and e4m3
+    expert weights with 128x128 block scales at T=8192 (W8A16)."""
+    import torch
+
+    from synth import get_config, make_inputs
+    from synth.inputs import make_router_bias, make_x
+
+    res = {}
+    for name in ("k3_zipf_t16384", "k3_fp8_t8192"):
+        cfg = get_config(name)
+        print(f"# secondary: {name}", file=sys.stderr, flush=True)
+        if cfg.w_expert == "bf16":
+            g = dict(g_bf16)
+            g["b_router"] = make_router_bias(cfg, dev)
+        else:
+            g = make_inputs(cfg, device=dev, with_x=False)
+        x = make_x(cfg, dev)
+        sh = lmoe.shape_of(cfg)
+        w = lmoe.make_weights(sh, g)
+        T = cfg.T
+        y = torch.empty((T, cfg.H), dtype=x.dtype, device=dev)
+        idx = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
+        tw = torch.empty((T, cfg.k), dtype=torch.float32, device=dev)
+        ws = lmoe.alloc_workspace(sh, dev)
+        steps = max(5, a.steps // 2)
+        ms, _ = timed_loop(lmoe, sh, w, x, y, idx, tw, ws, steps, min(a.warmup, 3), per_stage=False)
+        _, stages = timed_loop(lmoe, sh, w, x, y, idx, tw, ws, steps, 1, per_stage=True)
+        counts = torch.bincount(idx.flatten().long(), minlength=cfg.E)
+        flops = lmoe.layer_flops(sh)
+        res[name] = {"T": T, "steps": steps, "ms_per_step": round(ms, 4),
+                     "tokens_per_s": round(T / (ms * 1e-3), 1),
+                     "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "mfma_peak_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "w_expert": cfg.w_expert, "bias": cfg.bias,
+                     "rows_per_expert": {"max": int(counts.max()), "min": int(counts.min()),
+                                         "mean": round(T * cfg.k / cfg.E, 1)},
+                     "stages_ms": {k: round(v, 4) for k, v in stages.items()}}
+        del ws, y, idx, tw, x, w
+        if cfg.w_expert != "bf16":
+            g.clear()
+        torch.cuda.empty_cache()
+    return res
 
 
 def bench_backward(a, lmoe, dev):
@@ -604,7 +718,30 @@ def cpu_baseline(cfg, g, idx, y, n, dev):
             "seconds": round(dt, 2)}
     parity = {"rows": len(rows), "max_row_rel_err": err, "tol": 6e-2 if cfg.w_expert == "f8" else 2e-2,
               "ok": err <= (6e-2 if cfg.w_expert == "f8" else 2e-2)}
+    parity["selection"] = selection_stats(cfg, g, idx)
     return base, parity
+
+
+def selection_stats(cfg, g, idx, gap=1e-3):
+    """The GPU's top-k against the oracle's fp64 routing on every token of the
+    batch (not timed): strict set mismatches over all tokens, the fraction of
+    near-tie tokens (oracle k-th minus (k+1)-th biased score below `gap`),
+    and the largest such gap among the mismatches."""
+    import numpy as np
+
+    from oracle import lmoe_oracle as O
+    from synth import raw_numpy
+
+    print(f"# oracle routing of all {cfg.T} tokens", file=sys.stderr, flush=True)
+    r = O.route(O.decode(raw_numpy(g["x"]), cfg.act), O.decode(raw_numpy(g["w_router"]), cfg.act),
+                raw_numpy(g["b_router"]).astype(np.float64), cfg.k)
+    got = np.sort(idx.cpu().numpy().astype(np.int64), axis=1)
+    want = np.sort(r["idx"], axis=1)
+    mism = (got != want).any(axis=1)
+    return {"tokens": int(cfg.T), "strict_mismatch": int(mism.sum()),
+            "near_tie_frac": round(float((r["gap"] < gap).mean()), 4),
+            "mismatch_outside_near_ties": int((mism & (r["gap"] >= gap)).sum()),
+            "max_gap_among_mismatches": float(r["gap"][mism].max()) if mism.any() else 0.0}
 
 
 if __name__ == "__main__":
