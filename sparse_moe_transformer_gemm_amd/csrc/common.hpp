@@ -56,19 +56,28 @@ __device__ __forceinline__ float situ_glu(float g, float v, float c, float inv_c
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+// Every address passed to these loads is wave-uniform by construction; the
+// compiler's divergence analysis does not always prove it, so the address is
+// taken from the first lane, which places it in scalar registers.
+__device__ __forceinline__ const int* su(const int* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const int*>(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ int sload1(const int* p) {
   int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(su(p)) : "memory");
   return v;
 }
 __device__ __forceinline__ i32x2 sload2(const int* p) {
   i32x2 v;
-  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(su(p)) : "memory");
   return v;
 }
 __device__ __forceinline__ i32x4 sload4(const int* p) {
   i32x4 v;
-  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(su(p)) : "memory");
   return v;
 }
 // Two uniform ints *a, *b in one round trip.
@@ -76,7 +85,7 @@ __device__ __forceinline__ i32x2 sload_pair(const int* a, const int* b) {
   int v0, v1;
   asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
                : "=&s"(v0), "=&s"(v1)
-               : "s"(a), "s"(b)
+               : "s"(su(a)), "s"(su(b))
                : "memory");
   i32x2 v = {v0, v1};
   return v;
@@ -89,8 +98,8 @@ __device__ __forceinline__ i32x8 sload_gather8(const int* p, const int (&idx)[8]
       "s_load_dword %3, %11, 0x0\n\ts_load_dword %4, %12, 0x0\n\ts_load_dword %5, %13, 0x0\n\t"
       "s_load_dword %6, %14, 0x0\n\ts_load_dword %7, %15, 0x0\n\ts_waitcnt lgkmcnt(0)"
       : "=&s"(v0), "=&s"(v1), "=&s"(v2), "=&s"(v3), "=&s"(v4), "=&s"(v5), "=&s"(v6), "=&s"(v7)
-      : "s"(p + idx[0]), "s"(p + idx[1]), "s"(p + idx[2]), "s"(p + idx[3]), "s"(p + idx[4]), "s"(p + idx[5]),
-        "s"(p + idx[6]), "s"(p + idx[7])
+      : "s"(su(p + idx[0])), "s"(su(p + idx[1])), "s"(su(p + idx[2])), "s"(su(p + idx[3])), "s"(su(p + idx[4])),
+        "s"(su(p + idx[5])), "s"(su(p + idx[6])), "s"(su(p + idx[7]))
       : "memory");
   i32x8 v = {v0, v1, v2, v3, v4, v5, v6, v7};
   return v;
