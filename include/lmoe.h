@@ -48,8 +48,9 @@
  *     the ABI.  Per call the library keeps no state outside the caller's
  *     workspace: calls on different streams are independent if their
  *     workspaces differ.  Process-wide it caches, once per device, host-side
- *     facts (the compute-unit count, kernel launch attributes), each written
- *     once under a once-flag.
+ *     facts (the compute-unit count, kernel launch attributes, the address of
+ *     lmoe_forward_noalloc's scratch), each written once under a once-flag or
+ *     a lock; lmoe_forward_noalloc shares one scratch array per device.
  */
 #ifndef LMOE_H
 #define LMOE_H
@@ -157,6 +158,23 @@ size_t lmoe_workspace_bytes(const lmoe_shape *shape);
 lmoe_status lmoe_forward(const lmoe_shape *shape, const lmoe_weights *w, const void *x, void *y,
                          int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                          void *stream, void *const *stage_events);
+
+/* The whole layer as lmoe_forward, for callers that cannot allocate device
+ * memory or hand over a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Scratch comes from a
+ * fixed array of LMOE_NOALLOC_SCRATCH_BYTES in the library's own device memory,
+ * one per device, held from the first use on a device until the process ends
+ * (at the K3 shape that covers up to about 350 tokens per call).  The call
+ * allocates and frees nothing.  Arguments, outputs and results are those of
+ * lmoe_forward (no stage events); LMOE_EWORKSPACE when
+ * lmoe_workspace_bytes(shape) exceeds the array, LMOE_EUNSUPPORTED on a
+ * device id of 64 or more.  Every call on one device shares that device's
+ * array and leaves its contents behind (nothing in it needs to start at
+ * zero): calls that overlap on one device -- on different streams, or from
+ * different threads without ordering -- race on it and must not be issued.  */
+#define LMOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+lmoe_status lmoe_forward_noalloc(const lmoe_shape *shape, const lmoe_weights *w, const void *x, void *y,
+                                 int32_t *topk_idx, float *topk_w, void *stream);
 
 /* Router and latent down-projection (P1 Technical Details; P2 MoE and Stable
  * LatentMoE passages).  One GEMM over x serves both: logits = x . W_r^T in fp32

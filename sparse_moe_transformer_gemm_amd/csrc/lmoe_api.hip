@@ -820,9 +820,13 @@ lmoe_status lmoe_up(const lmoe_shape* sh, const lmoe_weights* w, const void* n, 
   return LMOE_OK;
 }
 
-lmoe_status lmoe_forward(const lmoe_shape* sh, const lmoe_weights* w, const void* x, void* y, int32_t* topk_idx,
+}  // extern "C"
+
+namespace lmoe {
+namespace {
+
+lmoe_status forward_impl(const lmoe_shape* sh, const lmoe_weights* w, const void* x, void* y, int32_t* topk_idx,
                          float* topk_w, void* ws, size_t ws_bytes, void* stream, void* const* ev) {
-  g_err[0] = 0;
   if (lmoe_status s = lmoe_validate(sh, w, ws_bytes)) return s;
   if (lmoe_status s = check_ws(sh, ws, ws_bytes)) return s;
   if (sh->T == 0) return LMOE_OK;
@@ -883,6 +887,70 @@ lmoe_status lmoe_forward(const lmoe_shape* sh, const lmoe_weights* w, const void
   LMOE_HIP(bf ? upgemm_any<bf16>(cd, n, hs, y) : upgemm_any<float>(cd, n, hs, y), "up GEMM");
   if (lmoe_status s = record(ev, 7, c.st)) return s;
   return LMOE_OK;
+}
+
+}  // namespace
+}  // namespace lmoe
+
+// ---------------------------------------------------------------------------
+// Scratch of lmoe_forward_noalloc: one array per device in the library's code
+// object (device memory that exists from the code object's load on a device
+// until the process ends).  Its name in host code is only a host-side
+// stand-in; host code resolves each device's address once with
+// hipGetSymbolAddress and passes that address to the kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[LMOE_NOALLOC_SCRATCH_BYTES];
+
+namespace lmoe {
+namespace {
+
+// Device address of `scratch` on the current device, resolved on the first
+// call made on that device (with it current) and kept for the process.
+lmoe_status scratch_on_device(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  const int dev = current_device();
+  if (dev < 0) return fail(LMOE_EHIP, "hipGetDevice failed");
+  if (dev >= kMaxDevices)
+    return fail(LMOE_EUNSUPPORTED, "device %d: the no-allocation entry point serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    LMOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255)) return fail(LMOE_EHIP, "scratch address %p unusable", p);
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return LMOE_OK;
+}
+
+}  // namespace
+}  // namespace lmoe
+
+extern "C" {
+
+lmoe_status lmoe_forward(const lmoe_shape* sh, const lmoe_weights* w, const void* x, void* y, int32_t* topk_idx,
+                         float* topk_w, void* ws, size_t ws_bytes, void* stream, void* const* ev) {
+  g_err[0] = 0;
+  return forward_impl(sh, w, x, y, topk_idx, topk_w, ws, ws_bytes, stream, ev);
+}
+
+lmoe_status lmoe_forward_noalloc(const lmoe_shape* sh, const lmoe_weights* w, const void* x, void* y,
+                                 int32_t* topk_idx, float* topk_w, void* stream) {
+  g_err[0] = 0;
+  if (lmoe_status s = check_shape(sh)) return s;
+  const size_t need = plan(sh).total;
+  if (need > LMOE_NOALLOC_SCRATCH_BYTES)
+    return fail(LMOE_EWORKSPACE,
+                "this layer call needs %zu bytes of scratch; lmoe_forward_noalloc holds %zu per device "
+                "(call lmoe_forward with a workspace instead)",
+                need, (size_t)LMOE_NOALLOC_SCRATCH_BYTES);
+  if (lmoe_status s = check_weights(sh, w, NEED_ROUTE | NEED_EXPERT | NEED_UP | NEED_NORM)) return s;
+  if (sh->T == 0) return LMOE_OK;
+  void* ws = nullptr;
+  if (lmoe_status s = scratch_on_device(&ws)) return s;
+  return forward_impl(sh, w, x, y, topk_idx, topk_w, ws, LMOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 lmoe_status lmoe_router_logits(const lmoe_shape* sh, const lmoe_weights* w, const void* x, float* logits,

@@ -17,13 +17,15 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblmoe.so"
 
 F32, BF16, F8E4M3 = 0, 1, 2
 NUM_STAGES = 7
+NOALLOC_SCRATCH_BYTES = 64 << 20  # LMOE_NOALLOC_SCRATCH_BYTES
 STAGES = ("route_gemm", "topk", "permute", "expert_gate_value", "expert_down", "combine_norm", "up")
 BWD_STAGES = ("forward_recompute", "up_norm_grads", "expert_grads", "latent_router_grads", "shared_grads")
 STATUS = {0: "LMOE_OK", 1: "LMOE_EINVAL", 2: "LMOE_EUNSUPPORTED", 3: "LMOE_EWORKSPACE", 4: "LMOE_EHIP"}
 DTYPE_CODE = {"f32": F32, "bf16": BF16, "f8": F8E4M3}
 _TORCH = {F32: torch.float32, BF16: torch.bfloat16, F8E4M3: torch.float8_e4m3fn}
 
-EXPORTS = ("lmoe_validate", "lmoe_workspace_bytes", "lmoe_forward", "lmoe_route", "lmoe_permute",
+EXPORTS = ("lmoe_validate", "lmoe_workspace_bytes", "lmoe_forward", "lmoe_forward_noalloc", "lmoe_route",
+           "lmoe_permute",
            "lmoe_expert_gemm", "lmoe_combine_norm", "lmoe_up", "lmoe_router_logits", "lmoe_quantile_bias",
            "lmoe_packed_bytes", "lmoe_pack_experts", "lmoe_quantize_1x128", "lmoe_backward",
            "lmoe_backward_workspace_bytes",
@@ -77,6 +79,7 @@ def load_library(path: str = LIB_PATH):
         "lmoe_validate": (ctypes.c_int, [sp, wp, sz]),
         "lmoe_workspace_bytes": (sz, [sp]),
         "lmoe_forward": (ctypes.c_int, [sp, wp, vp, vp, i32p, f32p, vp, sz, vp, vp]),
+        "lmoe_forward_noalloc": (ctypes.c_int, [sp, wp, vp, vp, i32p, f32p, vp]),
         "lmoe_route": (ctypes.c_int, [sp, wp, vp, i32p, f32p, vp, vp, sz, vp]),
         "lmoe_permute": (ctypes.c_int, [sp, i32p, i32p, i32p, i32p, vp, sz, vp]),
         "lmoe_expert_gemm": (ctypes.c_int, [sp, wp, vp, i32p, i32p, vp, vp, sz, vp]),
@@ -319,6 +322,19 @@ def forward(sh: Shape, w: Weights, x, y=None, topk_idx=None, topk_w=None, ws=Non
                             _ptr(y, _act_dtype(sh), "y"), _ptr(topk_idx, torch.int32, "topk_idx"),
                             _ptr(topk_w, torch.float32, "topk_w"), _ptr(ws, torch.uint8, "ws"), ws.numel(),
                             _stream(stream), ev))
+    return y, topk_idx, topk_w
+
+
+def forward_noalloc(sh: Shape, w: Weights, x, y, topk_idx=None, topk_w=None, stream=None):
+    """Whole layer through lmoe_forward_noalloc (the library's own per-device
+    scratch, no workspace); y, and topk_idx / topk_w when given, are written
+    in place.  Returns (y, topk_idx, topk_w)."""
+    lib = load_library()
+    _check(lib.lmoe_forward_noalloc(ctypes.byref(sh), ctypes.byref(w), _ptr(x, _act_dtype(sh), "x"),
+                                    _ptr(y, _act_dtype(sh), "y"),
+                                    None if topk_idx is None else _ptr(topk_idx, torch.int32, "topk_idx"),
+                                    None if topk_w is None else _ptr(topk_w, torch.float32, "topk_w"),
+                                    _stream(stream)))
     return y, topk_idx, topk_w
 
 

@@ -286,3 +286,24 @@ def test_backward_rejects_before_any_gpu_call(lib):
     packed_only = fake_weights(sh, w_gate=None, w_value=None, w_out=None, packed=0x9000)
     assert bw(ctypes.byref(sh), ctypes.byref(packed_only), buf, buf, None, ctypes.byref(g), ws, need, None, None) == 1
 
+
+def test_forward_noalloc_rejects_before_any_gpu_call(lib):
+    """The no-allocation entry point checks the shape, its scratch limit and
+    the weights on the host first (EWORKSPACE names the limit), and an empty
+    call returns before touching a device."""
+    vp = ctypes.c_void_p
+    big = k3()  # T = 8192: far more scratch than the fixed array holds
+    assert lmoe.workspace_bytes(big) > lmoe.NOALLOC_SCRATCH_BYTES
+    st = lib.lmoe_forward_noalloc(ctypes.byref(big), ctypes.byref(fake_weights(big)), vp(0x10), vp(0x20), None,
+                                  None, None)
+    assert st == 3 and "lmoe_forward_noalloc holds" in lmoe.last_error()
+    small = k3(T=64)
+    assert lmoe.workspace_bytes(small) <= lmoe.NOALLOC_SCRATCH_BYTES
+    st = lib.lmoe_forward_noalloc(ctypes.byref(small), ctypes.byref(fake_weights(small, gamma=None)), vp(0x10),
+                                  vp(0x20), None, None, None)
+    assert st == 1 and "gamma" in lmoe.last_error()
+    assert lib.lmoe_forward_noalloc(None, ctypes.byref(fake_weights(small)), vp(0x10), vp(0x20), None, None,
+                                    None) == 1
+    empty = k3(T=0)
+    assert lib.lmoe_forward_noalloc(ctypes.byref(empty), ctypes.byref(fake_weights(empty)), None, None, None, None,
+                                    None) == 0
