@@ -84,15 +84,44 @@ struct NSeg {
   int vec;            // output rows allow vector stores
 };
 
+// Tile walk of a dense GEMM.  The output is cut into big tiles (the main
+// launch's tile size), numbered with 8 token tiles per group and the feature
+// tiles running over the group, so 8 neighbours share one weight tile.  A
+// launch covers big tiles first .. first + count - 1, each as sf x st
+// sub-tiles (sf along the features, st along the tokens; 1 x 1 = the big tile
+// itself): the tail launch re-cuts the last, partial wave of big tiles into
+// smaller tiles so that it spreads over every CU.  Every tile runs the same
+// k-tile sequence, so an output element's sum is the same in any tile shape.
+struct DenseWalk {
+  int nft, ntt;       // big-tile grid: feature tiles, token tiles
+  int first, count;   // big tiles of this launch
+  int sf, st;         // sub-tiles per big tile
+  __device__ int num_logical() const { return count * sf * st; }
+  __device__ bool map(int lg, int& ttb, int& ftb, int& qf, int& qt) const {
+    const int n = sf * st;
+    if (lg >= count * n) return false;
+    const int b = first + lg / n, q = lg - (lg / n) * n;
+    const int grp = b / (8 * nft);
+    const int gsz = min(8, ntt - grp * 8);
+    const int within = b - grp * 8 * nft;
+    ftb = within / gsz;
+    ttb = grp * 8 + within % gsz;
+    qf = q % sf;
+    qt = q / sf;
+    return true;
+  }
+};
+
 template <class Cfg, typename CT>
 struct DenseXProb {
   static constexpr bool kDenseRows = true;  // rows past T: loaded from row 0, never stored
   const char* x;
   int64_t T;
   int K;              // H
-  int nseg, nft, ntt, padded;
+  int nseg, padded;
+  DenseWalk walk;
   float cap, inv_cap;
-  NSeg seg[3];
+  NSeg seg[3];        // ft0: first big feature tile of the segment
 
   struct State {
     int tt, f0;       // token tile, first feature (GLU: unit) of the tile
@@ -103,23 +132,19 @@ struct DenseXProb {
     if (bid >= padded) return false;
     return setup_lg(xcd_remap(bid, padded), st);
   }
-  __device__ int num_logical() const { return ntt * nft; }
-  // logical tile -> (token tile, feature tile): 8 token tiles per group,
-  // feature tiles run over the group, so 8 neighbours share one weight tile
-  // and an XCD's window covers a few weight tiles
+  __device__ int num_logical() const { return walk.num_logical(); }
+  // logical tile -> (token tile, feature tile) of this launch's tile size;
+  // an XCD's window of neighbours covers a few weight tiles
   __device__ bool setup_lg(int lg, State& st) const {
-    if (lg >= ntt * nft) return false;
-    const int grp = lg / (8 * nft);
-    const int gsz = min(8, ntt - grp * 8);
-    const int within = lg - grp * 8 * nft;
-    const int ft = within / gsz;
-    st.tt = grp * 8 + within % gsz;
+    int ttb, ftb, qf, qt;
+    if (!walk.map(lg, ttb, ftb, qf, qt)) return false;
+    st.tt = ttb * walk.st + qt;
     // constant indices only: the argument block stays in kernarg memory
     st.s = seg[0];
-    if (nseg > 1 && ft >= seg[1].ft0) st.s = seg[1];
-    if (nseg > 2 && ft >= seg[2].ft0) st.s = seg[2];
+    if (nseg > 1 && ftb >= seg[1].ft0) st.s = seg[1];
+    if (nseg > 2 && ftb >= seg[2].ft0) st.s = seg[2];
     const int per = st.s.kind == EPI_GLU ? Cfg::BF / 2 : Cfg::BF;
-    st.f0 = (ft - st.s.ft0) * per;
+    st.f0 = ((ftb - st.s.ft0) * walk.sf + qf) * per;
     return true;
   }
   __device__ int num_ksegs() const { return 1; }
@@ -179,7 +204,8 @@ struct UpProb {
   static constexpr bool kDenseRows = true;  // rows past T: never stored
   int64_t T;
   int N;              // H
-  int nks, nft, ntt, padded;
+  int nks, padded;
+  DenseWalk walk;
   char* y;
   const char* addend; // [T, N] act dtype, or null (identity up-projection adds n)
   int vec;
@@ -193,14 +219,12 @@ struct UpProb {
     if (bid >= padded) return false;
     return setup_lg(xcd_remap(bid, padded), st);
   }
-  __device__ int num_logical() const { return ntt * nft; }
+  __device__ int num_logical() const { return walk.num_logical(); }
   __device__ bool setup_lg(int lg, State& st) const {
-    if (lg >= ntt * nft) return false;
-    const int grp = lg / (8 * nft);
-    const int gsz = min(8, ntt - grp * 8);
-    const int within = lg - grp * 8 * nft;
-    st.ft = within / gsz;
-    st.tt = grp * 8 + within % gsz;
+    int ttb, ftb, qf, qt;
+    if (!walk.map(lg, ttb, ftb, qf, qt)) return false;
+    st.ft = ftb * walk.sf + qf;
+    st.tt = ttb * walk.st + qt;
     return true;
   }
   __device__ int num_ksegs() const { return nks; }

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -293,6 +294,52 @@ struct Ctx {
   float inv_cap() const { return isinf(sh->cap) ? 0.f : 1.f / sh->cap; }
 };
 
+// Dense GEMM launch over nft x ntt big tiles.  With the LDS-DMA 256 x 256
+// tile, when the tiles make some full waves over the CUs plus a last wave
+// that would leave at least half of them idle, the full waves run as they are
+// and the last wave's tiles are re-cut into 2 or 4 sub-tiles each (128 x 128
+// or 128 x 256), launched after them on the same stream.  Each output element
+// is summed over the same k-tiles in the same order in either tile, so the
+// results are bitwise those of the single launch.
+typedef Tile3<128, 128, 2, 2, 0> T2DenseQuarter;
+typedef Tile3<128, 256, 2, 4, 0> T2DenseHalf;
+
+template <class To, class From>
+To with_cfg(const From& f) {
+  static_assert(sizeof(To) == sizeof(From), "same problem, another tile");
+  To t;
+  memcpy(static_cast<void*>(&t), &f, sizeof(To));
+  return t;
+}
+
+template <class Cfg, typename CT, template <class, typename> class Prob>
+hipError_t launch_dense(Prob<Cfg, CT>& p, int nft, int ntt, hipStream_t st) {
+  const int ntiles = nft * ntt;
+  p.walk = DenseWalk{nft, ntt, 0, ntiles, 1, 1};
+  if constexpr (std::is_same_v<Cfg, T2Dense>) {
+    const int ncu = persistent_grid();
+    const int full = ntiles / ncu * ncu, tail = ntiles - full;
+    if (full > 0 && tail > 0 && 2 * tail <= ncu) {
+      p.walk.count = full;
+      p.padded = (int)pad8(full);
+      hipError_t e = launch_gemm<Cfg, CT>(p, p.padded, st);
+      if (e != hipSuccess) return e;
+      if (4 * tail <= ncu) {
+        auto q = with_cfg<Prob<T2DenseQuarter, CT>>(p);
+        q.walk = DenseWalk{nft, ntt, full, tail, 2, 2};
+        q.padded = (int)pad8((int64_t)tail * 4);
+        return launch_gemm<T2DenseQuarter, CT>(q, q.padded, st);
+      }
+      auto q = with_cfg<Prob<T2DenseHalf, CT>>(p);
+      q.walk = DenseWalk{nft, ntt, full, tail, 2, 1};
+      q.padded = (int)pad8((int64_t)tail * 2);
+      return launch_gemm<T2DenseHalf, CT>(q, q.padded, st);
+    }
+  }
+  p.padded = (int)pad8(ntiles);
+  return launch_gemm<Cfg, CT>(p, p.padded, st);
+}
+
 // x-GEMM: any of router logits (fp32 [T, E]), latent z ([T, L]) and the shared
 // experts' SiTU-GLU activations (hs [T, S*Is]) from one pass over x.
 // z_f32: z is written in fp32 (the W8A8 quantiser's input) instead of the
@@ -351,10 +398,7 @@ hipError_t xgemm(const Ctx& c, const void* x, float* logits, void* z, void* hs, 
   }
   if (ns == 0 || sh->T == 0) return hipSuccess;
   p.nseg = ns;
-  p.nft = ft;
-  p.ntt = (int)cdiv(sh->T, Cfg::BT);
-  p.padded = (int)pad8((int64_t)p.ntt * p.nft);
-  return launch_gemm<Cfg, CT>(p, p.padded, c.st);
+  return launch_dense<Cfg, CT>(p, ft, (int)cdiv(sh->T, Cfg::BT), c.st);
 }
 
 // y = n . W_up^T + sum_s hs_s . W_so[s]^T  (n added directly when w_up is NULL).
@@ -389,10 +433,7 @@ hipError_t upgemm(const Ctx& c, const void* n, const void* hs, void* y) {
     q.nkt = (int)(sh->Is * c.es() / 128);
   }
   p.nks = nk;
-  p.nft = (int)cdiv(sh->H, Cfg::BF);
-  p.ntt = (int)cdiv(sh->T, Cfg::BT);
-  p.padded = (int)pad8((int64_t)p.ntt * p.nft);
-  return launch_gemm<Cfg, CT>(p, p.padded, c.st);
+  return launch_dense<Cfg, CT>(p, (int)cdiv(sh->H, Cfg::BF), (int)cdiv(sh->T, Cfg::BT), c.st);
 }
 
 // xs: W8A8 row scales (z then holds e4m3 codes), [L/128, T*k] in expert
