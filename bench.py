@@ -109,8 +109,10 @@ def summarize_pmc(a):
         fk = [v["FETCH_SIZE"] for k, v in fetch.items() if tag in k and "FETCH_SIZE" in v]
         wk = [v["WRITE_SIZE"] for k, v in write.items() if tag in k and "WRITE_SIZE" in v]
         if fk and wk:
-            out["kernels"][name] = {"fetch_bytes": max(fk) * f_scale, "write_bytes": max(wk) * w_scale,
-                                    "FETCH_SIZE": max(fk), "WRITE_SIZE": max(wk)}
+            # a dense GEMM runs as two kernels (full waves, then the re-cut
+            # last wave): the step's traffic is their sum
+            out["kernels"][name] = {"fetch_bytes": sum(fk) * f_scale, "write_bytes": sum(wk) * w_scale,
+                                    "FETCH_SIZE": sum(fk), "WRITE_SIZE": sum(wk), "kernels": len(fk)}
     path = os.path.join(PROFILES, f"traffic_{a.workload}.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -131,56 +133,53 @@ def measured_traffic(workload, kernel):
     return k["fetch_bytes"] + k["write_bytes"]
 
 
-class ClockSampler:
-    """Samples the GPU's graphics clock (amdsmi) from a host thread while the
-    layer runs; reports the samples' median, minimum and maximum in MHz."""
+def sample_clock(step, seconds=3.0, depth=8, period_s=0.002):
+    """The GPU's graphics clock and socket power while the layer runs.  The
+    host keeps `depth` calls of `step()` queued for `seconds`, reading amdsmi's
+    GPU metrics table between polls of the queued calls' events.  The
+    firmware refreshes that table about once a second, so only snapshots that
+    carry a new firmware timestamp, taken while calls are queued, count; the
+    reading from before the loop never does."""
+    import collections
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
 
-    def __init__(self, period_s=0.01):
-        import threading
-        self.period, self.samples, self.error = period_s, [], None
-        self._stop = threading.Event()
-        self._thread = threading.Thread(target=self._run, daemon=True)
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            self._smi = amdsmi
-            self._h = amdsmi.amdsmi_get_processor_handles()[0]
-            self._read()
-        except Exception as e:  # no amdsmi or no permission: the field says why
-            self.error = f"{type(e).__name__}: {e}"
-
-    def _read(self):
-        info = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
-        for key in ("clk", "cur_clk"):
-            if key in info:
-                return float(info[key])
-        raise KeyError(f"no current clock among {sorted(info)}")
-
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                self.samples.append(self._read())
-            except Exception as e:
-                self.error = f"{type(e).__name__}: {e}"
-                return
-            self._stop.wait(self.period)
-
-    def __enter__(self):
-        if self.error is None:
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        if self._thread.is_alive():
-            self._thread.join()
-
-    def summary(self):
-        if not self.samples:
-            return {"mhz_median": None, "error": self.error or "no samples"}
-        v = sorted(self.samples)
-        return {"mhz_median": v[len(v) // 2], "mhz_min": v[0], "mhz_max": v[-1], "samples": len(v),
-                "source": "amdsmi GFX clock, sampled every 10 ms during the layer loop"}
+        def read():
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            xcd = [float(c) for c in m["current_gfxclks"] if isinstance(c, (int, float)) and c > 0]
+            return m["firmware_timestamp"], sum(xcd) / len(xcd), float(m["current_socket_power"]), \
+                float(m["average_gfx_activity"])
+        last = read()[0]
+    except Exception as e:  # no amdsmi, no permission or no such field: the field says why
+        return {"mhz_mean_over_xcds": None, "error": f"{type(e).__name__}: {e}"}
+    pending, snaps, calls = collections.deque(), [], 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        while len(pending) < depth:
+            step()
+            ev = torch.cuda.Event()
+            ev.record()
+            pending.append(ev)
+            calls += 1
+        fw, mhz, watts, busy = read()
+        if fw != last and calls > depth:
+            snaps.append((mhz, watts, busy))
+        last = fw
+        while pending and pending[0].query():
+            pending.popleft()
+        time.sleep(period_s)
+    torch.cuda.synchronize()
+    if not snaps:
+        return {"mhz_mean_over_xcds": None, "error": f"no metrics refresh during the {seconds:.1f} s loop"}
+    mhz = sorted(s[0] for s in snaps)
+    return {"mhz_mean_over_xcds": round(mhz[len(mhz) // 2]), "mhz_min": round(mhz[0]), "mhz_max": round(mhz[-1]),
+            "socket_watts": max(s[1] for s in snaps), "gfx_activity_pct": min(s[2] for s in snaps),
+            "snapshots": len(snaps), "layer_calls": calls,
+            "source": "amdsmi GPU metrics (current_gfxclks averaged over the XCDs), snapshots refreshed "
+                      "by the firmware while layer calls were queued"}
 
 
 def timed_loop(lmoe, sh, w, x, y, idx, tw, ws, steps, warmup, per_stage):
@@ -279,8 +278,7 @@ def main():
     gv_gbs = gv_bytes / (gv_ms * 1e-3) / 1e9
     dn_bytes = lmoe.expert_bytes(sh, touched, "down")
     layer_bytes = lmoe.expert_bytes(sh, touched) + lmoe.dense_bytes(sh, projections=proj) + 2 * T * cfg.H * es
-    with ClockSampler() as clk:
-        timed_loop(lmoe, sh, w, x, y, idx, tw, ws, max(50, a.steps), 0, per_stage=False)
+    clock = sample_clock(lambda: lmoe.forward(sh, w, x, y, idx, tw, ws))
 
     out = {
         "metric": METRIC,
@@ -325,7 +323,7 @@ def main():
         "expert_down": {"avg_ms": round(stages["expert_down"], 4), "weight_bytes": dn_bytes,
                         "gbs": round(dn_bytes / (stages["expert_down"] * 1e-3) / 1e9, 1),
                         "frac": round(dn_bytes / (stages["expert_down"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-        "gpu_clock": clk.summary(),
+        "gpu_clock": clock,
     }
 
     if not a.no_decode:
