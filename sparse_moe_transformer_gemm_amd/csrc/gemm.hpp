@@ -65,6 +65,41 @@ __device__ __forceinline__ void store4(OT* row, int f, const float* v, int fvali
   }
 }
 
+// bf16 outputs, 16 bytes per lane.  In a 32x32 MFMA block, lanes l and l + 32
+// hold the same output row: of the 16 features b .. b + 15 that accumulator
+// groups 2h and 2h + 1 cover, lane l has b .. b+3 (va) and b+8 .. b+11 (vb),
+// lane l + 32 has b+4 .. b+7 and b+12 .. b+15.  One exchange between the
+// half-waves leaves b .. b+7 with lane l and b+8 .. b+15 with lane l + 32, so
+// a wave stores a row's 16 features with one 16-byte store per lane instead
+// of two 8-byte ones (half the store instructions, each covering 32 bytes
+// of a row).  The values and their rounding are those of store4.  Every lane
+// of the wave calls it (the exchange reads the partner lane); `ok` says
+// whether the row is stored and is the same for both lanes of a pair.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 v = {(bf16)a, (bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// a0, a1 are va packed in pairs by pack_bf16x2, b0, b1 likewise vb.
+__device__ __forceinline__ void store16_pair(bf16* row, int b, uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
+                                             int fvalid, bool ok, bool vec, int lane) {
+  // v_permlane32_swap trades the upper half-wave of its first operand with
+  // the lower half-wave of its second: afterwards lane l < 32 holds its own a
+  // and lane l + 32's a, lane l + 32 holds lane l's b and its own b.
+  const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+  if (!ok) return;
+  const uint32_t w[4] = {s0[0], s1[0], s0[1], s1[1]};
+  const int f = b + (lane >= 32 ? 8 : 0);
+  if (vec && f + 7 < fvalid) {
+    *reinterpret_cast<uint4*>(row + f) = uint4{w[0], w[1], w[2], w[3]};
+  } else {
+    uint16_t* r16 = reinterpret_cast<uint16_t*>(row);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (f + e < fvalid) r16[f + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Problem: x-GEMM (router logits, latent z, shared-expert gate/value) -- one
 // GEMM over x with the weight matrices concatenated along the features.
@@ -648,6 +683,18 @@ __device__ __forceinline__ void for_glu(int wf0, int wt0, int lane, F&& f) {
         f(i, j, g, (wf0 + i * 32) / 2 + g * 8 + (lane >> 5) * 4, wt0 + j * 32 + (lane & 31));
 }
 
+// for_acc by pairs of accumulator groups (2h, 2h + 1) for store16_pair:
+// f(i, j, h, b, tl), b the pair's first feature.
+template <class Cfg, class F>
+__device__ __forceinline__ void for_acc_pairs(int wf0, int wt0, int lane, F&& f) {
+#pragma unroll
+  for (int i = 0; i < Cfg::FI; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TI; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) f(i, j, h, wf0 + i * 32 + h * 16, wt0 + j * 32 + (lane & 31));
+}
+
 template <class Cfg, typename CT>
 template <class Acc>
 __device__ __forceinline__ void DenseXProb<Cfg, CT>::epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const {
@@ -689,6 +736,30 @@ template <class Acc>
 __device__ __forceinline__ void UpProb<Cfg, CT>::epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const {
   const int tv = tokens_valid(st);
   const int tt = st.tt, ft = st.ft;
+  if constexpr (std::is_same_v<CT, bf16>) {
+    for_acc_pairs<Cfg>(wf0, wt0, lane, [&](int i, int j, int h, int fb, int tl) __attribute__((always_inline)) {
+      const int f = ft * Cfg::BF + fb;
+      const int64_t t = (int64_t)tt * Cfg::BT + min(tl, tv - 1);
+      float va[4], vb[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        va[r] = acc[i][j][8 * h + r];
+        vb[r] = acc[i][j][8 * h + 4 + r];
+      }
+      if (addend && tl < tv) {
+        // this lane's own features: f + 4 (lane / 32) + r and 8 further on
+        const bf16* ar = reinterpret_cast<const bf16*>(addend) + t * N + f + (lane >> 5) * 4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (f + (lane >> 5) * 4 + r < N) va[r] += to_f32(ar[r]);
+          if (f + (lane >> 5) * 4 + 8 + r < N) vb[r] += to_f32(ar[8 + r]);
+        }
+      }
+      store16_pair(reinterpret_cast<bf16*>(y) + t * N, f, pack_bf16x2(va[0], va[1]), pack_bf16x2(va[2], va[3]),
+                   pack_bf16x2(vb[0], vb[1]), pack_bf16x2(vb[2], vb[3]), N, tl < tv, vec, lane);
+    });
+    return;
+  }
   for_acc<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int fl, int tl) __attribute__((always_inline)) {
     const int f = ft * Cfg::BF + fl;
     if (tl < tv && f < N) {
@@ -738,6 +809,16 @@ __device__ __forceinline__ void ExpertGVProb<Cfg, CT, RAW>::epilogue(const State
 template <class Cfg, typename CT>
 template <class Acc>
 __device__ __forceinline__ void ExpertDownProb<Cfg, CT>::epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const {
+  if constexpr (std::is_same_v<CT, bf16>) {
+    for_acc_pairs<Cfg>(wf0, wt0, lane, [&](int i, int j, int h, int fb, int tl) __attribute__((always_inline)) {
+      const f32x16& a = acc[i][j];
+      bf16* row = reinterpret_cast<bf16*>(out) + (int64_t)(st.m0 + min(tl, st.rows - 1)) * L;
+      store16_pair(row, st.ft * Cfg::BF + fb, pack_bf16x2(a[8 * h], a[8 * h + 1]), pack_bf16x2(a[8 * h + 2], a[8 * h + 3]),
+                   pack_bf16x2(a[8 * h + 4], a[8 * h + 5]), pack_bf16x2(a[8 * h + 6], a[8 * h + 7]), L, tl < st.rows,
+                   true, lane);
+    });
+    return;
+  }
   for_acc<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int fl, int tl) __attribute__((always_inline)) {
     if (tl < st.rows) {
       float v[4];
