@@ -187,8 +187,11 @@ __device__ __forceinline__ bool bg_vec_ok(const char* base, int64_t ld, int es) 
 // its full register budget.
 template <int MODE, int ARC, int AF32, int BRC, int BF32>
 __global__ __launch_bounds__(256, MODE != BG_DENSE ? 4 : 1) void bgemm_kernel(const BgArgs p) {
-  __shared__ __attribute__((aligned(16))) char sA[2][kBgTileBytes];
-  __shared__ __attribute__((aligned(16))) char sB[2][kBgTileBytes];
+  // operand double buffers; after the k-loop the grouped-K mode reuses them
+  // to stage its output tile (below)
+  __shared__ __attribute__((aligned(16))) char smem[4 * kBgTileBytes];
+  char (*sA)[kBgTileBytes] = reinterpret_cast<char (*)[kBgTileBytes]>(smem);
+  char (*sB)[kBgTileBytes] = reinterpret_cast<char (*)[kBgTileBytes]>(smem + 2 * kBgTileBytes);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int e = 0, rowbase = 0, M = p.M, K = p.K, m0 = 0;
   const int n0 = blockIdx.x * kBgN;
@@ -259,8 +262,9 @@ __global__ __launch_bounds__(256, MODE != BG_DENSE ? 4 : 1) void bgemm_kernel(co
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           if (wm + i * 32 < rows_a && wn + j * 32 < rows_b) {
-            // dense mode: transposed blocks, for row-vector stores (below)
-            if constexpr (MODE == BG_DENSE)
+            // dense and grouped-K modes: transposed blocks, for row-vector
+            // stores (below)
+            if constexpr (MODE != BG_GROUP_M)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
             else
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
@@ -275,12 +279,68 @@ __global__ __launch_bounds__(256, MODE != BG_DENSE ? 4 : 1) void bgemm_kernel(co
 
   char* cbase = p.c + (int64_t)e * p.cgstride * (p.cbf16 ? 2 : 4);
   const int crow0 = (MODE == BG_GROUP_M ? rowbase : 0) + m0;
+  if constexpr (MODE == BG_GROUP_K) {
+    // The weight gradients are the backward's largest writes (fp32, every
+    // expert's full matrices).  The tile goes out through LDS in two halves of
+    // 64 rows: the two waves holding a half write their transposed blocks
+    // (lane l: row l % 32, 4 consecutive columns per group g), then all 256
+    // threads store it row by row, 16 bytes per lane, so each store
+    // instruction covers two whole 512-byte row segments.
+    constexpr int CP = kBgN + 4;  // staged row pitch in floats
+    static_assert(64 * CP * 4 <= 4 * kBgTileBytes, "half tile in LDS");
+    float* sc = reinterpret_cast<float*>(smem);
+    const bool cvec = !p.cbf16 && (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(cbase) & 15) == 0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if ((wid & 1) == half) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int m = i * 32 + lr, n = wn + j * 32 + g * 8 + (lane >> 5) * 4;
+              *reinterpret_cast<f32x4*>(sc + m * CP + n) =
+                  f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+            }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int ml = q * 8 + (tid >> 5), n = (tid & 31) * 4;
+        const int m = half * 64 + ml;
+        if (m < rows_a && n < rows_b) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(sc + ml * CP + n);
+          const int64_t off = (int64_t)(crow0 + m) * p.ldc + n0 + n;
+          if (cvec && n + 3 < rows_b) {
+            float* cp = reinterpret_cast<float*>(cbase) + off;
+            f32x4 o = v;
+            if (p.accumulate) o += *reinterpret_cast<const f32x4*>(cp);
+            *reinterpret_cast<f32x4*>(cp) = o;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (n + r >= rows_b) continue;
+              if (p.cbf16) {
+                reinterpret_cast<unsigned short*>(cbase)[off + r] = f2bf(v[r]);
+              } else {
+                float* cp = reinterpret_cast<float*>(cbase) + off + r;
+                *cp = p.accumulate ? *cp + v[r] : v[r];
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
   if constexpr (MODE == BG_DENSE) {
     // acc[i][j] is the transposed 32x32 block: lane l holds row m = l % 32 of
     // C and its columns 8 g + 4 (l / 32) + r (g, r < 4), so each g is four
     // consecutive elements of one C row, stored as one 16-byte (fp32) or
     // 8-byte (bf16) vector where aligned and wholly inside the tile.  (The
-    // grouped modes measured slower this way and keep the layout below.)
+    // grouped-M mode measured slower this way and keeps the layout below.)
     const bool cvec = (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(cbase) & (p.cbf16 ? 7 : 15)) == 0;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
