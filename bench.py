@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the secondary lines (Zipf-skewed router at T=16384, e4m3 expert weights at T=8192)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the 3 s clock reading (profiler runs)")
     ap.add_argument("--pack", action="store_true",
                     help="pack the routed expert weights once (lmoe_pack_experts) and time the layer on them")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -278,7 +280,8 @@ def main():
     gv_gbs = gv_bytes / (gv_ms * 1e-3) / 1e9
     dn_bytes = lmoe.expert_bytes(sh, touched, "down")
     layer_bytes = lmoe.expert_bytes(sh, touched) + lmoe.dense_bytes(sh, projections=proj) + 2 * T * cfg.H * es
-    clock = sample_clock(lambda: lmoe.forward(sh, w, x, y, idx, tw, ws))
+    clock = {"mhz_mean_over_xcds": None, "error": "skipped (--no-clock)"} if a.no_clock else \
+        sample_clock(lambda: lmoe.forward(sh, w, x, y, idx, tw, ws))
 
     out = {
         "metric": METRIC,
@@ -313,7 +316,7 @@ def main():
             "frac": round(gv_gbs / PEAK_HBM_GBS, 4),
             "traffic": measured_traffic(cfg.name, "expert_gate_value"),
             "bytes_per_launch": gv_bytes,
-            "bytes_unit": "gate + value weights of one touched expert, 2*I*L*2 B",
+            "bytes_unit": "gate + value weights of one touched expert, 2*I*L*%d B" % (1 if cfg.w_expert == "f8" else es),
             "units_per_launch": touched,
             "avg_ms": round(gv_ms, 4),
             "intermediate_bytes": gv_inter,
