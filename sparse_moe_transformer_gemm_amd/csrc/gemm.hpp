@@ -484,6 +484,55 @@ struct ExpertDownProb {
   __device__ __forceinline__ void epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const;
 };
 
+// Backward data gradients of the routed experts on the persistent engine
+// (Tile3 WTR): C[r, f] = sum over the K segments s of X_s[r, k] W_s[e][k, f],
+// the expert matrices read as the forward stores them ([E, K_s, F], features
+// contiguous) and transposed between LDS and the MFMAs.  X_s: rows in
+// assignment (expert) order, [T*k, K_s], bf16.  C: fp32 [T*k, F].
+//   dA = dO W_o[e]        (one segment, K = L, F = I)
+//   dz rows = dG W_g[e] + dV W_v[e]   (two segments, K = I each, F = L)
+template <class Cfg, typename CT>
+struct ExpertTGradProb {
+  ExpertTiles<Cfg> et;
+  const char* x[2];   // [T*k, kd[s]]
+  const char* w[2];   // [E, kd[s], F]
+  int kd[2];
+  int nseg, F;
+  float* out;         // [T*k, F]
+
+  typedef ExpertState State;
+  __device__ bool setup(int bid, State& st) const { return et.locate(bid, st); }
+  __device__ int num_logical() const { return et.num_logical(); }
+  __device__ bool setup_lg(int lg, State& st) const { return et.locate_lg(lg, et.num_logical(), st); }
+  __device__ int num_ksegs() const { return nseg; }
+  __device__ int seg_ktiles(int s) const { return kd[s] * (int)sizeof(CT) / 128; }
+  __device__ bool seg_f8(const State&, int) const { return false; }
+  __device__ int tokens_valid(const State& st) const { return st.rows; }
+  __device__ int feats_valid(const State& st) const { return min(Cfg::BF, F - st.ft * Cfg::BF); }
+  __device__ const char* x_row(const State& st, int s, int r) const {
+    if (r >= st.rows) return nullptr;
+    return x[s] + (int64_t)(st.m0 + r) * kd[s] * (int64_t)sizeof(CT);
+  }
+  template <int RPI = 8>
+  __device__ const char* x_row_grp(const State& st, int s, int r0, int lane) const {
+    return x_row(st, s, min(r0 + lane / (64 / RPI), tokens_valid(st) - 1));
+  }
+  // 16-byte chunk c (features ft * BF + 8 c ..) of k-row kr of the first
+  // k-tile of segment s; each k-tile moves it by w_tstep bytes.  Chunks past
+  // F (a last, partial feature tile) read the row's last chunk instead: they
+  // only feed accumulator columns that are never stored, and no read leaves
+  // the matrix.
+  __device__ const char* w_tsrc(const State& st, int s, int kr, int c) const {
+    const int f = min(st.ft * Cfg::BF + 8 * c, F - 8);
+    return w[s] + (((int64_t)st.e * kd[s] + kr) * F + f) * (int64_t)sizeof(CT);
+  }
+  __device__ int64_t w_tstep(const State&, int) const { return (int64_t)64 * F * sizeof(CT); }
+  __device__ const char* w_row(const State&, int, int, const float**) const { return nullptr; }
+  __device__ const char* w_block(const State&) const { return nullptr; }
+  template <class Acc>
+  __device__ __forceinline__ void epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const;
+};
+
 // ---------------------------------------------------------------------------
 // The mainloop.
 // ---------------------------------------------------------------------------
@@ -826,6 +875,20 @@ __device__ __forceinline__ void ExpertDownProb<Cfg, CT>::epilogue(const State& s
       for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r];
       CT* row = reinterpret_cast<CT*>(out) + (int64_t)(st.m0 + tl) * L;
       store4<CT>(row, st.ft * Cfg::BF + fl, v, L, true);
+    }
+  });
+}
+
+template <class Cfg, typename CT>
+template <class Acc>
+__device__ __forceinline__ void ExpertTGradProb<Cfg, CT>::epilogue(const State& st, const Acc& acc, int wf0, int wt0,
+                                                                   int lane) const {
+  for_acc<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int fl, int tl) __attribute__((always_inline)) {
+    if (tl < st.rows) {
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r];
+      store4<float>(out + (int64_t)(st.m0 + tl) * F, st.ft * Cfg::BF + fl, v, F, true);
     }
   });
 }

@@ -51,9 +51,16 @@ struct Tile2 {
 // Dense GEMMs over many tokens / few tokens (weight streaming); experts
 // holding many rows, a few dozen rows, or one or two rows (decode).
 // Split-ring tile (gemm3_kernel below): weights three stages deep, tokens two.
-template <int BF_, int BT_, int WF_, int WT_, int WAUX_, int PERSIST_ = 0, int WF8_ = 0, int SW_ = 3, int XF8_ = 0>
+template <int BF_, int BT_, int WF_, int WT_, int WAUX_, int PERSIST_ = 0, int WF8_ = 0, int SW_ = 3, int XF8_ = 0,
+          int WTR_ = 0>
 struct Tile3 {
   static constexpr int BF = BF_, BT = BT_, WF = WF_, WT = WT_, WAUX = WAUX_;
+  // WTR: the weights are stored transposed ([K, F] per matrix, features
+  // contiguous, as the backward's data gradients read the forward's
+  // weights).  A stage then holds the k-tile's 64 k-rows of the tile's 256
+  // features (512 bytes each, two per DMA instruction), and the MFMA's weight
+  // fragments come out of it through transposing LDS reads.
+  static constexpr int WTR = WTR_;
   // PERSIST: a grid of resident work-groups walks the tile list with one
   // continuous DMA pipeline (gemm3p_kernel) instead of one tile per group
   static constexpr int PERSIST = PERSIST_;
@@ -87,6 +94,7 @@ struct Tile3 {
   static_assert(PERSIST || (!WF8 && SW == 3), "one-tile-per-group kernel: bf16 weights, three stages");
   static_assert(!XF8 || (WF8 && PERSIST), "e4m3 tokens go with e4m3 weights in the persistent kernel");
   static_assert(!XF8 || (BT % 64 == 0 && BT / 64 <= NW), "one 4-byte scale DMA per 64 token rows");
+  static_assert(!WTR || (PERSIST && !WF8 && !XF8 && BF == 256), "transposed weights: bf16, 256 features");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
@@ -401,6 +409,54 @@ __device__ __forceinline__ void mma_ktile_a8(f32x16 (&acc)[FI][TI], const char* 
     }
 }
 
+// Transposed weight stage (Tile3 WTR): k-row kr (0..63) of the tile's 256
+// features at kr * 512 bytes, its 16-byte chunk c stored at position
+// c ^ ((kr & 3) << 2), so the four k-rows one transposing read spans fall in
+// different bank windows.
+__device__ __forceinline__ int wtr_off(int kr, int f) {
+  return kr * 512 + ((((f >> 3) ^ ((kr & 3) << 2))) << 4) + (f & 7) * 2;
+}
+
+// As mma_ktile, with the weight fragments (32 features x 16 k per MFMA)
+// read from a transposed stage with ds_read_b64_tr_b16: within each 16-lane
+// group, lane i receives element i % 4 of the 4-element loads of lanes
+// 4 j + i / 4 (j = 0..3).  So lane q of group G loads k-row
+// 8 (G / 2) + q / 4 of the k-step at features r0 + 16 (G % 2) + 4 (q % 4)
+// .. + 3, and a second load 4 k-rows further gives its other 4 k: lane l
+// ends up with the 8 consecutive k (8 (l / 32) .. + 7) of feature
+// r0 + l % 32, the fragment mma_ktile reads from a k-contiguous stage.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+template <int FI, int TI>
+__device__ __forceinline__ void mma_ktile_wt(f32x16 (&acc)[FI][TI], const char* sW, const char* sX, int wf0, int wt0,
+                                             int lane, int tiv) {
+  const int lr = lane & 31;
+  const int sw = swz(lr);  // token fragment row offsets are multiples of 32
+  const char* px = sX + (wt0 + lr) * 128;
+  const int G = lane >> 4, q = lane & 15;
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int kr = ks * 16 + 8 * (G >> 1) + (q >> 2);
+    bf16x8 a[FI];
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const char* pa = sW + wtr_off(kr, wf0 + i * 32 + 16 * (G & 1) + 4 * (q & 3));
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa + 4 * 512));
+      const short v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      a[i] = *reinterpret_cast<const bf16x8*>(v);
+    }
+    const int ch = ((2 * ks + (lane >> 5)) ^ sw) << 4;
+#pragma unroll
+    for (int j = 0; j < TI; ++j)
+      if (j < tiv) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(px + j * 32 * 128 + ch);
+#pragma unroll
+        for (int i = 0; i < FI; ++i) acc[i][j] = mfma32(a[i], b, acc[i][j]);
+      }
+  }
+}
+
 template <class Cfg, class Prob>
 __global__ __launch_bounds__(Cfg::NT) void gemm2_kernel(const Prob p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -691,6 +747,17 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
   const char* wblk = nullptr;
   int64_t wstep = Cfg::RBW;
   auto set_w = [&]() __attribute__((always_inline)) {
+    if constexpr (Cfg::WTR) {
+      // instruction q stages k-rows 2 q and 2 q + 1; lane l fetches the chunk
+      // that belongs at position l % 32 of k-row 2 q + l / 32
+      wstep = p.w_tstep(wst, wsg);
+#pragma unroll
+      for (int i = 0; i < NQW; ++i) {
+        const int q = wid + NW * i, kr = 2 * q + (lane >> 5);
+        srcW[i] = p.w_tsrc(wst, wsg, kr, (lane & 31) ^ ((kr & 3) << 2));
+      }
+      return;
+    }
     wblk = Cfg::WF8 ? nullptr : p.w_block(wst);
     wstep = wblk ? kPackBlock : Cfg::RBW;
     const float* dummy = nullptr;
@@ -862,6 +929,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
         }
         if constexpr (Cfg::XF8) mma_ktile_a8<FI, TI>(acc, sW, sX, wf0, wt0, lane, tiv);
         else mma_ktile_f8<FI, TI>(acc, sW, sX, wf0, wt0, lane, tiv);
+      } else if constexpr (Cfg::WTR) {
+        mma_ktile_wt<FI, TI>(acc, sW, sX, wf0, wt0, lane, tiv);
       } else {
         mma_ktile<FI, TI, false>(acc, sW, sX, wf0, wt0, lane, tiv);
       }

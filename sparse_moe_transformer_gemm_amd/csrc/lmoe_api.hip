@@ -492,6 +492,31 @@ hipError_t expert_down(const Ctx& c, const void* act, const int32_t* offsets, co
   return launch_gemm<Cfg, CT>(p, pad8(max_tiles(sh, Cfg::BT) * p.et.nft), c.st);
 }
 
+// Backward data gradients of the routed experts on the persistent engine,
+// weights transposed on the way into the MFMAs: out = x0 W0[e] (+ x1 W1[e]),
+// x_s [T*k, k_s] bf16 in expert order, W_s [E, k_s, F], out fp32 [T*k, F].
+typedef Tile3<256, 256, 4, 4, 0, 1, 0, 3, 0, 1> T2ExpertTGrad;
+hipError_t expert_tgrad(const Ctx& c, const int32_t* offsets, const int4* tiles, const int32_t* tcount, int F,
+                        const void* x0, const void* w0, int k0, const void* x1, const void* w1, int k1, float* out) {
+  using Cfg = T2ExpertTGrad;
+  const lmoe_shape* sh = c.sh;
+  ExpertTGradProb<Cfg, bf16> p{};
+  p.et.offsets = offsets;
+  p.et.tiles = tiles;
+  p.et.tile_count = tcount;
+  p.et.nft = (int)cdiv(F, Cfg::BF);
+  p.x[0] = static_cast<const char*>(x0);
+  p.w[0] = static_cast<const char*>(w0);
+  p.kd[0] = k0;
+  p.x[1] = static_cast<const char*>(x1);
+  p.w[1] = static_cast<const char*>(w1);
+  p.kd[1] = k1;
+  p.nseg = x1 ? 2 : 1;
+  p.F = F;
+  p.out = out;
+  return launch_gemm<Cfg, bf16>(p, pad8(max_tiles(sh, Cfg::BT) * p.et.nft), c.st);
+}
+
 // Gate and value pre-activations (fp32, assignment order) for the backward's
 // recompute, with the forward's persistent bf16 expert GEMM.
 hipError_t expert_gv_raw(const Ctx& c, const void* z, const int32_t* offsets, const int32_t* sorted,
@@ -1039,6 +1064,9 @@ lmoe_status lmoe_quantize_1x128(const void* x, int64_t R, int32_t C, void* q, fl
 // ---------------------------------------------------------------------------
 // Backward pass.
 // ---------------------------------------------------------------------------
+#ifndef LMOE_BW_TGRAD
+#define LMOE_BW_TGRAD 1
+#endif
 size_t lmoe_backward_workspace_bytes(const lmoe_shape* sh) {
   if (check_shape(sh) != LMOE_OK) return 0;
   return bplan(sh).total;
@@ -1135,19 +1163,31 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   }
   if (lmoe_status s = record(ev, 2, st)) return s;
   // --- routed experts -----------------------------------------------------
-  LMOE_HIP((bg<BG_GROUP_M, 0, 0, 1, 0>(bop(dO, L, 0, nullptr, 1, 1), bop(w->w_out, I, (int64_t)L * I), dA, I, 0, I, L, 0,
-                                       st, sh, 0, 0, offsets, tiles, tc)),
-           "dA");
+  // The grouped data gradients run on the persistent engine with transposed
+  // weight stages when its 256-row token tiles fit the batch (its tile list
+  // is the forward's); the register-staged grouped GEMM otherwise.
+  const bool tgrad = T > 256 && LMOE_BW_TGRAD;
+  if (tgrad) {
+    LMOE_HIP(expert_tgrad(cx, offsets, tiles2, tc2, I, dO, w->w_out, L, nullptr, nullptr, 0, dA), "dA");
+  } else {
+    LMOE_HIP((bg<BG_GROUP_M, 0, 0, 1, 0>(bop(dO, L, 0, nullptr, 1, 1), bop(w->w_out, I, (int64_t)L * I), dA, I, 0, I, L,
+                                         0, st, sh, 0, 0, offsets, tiles, tc)),
+             "dA");
+  }
   LMOE_HIP((bg<BG_GROUP_K, 1, 0, 1, 0>(bop(dO, L, 0, nullptr, 1, 1), bop(A, I, 0, nullptr, 1, 1), gr->dw_out, I, L, I, 0,
                                        0, st, sh, 0, (int64_t)L * I, offsets)),
            "dW_out");
   LMOE_HIP(bw_situ(1, G, V, dA, dG, dV, (int64_t)tk * I, sh, st), "SiTU-GLU gradient");
-  LMOE_HIP((bg<BG_GROUP_M, 0, 0, 1, 0>(bop(dG, I, 0, nullptr, 1, 1), bop(w->w_gate, L, (int64_t)I * L), zr, L, 0, L, I, 0,
-                                       st, sh, 0, 0, offsets, tiles, tc)),
-           "dz rows (gate)");
-  LMOE_HIP((bg<BG_GROUP_M, 0, 0, 1, 0>(bop(dV, I, 0, nullptr, 1, 1), bop(w->w_value, L, (int64_t)I * L), zr, L, 0, L, I, 1,
-                                       st, sh, 0, 0, offsets, tiles, tc)),
-           "dz rows (value)");
+  if (tgrad) {
+    LMOE_HIP(expert_tgrad(cx, offsets, tiles2, tc2, L, dG, w->w_gate, I, dV, w->w_value, I, zr), "dz rows");
+  } else {
+    LMOE_HIP((bg<BG_GROUP_M, 0, 0, 1, 0>(bop(dG, I, 0, nullptr, 1, 1), bop(w->w_gate, L, (int64_t)I * L), zr, L, 0, L, I,
+                                         0, st, sh, 0, 0, offsets, tiles, tc)),
+             "dz rows (gate)");
+    LMOE_HIP((bg<BG_GROUP_M, 0, 0, 1, 0>(bop(dV, I, 0, nullptr, 1, 1), bop(w->w_value, L, (int64_t)I * L), zr, L, 0, L, I,
+                                         1, st, sh, 0, 0, offsets, tiles, tc)),
+             "dz rows (value)");
+  }
   LMOE_HIP((bg<BG_GROUP_K, 1, 0, 1, 0>(bop(dG, I, 0, nullptr, 1, 1), bop(zsrc, L, 0, sorted, k, 1), gr->dw_gate, L, I, L,
                                        0, 0, st, sh, 0, (int64_t)I * L, offsets)),
            "dW_gate");
