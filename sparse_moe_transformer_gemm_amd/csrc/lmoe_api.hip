@@ -9,7 +9,7 @@
 #include <mutex>
 
 #include "backward.hpp"
-#include "gemm2.hpp"
+#include "wgrad.hpp"
 #include "kernels.hpp"
 #include "lmoe.h"
 
@@ -517,6 +517,33 @@ hipError_t expert_tgrad(const Ctx& c, const int32_t* offsets, const int4* tiles,
   return launch_gemm<Cfg, bf16>(p, pad8(max_tiles(sh, Cfg::BT) * p.et.nft), c.st);
 }
 
+// Expert weight gradients on the persistent pipeline: C_e = P_e^T Q_e for
+// every expert (wgrad.hpp).
+hipError_t wgrad(const Ctx& c, const void* pm, int64_t ldp, const void* qn, int64_t ldq, const int32_t* gather, int gk,
+                 float* out, int M, int N, const int32_t* offsets, const void* zero) {
+  using Cfg = TWGrad;
+  WGradArgs a{static_cast<const char*>(pm), ldp, static_cast<const char*>(qn), ldq, gather, gk, out, M, N,
+              c.sh->E, offsets, static_cast<const char*>(zero)};
+  auto kern = wgrad3p_kernel<Cfg>;
+  static std::once_flag once[kMaxDevices];
+  static hipError_t attr[kMaxDevices];
+  auto set_attr = [&] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               Cfg::LDS);
+  };
+  const int dev = current_device();
+  hipError_t e;
+  if (dev < 0 || dev >= kMaxDevices) {
+    e = set_attr();
+  } else {
+    std::call_once(once[dev], [&] { attr[dev] = set_attr(); });
+    e = attr[dev];
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)persistent_grid()), dim3(Cfg::NT), Cfg::LDS, c.st, a);
+  return hipGetLastError();
+}
+
 // Gate and value pre-activations (fp32, assignment order) for the backward's
 // recompute, with the forward's persistent bf16 expert GEMM.
 hipError_t expert_gv_raw(const Ctx& c, const void* z, const int32_t* offsets, const int32_t* sorted,
@@ -679,7 +706,7 @@ constexpr int kBwChunks = 64;  // token chunks of the dgamma reduction
 
 struct BPlan {
   size_t logits, z, idx, w, bcounts, offsets, sorted, pos, tiles, tcount, tiles2, tcount2;
-  size_t G, V, A, dA, dG, dV, O, zr, dO, c, n, dn, dz, r, dw, dl, gs, vs, hs, dhs, dgs, dvs, dgp, total;
+  size_t G, V, A, dA, dG, dV, O, zr, dO, c, n, dn, dz, r, dw, dl, gs, vs, hs, dhs, dgs, dvs, dgp, zpage, total;
 };
 
 BPlan bplan(const lmoe_shape* sh) {
@@ -728,6 +755,7 @@ BPlan bplan(const lmoe_shape* sh) {
   p.dgs = take(T * sis * 2);
   p.dvs = take(T * sis * 2);
   p.dgp = take((size_t)kBwChunks * sh->L * 4);
+  p.zpage = take(512);  // zeros, the source of rows past an expert's last (wgrad3p_kernel)
   p.total = off;
   return p;
 }
@@ -1067,6 +1095,9 @@ lmoe_status lmoe_quantize_1x128(const void* x, int64_t R, int32_t C, void* q, fl
 #ifndef LMOE_BW_TGRAD
 #define LMOE_BW_TGRAD 1
 #endif
+#ifndef LMOE_BW_WGRAD
+#define LMOE_BW_WGRAD 1
+#endif
 size_t lmoe_backward_workspace_bytes(const lmoe_shape* sh) {
   if (check_shape(sh) != LMOE_OK) return 0;
   return bplan(sh).total;
@@ -1174,9 +1205,21 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
                                          0, st, sh, 0, 0, offsets, tiles, tc)),
              "dA");
   }
-  LMOE_HIP((bg<BG_GROUP_K, 1, 0, 1, 0>(bop(dO, L, 0, nullptr, 1, 1), bop(A, I, 0, nullptr, 1, 1), gr->dw_out, I, L, I, 0,
-                                       0, st, sh, 0, (int64_t)L * I, offsets)),
-           "dW_out");
+  // The weight gradients take the persistent pipeline above 256 tokens when
+  // their matrices are whole 256 x 256 tiles.
+  const bool wg3 = T > 256 && I % 256 == 0 && L % 256 == 0 && LMOE_BW_WGRAD;
+  void* zpage = at<void>(ws, pl.zpage);
+  if (wg3) {
+    hipLaunchKernelGGL(zero_page_kernel, dim3(1), dim3(128), 0, st, static_cast<uint32_t*>(zpage));
+    LMOE_HIP(hipGetLastError(), "zero page");
+  }
+  if (wg3) {
+    LMOE_HIP(wgrad(cx, dO, L, A, I, nullptr, 1, gr->dw_out, L, I, offsets, zpage), "dW_out");
+  } else {
+    LMOE_HIP((bg<BG_GROUP_K, 1, 0, 1, 0>(bop(dO, L, 0, nullptr, 1, 1), bop(A, I, 0, nullptr, 1, 1), gr->dw_out, I, L, I,
+                                         0, 0, st, sh, 0, (int64_t)L * I, offsets)),
+             "dW_out");
+  }
   LMOE_HIP(bw_situ(1, G, V, dA, dG, dV, (int64_t)tk * I, sh, st), "SiTU-GLU gradient");
   if (tgrad) {
     LMOE_HIP(expert_tgrad(cx, offsets, tiles2, tc2, L, dG, w->w_gate, I, dV, w->w_value, I, zr), "dz rows");
@@ -1188,12 +1231,17 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
                                          1, st, sh, 0, 0, offsets, tiles, tc)),
              "dz rows (value)");
   }
-  LMOE_HIP((bg<BG_GROUP_K, 1, 0, 1, 0>(bop(dG, I, 0, nullptr, 1, 1), bop(zsrc, L, 0, sorted, k, 1), gr->dw_gate, L, I, L,
-                                       0, 0, st, sh, 0, (int64_t)I * L, offsets)),
-           "dW_gate");
-  LMOE_HIP((bg<BG_GROUP_K, 1, 0, 1, 0>(bop(dV, I, 0, nullptr, 1, 1), bop(zsrc, L, 0, sorted, k, 1), gr->dw_value, L, I, L,
-                                       0, 0, st, sh, 0, (int64_t)I * L, offsets)),
-           "dW_value");
+  if (wg3) {
+    LMOE_HIP(wgrad(cx, dG, I, zsrc, L, sorted, k, gr->dw_gate, I, L, offsets, zpage), "dW_gate");
+    LMOE_HIP(wgrad(cx, dV, I, zsrc, L, sorted, k, gr->dw_value, I, L, offsets, zpage), "dW_value");
+  } else {
+    LMOE_HIP((bg<BG_GROUP_K, 1, 0, 1, 0>(bop(dG, I, 0, nullptr, 1, 1), bop(zsrc, L, 0, sorted, k, 1), gr->dw_gate, L, I,
+                                         L, 0, 0, st, sh, 0, (int64_t)I * L, offsets)),
+             "dW_gate");
+    LMOE_HIP((bg<BG_GROUP_K, 1, 0, 1, 0>(bop(dV, I, 0, nullptr, 1, 1), bop(zsrc, L, 0, sorted, k, 1), gr->dw_value, L, I,
+                                         L, 0, 0, st, sh, 0, (int64_t)I * L, offsets)),
+             "dW_value");
+  }
   if (lmoe_status s = record(ev, 3, st)) return s;
   // --- latent projection and dx --------------------------------------------
   if (T > 0) {

@@ -63,6 +63,11 @@ _LIST = [
                 act="bf16", w_expert="f8", seed=4),
     LayerConfig("small_w8a8", T=301, H=512, L=256, E=20, k=4, S=2, I=256, Is=128,
                 act="bf16", w_expert="f8", seed=4, a8=True),
+    # Whole 256-wide expert matrices (I, L multiples of 256) above 256 tokens,
+    # with more experts than the batch fills: the backward's persistent
+    # expert-gradient kernels, experts without rows included.
+    LayerConfig("small_wide_bf16", T=300, H=512, L=512, E=160, k=2, S=1, I=256, Is=128,
+                act="bf16", w_expert="bf16", seed=9),
     LayerConfig("small_identity_bf16", T=130, H=256, L=256, E=12, k=3, S=1, I=128,
                 Is=128, act="bf16", w_expert="bf16", seed=5, identity_proj=True),
     # Every expert selected (k == E) and no shared expert.

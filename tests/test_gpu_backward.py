@@ -64,15 +64,24 @@ def _run(cfg, dev):
     return grads, ref, worst
 
 
-@pytest.mark.parametrize("name,T", [("small_bf16", None), ("small_identity_bf16", None), ("small_full_k", None),
-                                    ("small_bf16", 40), ("small_bf16", 700)])
-def test_backward_matches_oracle(dev, name, T):
+@pytest.mark.parametrize("name,T,E", [("small_bf16", None, None), ("small_identity_bf16", None, None),
+                                      ("small_full_k", None, None), ("small_bf16", 40, None), ("small_bf16", 700, None),
+                                      ("small_wide_bf16", None, None), ("small_wide_bf16", 700, 8)])
+def test_backward_matches_oracle(dev, name, T, E):
+    """small_wide_bf16 runs the persistent expert-gradient kernels: at its own
+    size some of the 160 experts get no rows (their weight gradients must be
+    exact zeros), and at T = 700 over 8 experts each expert spans several
+    64-row k-tiles with a partial last one."""
     cfg = get_config(name)
     if T is not None:
         cfg = replace(cfg, T=T, name=f"{name}_T{T}")
+    if E is not None:
+        cfg = replace(cfg, E=E, name=f"{cfg.name}_E{E}")
     grads, ref, _ = _run(cfg, dev)
     # experts no token chose get exact zeros
     counts = np.bincount(ref["idx"].ravel(), minlength=cfg.E)
+    if name == "small_wide_bf16" and E is None:
+        assert (counts == 0).any(), "the case is meant to hold experts without rows"
     for e in np.nonzero(counts == 0)[0]:
         for n in ("dw_gate", "dw_value", "dw_out"):
             assert not grads[n][int(e)].any()
