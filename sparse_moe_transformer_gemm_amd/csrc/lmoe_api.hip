@@ -401,6 +401,39 @@ hipError_t xgemm(const Ctx& c, const void* x, float* logits, void* z, void* hs, 
   return launch_dense<Cfg, CT>(p, ft, (int)cdiv(sh->T, Cfg::BT), c.st);
 }
 
+// Two fp32 products of x in one pass: out_s = x . w_s^T ([T, rows_s], row
+// pitch rows_s) -- the backward's shared gate and value pre-activations.
+template <class Cfg, typename CT>
+hipError_t xgemm_f32x2(const Ctx& c, const void* x, const void* w0, float* out0, int rows0, const void* w1, float* out1,
+                       int rows1) {
+  const lmoe_shape* sh = c.sh;
+  DenseXProb<Cfg, CT> p{};
+  p.x = static_cast<const char*>(x);
+  p.T = sh->T;
+  p.K = sh->H;
+  p.cap = sh->cap;
+  p.inv_cap = c.inv_cap();
+  int ft = 0;
+  const void* ws[2] = {w0, w1};
+  float* os[2] = {out0, out1};
+  const int rs[2] = {rows0, rows1};
+  for (int i = 0; i < 2; ++i) {
+    NSeg& s = p.seg[i];
+    s = NSeg{};
+    s.w = static_cast<const char*>(ws[i]);
+    s.out = reinterpret_cast<char*>(os[i]);
+    s.ldo = rs[i];
+    s.rows = rs[i];
+    s.kind = EPI_F32;
+    s.vec = (rs[i] % 4) == 0;
+    s.ft0 = ft;
+    ft += (int)cdiv(rs[i], Cfg::BF);
+  }
+  if (sh->T == 0) return hipSuccess;
+  p.nseg = 2;
+  return launch_dense<Cfg, CT>(p, ft, (int)cdiv(sh->T, Cfg::BT), c.st);
+}
+
 // y = n . W_up^T + sum_s hs_s . W_so[s]^T  (n added directly when w_up is NULL).
 template <class Cfg, typename CT>
 hipError_t upgemm(const Ctx& c, const void* n, const void* hs, void* y) {
@@ -1147,10 +1180,9 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   // --- forward, keeping what the gradients need ---------------------------
   if (lmoe_status s = record(ev, 0, st)) return s;
   if (T > 0) {
-    LMOE_HIP((bg<BG_DENSE, 0, 0, 0, 0>(bop(x, H), bop(w->w_router, H), logits, E, T, E, H, 0, st, sh)), "router");
-    if (w->w_down)
-      LMOE_HIP((bg<BG_DENSE, 0, 0, 0, 0>(bop(x, H), bop(w->w_down, H), at<void>(ws, pl.z), L, T, L, H, 0, st, sh, 1)),
-               "latent down");
+    // router logits and z through the forward's route GEMM (the same kernels
+    // and tiles as lmoe_forward, so the same sums)
+    LMOE_HIP(xgemm_any<bf16>(cx, x, logits, w->w_down ? at<void>(ws, pl.z) : nullptr, nullptr), "router + latent down");
     LMOE_HIP(launch_topk(logits, w->b_router, sh->T, E, k, idx, tw, st), "top-k");
   }
   LMOE_HIP(launch_permute(idx, sh->T, E, k, at<int32_t>(ws, pl.bcounts), offsets, sorted, pos, st), "permute");
@@ -1263,8 +1295,12 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   if (lmoe_status s = record(ev, 4, st)) return s;
   // --- shared experts ---------------------------------------------------------
   if (S > 0) {
-    LMOE_HIP((bg<BG_DENSE, 0, 0, 0, 0>(bop(x, H), bop(w->ws_gate, H), gs, sis, T, sis, H, 0, st, sh)), "shared gate");
-    LMOE_HIP((bg<BG_DENSE, 0, 0, 0, 0>(bop(x, H), bop(w->ws_value, H), vs, sis, T, sis, H, 0, st, sh)), "shared value");
+    if (T > 256) {
+      LMOE_HIP((xgemm_f32x2<T2Dense, bf16>(cx, x, w->ws_gate, gs, sis, w->ws_value, vs, sis)), "shared gate + value");
+    } else {
+      LMOE_HIP((bg<BG_DENSE, 0, 0, 0, 0>(bop(x, H), bop(w->ws_gate, H), gs, sis, T, sis, H, 0, st, sh)), "shared gate");
+      LMOE_HIP((bg<BG_DENSE, 0, 0, 0, 0>(bop(x, H), bop(w->ws_value, H), vs, sis, T, sis, H, 0, st, sh)), "shared value");
+    }
     LMOE_HIP(bw_situ(0, gs, vs, nullptr, hs, nullptr, (int64_t)T * sis, sh, st), "shared SiTU-GLU");
     for (int s = 0; s < S; ++s) {
       const char* wso = static_cast<const char*>(w->ws_out) + (size_t)s * H * Is * 2;
