@@ -533,6 +533,68 @@ struct ExpertTGradProb {
   __device__ __forceinline__ void epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const;
 };
 
+// Backward data gradients of the dense projections on the persistent engine
+// (Tile3 WTR): C[t, f] = sum over the K segments s of X_s[t, k] W_s[k, f],
+// with each W_s read as the forward stores it (features contiguous) and
+// transposed between LDS and the MFMAs.  The F features may span several
+// matrices of fsplit features each (a stack, wms elements apart: the shared
+// experts' out matrices); a 256-wide feature tile lies in one of them.
+//   dn = dy W_up;  dh = dy [W_so[0] | W_so[1] ...];
+//   dx = dz W_dn + dg_s W_sg + dv_s W_sv  (three K segments)
+// X_s: bf16 [T, ldx], C: fp32 [T, ldo].
+template <class Cfg, typename CT>
+struct DenseTProb {
+  static constexpr bool kDenseRows = false;
+  int64_t T;
+  int F, fsplit;      // features; features per stacked matrix
+  int nks, ntt, nft;
+  const char* x[3];
+  int64_t ldx[3];
+  int kd[3];
+  const char* w[3];   // W_s: [K_s, fsplit] per matrix, matrices wms[s] elements apart
+  int64_t wms[3];
+  float* out;
+  int64_t ldo;
+  int accumulate;     // C += instead of C =
+
+  struct State {
+    int tt, ft;
+  };
+  __device__ int num_logical() const { return ntt * nft; }
+  // feature tiles outermost: neighbouring work-groups share a weight tile
+  __device__ bool setup_lg(int lg, State& st) const {
+    if (lg >= ntt * nft) return false;
+    st.ft = lg / ntt;
+    st.tt = lg - st.ft * ntt;
+    return true;
+  }
+  __device__ bool setup(int bid, State& st) const { return setup_lg(bid, st); }
+  __device__ int num_ksegs() const { return nks; }
+  __device__ int seg_ktiles(int s) const { return kd[s] * (int)sizeof(CT) / 128; }
+  __device__ bool seg_f8(const State&, int) const { return false; }
+  __device__ int tokens_valid(const State& st) const { return (int)imin64(Cfg::BT, T - (int64_t)st.tt * Cfg::BT); }
+  __device__ int feats_valid(const State& st) const { return min(Cfg::BF, F - st.ft * Cfg::BF); }
+  __device__ const char* x_row(const State& st, int s, int r) const {
+    const int64_t t = (int64_t)st.tt * Cfg::BT + r;
+    return t < T ? x[s] + t * ldx[s] * (int64_t)sizeof(CT) : nullptr;
+  }
+  template <int RPI = 8>
+  __device__ const char* x_row_grp(const State& st, int s, int r0, int lane) const {
+    return x_row(st, s, min(r0 + lane / (64 / RPI), tokens_valid(st) - 1));
+  }
+  // as ExpertTGradProb::w_tsrc; chunks past F read the tile's last chunk
+  __device__ const char* w_tsrc(const State& st, int s, int kr, int c) const {
+    const int f = min(st.ft * Cfg::BF + 8 * c, F - 8);
+    const int g = f / fsplit, fl = f - g * fsplit;
+    return w[s] + ((int64_t)g * wms[s] + (int64_t)kr * fsplit + fl) * (int64_t)sizeof(CT);
+  }
+  __device__ int64_t w_tstep(const State&, int) const { return (int64_t)64 * fsplit * sizeof(CT); }
+  __device__ const char* w_row(const State&, int, int, const float**) const { return nullptr; }
+  __device__ const char* w_block(const State&) const { return nullptr; }
+  template <class Acc>
+  __device__ __forceinline__ void epilogue(const State& st, const Acc& acc, int wf0, int wt0, int lane) const;
+};
+
 // ---------------------------------------------------------------------------
 // The mainloop.
 // ---------------------------------------------------------------------------
@@ -889,6 +951,28 @@ __device__ __forceinline__ void ExpertTGradProb<Cfg, CT>::epilogue(const State& 
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r];
       store4<float>(out + (int64_t)(st.m0 + tl) * F, st.ft * Cfg::BF + fl, v, F, true);
+    }
+  });
+}
+
+template <class Cfg, typename CT>
+template <class Acc>
+__device__ __forceinline__ void DenseTProb<Cfg, CT>::epilogue(const State& st, const Acc& acc, int wf0, int wt0,
+                                                              int lane) const {
+  const int tv = tokens_valid(st);
+  for_acc<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int fl, int tl) __attribute__((always_inline)) {
+    if (tl < tv) {
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r];
+      float* row = out + ((int64_t)st.tt * Cfg::BT + tl) * ldo;
+      const int f = st.ft * Cfg::BF + fl;
+      if (accumulate) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (f + r < F) v[r] += row[f + r];
+      }
+      store4<float>(row, f, v, F, (ldo & 3) == 0);
     }
   });
 }

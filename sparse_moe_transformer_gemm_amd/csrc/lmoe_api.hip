@@ -550,6 +550,35 @@ hipError_t expert_tgrad(const Ctx& c, const int32_t* offsets, const int4* tiles,
   return launch_gemm<Cfg, bf16>(p, pad8(max_tiles(sh, Cfg::BT) * p.et.nft), c.st);
 }
 
+// Backward data gradients of the dense projections on the persistent engine
+// with transposed weight stages: out (+)= sum_s x_s . W_s, x_s bf16 [T, ldx_s]
+// with K_s columns, W_s bf16 [K_s, fsplit] per stacked matrix (wms_s
+// elements apart), F features, out fp32 [T, ldo].
+hipError_t dense_tgrad(const Ctx& c, int nks, const void* const* x, const int64_t* ldx, const int* kd,
+                       const void* const* w, const int64_t* wms, int F, int fsplit, float* out, int64_t ldo,
+                       int accumulate) {
+  using Cfg = T2ExpertTGrad;
+  DenseTProb<Cfg, bf16> p{};
+  p.T = c.sh->T;
+  p.F = F;
+  p.fsplit = fsplit;
+  p.nks = nks;
+  p.ntt = (int)cdiv(c.sh->T, Cfg::BT);
+  p.nft = (int)cdiv(F, Cfg::BF);
+  for (int s = 0; s < nks; ++s) {
+    p.x[s] = static_cast<const char*>(x[s]);
+    p.ldx[s] = ldx[s];
+    p.kd[s] = kd[s];
+    p.w[s] = static_cast<const char*>(w[s]);
+    p.wms[s] = wms[s];
+  }
+  p.out = out;
+  p.ldo = ldo;
+  p.accumulate = accumulate;
+  if (c.sh->T == 0) return hipSuccess;
+  return launch_gemm<Cfg, bf16>(p, persistent_grid(), c.st);
+}
+
 // Expert weight gradients on the persistent pipeline: C_e = P_e^T Q_e for
 // every expert (wgrad.hpp).
 hipError_t wgrad(const Ctx& c, const void* pm, int64_t ldp, const void* qn, int64_t ldq, const int32_t* gather, int gk,
@@ -1131,6 +1160,9 @@ lmoe_status lmoe_quantize_1x128(const void* x, int64_t R, int32_t C, void* q, fl
 #ifndef LMOE_BW_WGRAD
 #define LMOE_BW_WGRAD 1
 #endif
+#ifndef LMOE_BW_DENSE_TGRAD
+#define LMOE_BW_DENSE_TGRAD 1
+#endif
 size_t lmoe_backward_workspace_bytes(const lmoe_shape* sh) {
   if (check_shape(sh) != LMOE_OK) return 0;
   return bplan(sh).total;
@@ -1202,8 +1234,19 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
 
   if (lmoe_status s = record(ev, 1, st)) return s;
   // --- up-projection ------------------------------------------------------
+  // dense data gradients on the persistent engine above 256 tokens
+  const bool dtg = T > 256 && LMOE_BW_DENSE_TGRAD;
   if (w->w_up) {
-    LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dy, H), bop(w->w_up, L), dn, L, T, L, H, 0, st, sh)), "dn");
+    if (dtg) {
+      const void* xs[1] = {dy};
+      const int64_t lx[1] = {H};
+      const int kd[1] = {H};
+      const void* wsrc[1] = {w->w_up};
+      const int64_t wm[1] = {0};
+      LMOE_HIP(dense_tgrad(cx, 1, xs, lx, kd, wsrc, wm, L, L, dn, L, 0), "dn");
+    } else {
+      LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dy, H), bop(w->w_up, L), dn, L, T, L, H, 0, st, sh)), "dn");
+    }
     LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dy, H), bop(n, L), gr->dw_up, L, H, L, T, 0, st, sh)), "dW_up");
   } else if (T > 0) {
     hipLaunchKernelGGL(bw_widen_kernel, dim3((unsigned)cdiv((int64_t)T * L, 256)), dim3(256), 0, st,
@@ -1282,7 +1325,16 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
     LMOE_HIP(hipGetLastError(), "dz");
   }
   if (w->w_down) {
-    LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dz, L), bop(w->w_down, H), gr->dx, H, T, H, L, 0, st, sh)), "dx (latent)");
+    if (dtg) {
+      const void* xs[1] = {dz};
+      const int64_t lx[1] = {L};
+      const int kd[1] = {L};
+      const void* wsrc[1] = {w->w_down};
+      const int64_t wm[1] = {0};
+      LMOE_HIP(dense_tgrad(cx, 1, xs, lx, kd, wsrc, wm, H, H, gr->dx, H, 0), "dx (latent)");
+    } else {
+      LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dz, L), bop(w->w_down, H), gr->dx, H, T, H, L, 0, st, sh)), "dx (latent)");
+    }
     LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dz, L), bop(x, H), gr->dw_down, H, L, H, T, 0, st, sh)), "dW_down");
   }
   // --- router ---------------------------------------------------------------
@@ -1302,19 +1354,40 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
       LMOE_HIP((bg<BG_DENSE, 0, 0, 0, 0>(bop(x, H), bop(w->ws_value, H), vs, sis, T, sis, H, 0, st, sh)), "shared value");
     }
     LMOE_HIP(bw_situ(0, gs, vs, nullptr, hs, nullptr, (int64_t)T * sis, sh, st), "shared SiTU-GLU");
+    // dh = dy [W_so[0] | W_so[1] ...] in one pass (a feature tile may span
+    // two matrices: each 8-feature chunk finds its own)
+    const bool dh1 = dtg;
+    if (dh1) {
+      const void* xs[1] = {dy};
+      const int64_t lx[1] = {H};
+      const int kd[1] = {H};
+      const void* wsrc[1] = {w->ws_out};
+      const int64_t wm[1] = {(int64_t)H * Is};
+      LMOE_HIP(dense_tgrad(cx, 1, xs, lx, kd, wsrc, wm, sis, Is, dhs, sis, 0), "shared dh");
+    }
     for (int s = 0; s < S; ++s) {
       const char* wso = static_cast<const char*>(w->ws_out) + (size_t)s * H * Is * 2;
-      LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dy, H), bop(wso, Is), dhs + (size_t)s * Is, sis, T, Is, H, 0, st, sh)),
-               "shared dh");
+      if (!dh1)
+        LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dy, H), bop(wso, Is), dhs + (size_t)s * Is, sis, T, Is, H, 0, st, sh)),
+                 "shared dh");
       LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dy, H), bop(hs + (size_t)s * Is, sis), gr->dws_out + (size_t)s * H * Is, Is,
                                          H, Is, T, 0, st, sh)),
                "dWs_out");
     }
     LMOE_HIP(bw_situ(1, gs, vs, dhs, dgs, dvs, (int64_t)T * sis, sh, st), "shared SiTU-GLU gradient");
-    LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dgs, sis), bop(w->ws_gate, H), gr->dx, H, T, H, sis, 1, st, sh)),
-             "dx (shared gate)");
-    LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dvs, sis), bop(w->ws_value, H), gr->dx, H, T, H, sis, 1, st, sh)),
-             "dx (shared value)");
+    if (dtg) {
+      const void* xs[2] = {dgs, dvs};
+      const int64_t lx[2] = {sis, sis};
+      const int kd[2] = {sis, sis};
+      const void* wsrc[2] = {w->ws_gate, w->ws_value};
+      const int64_t wm[2] = {0, 0};
+      LMOE_HIP(dense_tgrad(cx, 2, xs, lx, kd, wsrc, wm, H, H, gr->dx, H, 1), "dx (shared)");
+    } else {
+      LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dgs, sis), bop(w->ws_gate, H), gr->dx, H, T, H, sis, 1, st, sh)),
+               "dx (shared gate)");
+      LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dvs, sis), bop(w->ws_value, H), gr->dx, H, T, H, sis, 1, st, sh)),
+               "dx (shared value)");
+    }
     LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dgs, sis), bop(x, H), gr->dws_gate, H, sis, H, T, 0, st, sh)), "dWs_gate");
     LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dvs, sis), bop(x, H), gr->dws_value, H, sis, H, T, 0, st, sh)), "dWs_value");
   }

@@ -67,10 +67,13 @@ __device__ __forceinline__ void mma_ktile_tt(f32x16 (&acc)[FI][TI], const char* 
     for (int i = 0; i < FI; ++i) a[i] = frag(sW, kr, wf0 + i * 32);
 #pragma unroll
     for (int j = 0; j < TI; ++j) b[j] = frag(sX, kr, wt0 + j * 32);
+    // P side as the MFMA's A operand: a block's output rows (registers) run
+    // along m and its columns (lanes) along n, so each accumulator register
+    // holds 32 consecutive n of one row m per half-wave
 #pragma unroll
     for (int j = 0; j < TI; ++j)
 #pragma unroll
-      for (int i = 0; i < FI; ++i) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+      for (int i = 0; i < FI; ++i) acc[i][j] = mfma32(b[j], a[i], acc[i][j]);
   }
 }
 
@@ -182,13 +185,18 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
   T ct = xt;
   int cj = 0, ckt = 0;
   auto finish = [&]() __attribute__((always_inline)) {
-    float* ce = p.c + (int64_t)ct.e * p.M * p.N;
-    for_acc<Cfg>(wf0, wt0, lane, [&](int i, int j, int g, int fl, int tl) __attribute__((always_inline)) {
-      float v[4];
+    // block (i, j), register 4 g + r: row m = wt0 + 32 j + 8 g + 4 (lane / 32)
+    // + r, column n = wf0 + 32 i + lane % 32; one store instruction writes two
+    // 128-byte row segments
+    float* ce = p.c + (int64_t)ct.e * p.M * p.N + ((int64_t)ct.m0 + wt0 + 4 * (lane >> 5)) * p.N + ct.n0 + wf0 + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r];
-      store4<float>(ce + (int64_t)(ct.m0 + tl) * p.N, ct.n0 + fl, v, p.N, true);
-    });
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < TI; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ce[(int64_t)(32 * j + 8 * g + r) * p.N + 32 * i] = acc[i][j][4 * g + r];
   };
 
   // prologue and iterations as gemm3p_kernel: X(0), W(0), W(1); iteration g

@@ -87,6 +87,14 @@ def test_backward_matches_oracle(dev, name, T, E):
             assert not grads[n][int(e)].any()
 
 
+def test_backward_ragged_dense_tiles(dev):
+    """H = 576 and S * Is = 2 * 192 leave the dense data gradients (dx, dh)
+    with a partial last 256-feature tile, and one tile of dh spans both
+    shared experts' out matrices."""
+    cfg = replace(get_config("small_bf16"), T=700, H=576, Is=192, name="small_bf16_T700_H576_Is192")
+    _run(cfg, dev)
+
+
 def test_backward_empty_batch(dev):
     cfg = replace(get_config("small_bf16"), T=0, name="small_bf16_T0")
     t, g = make_case(cfg, dev)
