@@ -180,9 +180,24 @@ __device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
 // 16 bytes per lane from `g` into LDS at `lds` + 16 * lane (lds wave-uniform).
 // A __device__ function, not a lambda: lambdas are also compiled for the host,
 // where the builtin does not exist.
+//
+// With the default cache policy the instruction is written out (M0 = the LDS
+// address) instead of issued through the builtin: after a builtin LDS DMA the
+// compiler puts an s_waitcnt vmcnt(0) in front of the next transposed
+// (ds_read_b64_tr_b16) or e4m3 LDS read it cannot tell apart from the DMA's
+// target, which drains the whole ring once per k-tile.  The kernels' own
+// s_waitcnt + s_barrier at the top of each k-tile order every LDS read after
+// the DMA that fills its stage, so no compiler wait is needed.
+__device__ __forceinline__ uint32_t lds_u32(const char* lds) {
+  return (uint32_t)(uintptr_t)(lds_void*)lds;
+}
 template <int AUX>
 __device__ __forceinline__ void dma16(const char* g, char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, AUX);
+  if constexpr (AUX == 0) {
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_u32(lds)) : "memory");
+  } else {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, AUX);
+  }
 }
 
 // Packs the routed expert weights into 32 KB blocks, each the LDS image of
@@ -224,9 +239,10 @@ __global__ __launch_bounds__(256) void pack_experts_kernel(const char* wg, const
   }
 }
 
-// 4 bytes per lane from `g` into LDS at `lds` + 4 * lane (lds wave-uniform).
+// 4 bytes per lane from `g` into LDS at `lds` + 4 * lane (lds wave-uniform);
+// written out like dma16.
 __device__ __forceinline__ void dma4(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_u32(lds)) : "memory");
 }
 
 // Stacked e4m3 matrices [n, R, C] with one fp32 scale per 128x128 block
