@@ -579,13 +579,8 @@ hipError_t dense_tgrad(const Ctx& c, int nks, const void* const* x, const int64_
   return launch_gemm<Cfg, bf16>(p, persistent_grid(), c.st);
 }
 
-// Expert weight gradients on the persistent pipeline: C_e = P_e^T Q_e for
-// every expert (wgrad.hpp).
-hipError_t wgrad(const Ctx& c, const void* pm, int64_t ldp, const void* qn, int64_t ldq, const int32_t* gather, int gk,
-                 float* out, int M, int N, const int32_t* offsets, const void* zero) {
+hipError_t launch_wgrad(const Ctx& c, const WGradArgs& a) {
   using Cfg = TWGrad;
-  WGradArgs a{static_cast<const char*>(pm), ldp, static_cast<const char*>(qn), ldq, gather, gk, out, M, N,
-              c.sh->E, offsets, static_cast<const char*>(zero)};
   auto kern = wgrad3p_kernel<Cfg>;
   static std::once_flag once[kMaxDevices];
   static hipError_t attr[kMaxDevices];
@@ -604,6 +599,53 @@ hipError_t wgrad(const Ctx& c, const void* pm, int64_t ldp, const void* qn, int6
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)persistent_grid()), dim3(Cfg::NT), Cfg::LDS, c.st, a);
   return hipGetLastError();
+}
+
+// Expert weight gradients on the persistent pipeline: C_e = P_e^T Q_e for
+// every expert (wgrad.hpp); M and N multiples of 256.
+hipError_t wgrad(const Ctx& c, const void* pm, int64_t ldp, const void* qn, int64_t ldq, const int32_t* gather, int gk,
+                 float* out, int M, int N, const int32_t* offsets, const void* zero) {
+  WGradArgs a{};
+  a.p = static_cast<const char*>(pm);
+  a.ldp = ldp;
+  a.q = static_cast<const char*>(qn);
+  a.ldq = ldq;
+  a.gather_q = gather;
+  a.gk = gk;
+  a.c = out;
+  a.M = M;
+  a.N = N;
+  a.E = c.sh->E;
+  a.offsets = offsets;
+  a.zero = static_cast<const char*>(zero);
+  return launch_wgrad(c, a);
+}
+
+// Dense weight gradients C_s = P_s^T Q_s over all T rows, up to kWgSegs in
+// one launch (wgrad.hpp); each M and N a multiple of 256.
+struct WgDense {
+  const void* p;
+  int64_t ldp;
+  const void* q;
+  int64_t ldq;
+  float* c;
+  int M, N;
+};
+hipError_t wgrad_dense(const Ctx& c, const WgDense* d, int n, const void* zero) {
+  if (n < 1 || n > kWgSegs) return hipErrorInvalidValue;
+  WGradArgs a{};
+  a.nseg = n;
+  a.rows = (int)c.sh->T;
+  a.zero = static_cast<const char*>(zero);
+  int tiles = 0;
+  for (int s = 0; s < n; ++s) {
+    if (d[s].M % 256 || d[s].N % 256) return hipErrorInvalidValue;
+    a.seg[s] = WgSeg{static_cast<const char*>(d[s].p), static_cast<const char*>(d[s].q), d[s].c, d[s].ldp, d[s].ldq,
+                     d[s].M, d[s].N, tiles};
+    tiles += (d[s].M / 256) * (d[s].N / 256);
+  }
+  a.tiles = tiles;
+  return launch_wgrad(c, a);
 }
 
 // Gate and value pre-activations (fp32, assignment order) for the backward's
@@ -1163,6 +1205,9 @@ lmoe_status lmoe_quantize_1x128(const void* x, int64_t R, int32_t C, void* q, fl
 #ifndef LMOE_BW_DENSE_TGRAD
 #define LMOE_BW_DENSE_TGRAD 1
 #endif
+#ifndef LMOE_BW_DENSE_WGRAD
+#define LMOE_BW_DENSE_WGRAD 1
+#endif
 size_t lmoe_backward_workspace_bytes(const lmoe_shape* sh) {
   if (check_shape(sh) != LMOE_OK) return 0;
   return bplan(sh).total;
@@ -1236,6 +1281,16 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   // --- up-projection ------------------------------------------------------
   // dense data gradients on the persistent engine above 256 tokens
   const bool dtg = T > 256 && LMOE_BW_DENSE_TGRAD;
+  // The dense weight gradients whose matrices are whole 256 x 256 tiles are
+  // queued and run together at the end on the persistent weight-gradient
+  // pipeline (their inputs all stay in the workspace until then).
+  WgDense dseg[kWgSegs];
+  int nd = 0;
+  auto add_dense = [&](const void* pp, int64_t ldp, const void* qq, int64_t ldq, float* cc, int M, int N) {
+    if (!(T > 256 && LMOE_BW_DENSE_WGRAD) || M % 256 || N % 256 || nd == kWgSegs) return false;
+    dseg[nd++] = WgDense{pp, ldp, qq, ldq, cc, M, N};
+    return true;
+  };
   if (w->w_up) {
     if (dtg) {
       const void* xs[1] = {dy};
@@ -1247,7 +1302,8 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
     } else {
       LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dy, H), bop(w->w_up, L), dn, L, T, L, H, 0, st, sh)), "dn");
     }
-    LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dy, H), bop(n, L), gr->dw_up, L, H, L, T, 0, st, sh)), "dW_up");
+    if (!add_dense(dy, H, n, L, gr->dw_up, H, L))
+      LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dy, H), bop(n, L), gr->dw_up, L, H, L, T, 0, st, sh)), "dW_up");
   } else if (T > 0) {
     hipLaunchKernelGGL(bw_widen_kernel, dim3((unsigned)cdiv((int64_t)T * L, 256)), dim3(256), 0, st,
                        static_cast<const unsigned short*>(dy), dn, (int64_t)T * L);
@@ -1284,10 +1340,11 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   // their matrices are whole 256 x 256 tiles.
   const bool wg3 = T > 256 && I % 256 == 0 && L % 256 == 0 && LMOE_BW_WGRAD;
   void* zpage = at<void>(ws, pl.zpage);
-  if (wg3) {
+  auto zero_page = [&]() -> hipError_t {
     hipLaunchKernelGGL(zero_page_kernel, dim3(1), dim3(128), 0, st, static_cast<uint32_t*>(zpage));
-    LMOE_HIP(hipGetLastError(), "zero page");
-  }
+    return hipGetLastError();
+  };
+  if (wg3) LMOE_HIP(zero_page(), "zero page");
   if (wg3) {
     LMOE_HIP(wgrad(cx, dO, L, A, I, nullptr, 1, gr->dw_out, L, I, offsets, zpage), "dW_out");
   } else {
@@ -1335,7 +1392,8 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
     } else {
       LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dz, L), bop(w->w_down, H), gr->dx, H, T, H, L, 0, st, sh)), "dx (latent)");
     }
-    LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dz, L), bop(x, H), gr->dw_down, H, L, H, T, 0, st, sh)), "dW_down");
+    if (!add_dense(dz, L, x, H, gr->dw_down, L, H))
+      LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dz, L), bop(x, H), gr->dw_down, H, L, H, T, 0, st, sh)), "dW_down");
   }
   // --- router ---------------------------------------------------------------
   if (T > 0) {
@@ -1370,9 +1428,10 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
       if (!dh1)
         LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dy, H), bop(wso, Is), dhs + (size_t)s * Is, sis, T, Is, H, 0, st, sh)),
                  "shared dh");
-      LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dy, H), bop(hs + (size_t)s * Is, sis), gr->dws_out + (size_t)s * H * Is, Is,
-                                         H, Is, T, 0, st, sh)),
-               "dWs_out");
+      if (!add_dense(dy, H, hs + (size_t)s * Is, sis, gr->dws_out + (size_t)s * H * Is, H, Is))
+        LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dy, H), bop(hs + (size_t)s * Is, sis), gr->dws_out + (size_t)s * H * Is,
+                                           Is, H, Is, T, 0, st, sh)),
+                 "dWs_out");
     }
     LMOE_HIP(bw_situ(1, gs, vs, dhs, dgs, dvs, (int64_t)T * sis, sh, st), "shared SiTU-GLU gradient");
     if (dtg) {
@@ -1388,8 +1447,14 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
       LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dvs, sis), bop(w->ws_value, H), gr->dx, H, T, H, sis, 1, st, sh)),
                "dx (shared value)");
     }
-    LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dgs, sis), bop(x, H), gr->dws_gate, H, sis, H, T, 0, st, sh)), "dWs_gate");
-    LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dvs, sis), bop(x, H), gr->dws_value, H, sis, H, T, 0, st, sh)), "dWs_value");
+    if (!add_dense(dgs, sis, x, H, gr->dws_gate, sis, H))
+      LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dgs, sis), bop(x, H), gr->dws_gate, H, sis, H, T, 0, st, sh)), "dWs_gate");
+    if (!add_dense(dvs, sis, x, H, gr->dws_value, sis, H))
+      LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dvs, sis), bop(x, H), gr->dws_value, H, sis, H, T, 0, st, sh)), "dWs_value");
+  }
+  if (nd > 0) {
+    if (!wg3) LMOE_HIP(zero_page(), "zero page");
+    LMOE_HIP(wgrad_dense(cx, dseg, nd, zpage), "dense weight gradients");
   }
   if (lmoe_status s = record(ev, 5, st)) return s;
   return LMOE_OK;

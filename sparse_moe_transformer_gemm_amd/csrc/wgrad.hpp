@@ -1,5 +1,6 @@
-// Weight gradients of the routed experts on a persistent DMA pipeline
-// (gfx950).
+// Weight gradients on a persistent DMA pipeline (gfx950): the routed
+// experts', and in a second mode up to kWgSegs dense products over all T rows
+// in one launch (the dense projections' weight gradients).
 //
 //   C_e[m, n] = sum over expert e's assignment rows t of P[t, m] Q[t, n]
 //
@@ -26,7 +27,21 @@
 
 namespace lmoe {
 
+constexpr int kWgSegs = 12;
+
+// A dense product C = P^T Q over all rows [0, rows) of P [rows, ldp] and
+// Q [rows, ldq] (bf16), C fp32 [M, N] row-major; M and N multiples of 256.
+struct WgSeg {
+  const char* p;
+  const char* q;
+  float* c;
+  int64_t ldp, ldq;
+  int M, N;
+  int first;  // first logical tile of the segment
+};
+
 struct WGradArgs {
+  // routed experts (nseg == 0)
   const char* p;          // P rows, assignment order, bf16 [T*k, ldp]
   int64_t ldp;
   const char* q;          // Q rows, bf16 [rows, ldq]
@@ -36,6 +51,11 @@ struct WGradArgs {
   float* c;               // C_e at c + e * M * N, row-major [M, N]
   int M, N, E;
   const int* offsets;     // [E + 1]
+  // dense segments (nseg > 0), all in one launch
+  int nseg;
+  int rows;
+  int tiles;              // logical tiles over all segments
+  WgSeg seg[kWgSegs];
   const char* zero;       // 512 zero bytes
 };
 
@@ -87,9 +107,8 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
   const int wf0 = (wid % Cfg::WF) * Cfg::FW;  // columns n of the tile (Q side, MFMA A operand)
   const int wt0 = (wid / Cfg::WF) * Cfg::TW;  // rows m of the tile (P side, MFMA B operand)
 
-  // logical tiles: expert-major, then m tiles, then n tiles
-  const int ntm = p.M / 256, ntn = p.N / 256, per_e = ntm * ntn;
-  const int R = p.E * per_e;
+  // logical tiles, dealt to the XCDs in contiguous ranges
+  const int R = p.nseg == 0 ? p.E * (p.M / 256) * (p.N / 256) : p.tiles;
   const int per = (R + kXcds - 1) / kXcds;
   const int nslot = (int)gridDim.x / kXcds;
   const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
@@ -98,17 +117,46 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
   if (ntile == 0) return;
 
   struct T {
-    int e, m0, n0, off, rows, nkt;
+    const char* pb;  // P at (the tile's first row, column m0)
+    const char* qb;  // Q at column n0 (row index absolute)
+    float* cb;       // C at (m0, n0)
+    int64_t ldp, ldq, ldc;
+    int off, rows, nkt;
   };
+  // experts: expert-major, then m tiles, then n tiles; dense: segment after
+  // segment, m tiles, then n tiles
   auto locate = [&](int j, T& t) __attribute__((always_inline)) {
     const int lg = xcd * per + slot + j * nslot;
-    t.e = lg / per_e;
-    const int rem = lg - t.e * per_e;
-    t.m0 = (rem / ntn) * 256;
-    t.n0 = (rem % ntn) * 256;
-    const i32x2 ob = sload2(p.offsets + t.e);
-    t.off = ob.x;
-    t.rows = ob.y - ob.x;
+    if (p.nseg == 0) {
+      const int ntn = p.N / 256, per_e = (p.M / 256) * ntn;
+      const int e = lg / per_e, rem = lg - e * per_e;
+      const int m0 = (rem / ntn) * 256, n0 = (rem % ntn) * 256;
+      const i32x2 ob = sload2(p.offsets + e);
+      t.off = ob.x;
+      t.rows = ob.y - ob.x;
+      t.ldp = p.ldp;
+      t.ldq = p.ldq;
+      t.ldc = p.N;
+      t.pb = p.p + ((int64_t)t.off * p.ldp + m0) * 2;
+      t.qb = p.q + (int64_t)n0 * 2;
+      t.cb = p.c + (int64_t)e * p.M * p.N + (int64_t)m0 * p.N + n0;
+    } else {
+      int s = 0;
+#pragma unroll
+      for (int u = 1; u < kWgSegs; ++u)
+        if (u < p.nseg && lg >= p.seg[u].first) s = u;
+      const WgSeg& sg = p.seg[s];
+      const int ntn = sg.N / 256, rem = lg - sg.first;
+      const int m0 = (rem / ntn) * 256, n0 = (rem % ntn) * 256;
+      t.off = 0;
+      t.rows = p.rows;
+      t.ldp = sg.ldp;
+      t.ldq = sg.ldq;
+      t.ldc = sg.N;
+      t.pb = sg.p + (int64_t)m0 * 2;
+      t.qb = sg.q + (int64_t)n0 * 2;
+      t.cb = sg.c + (int64_t)m0 * sg.N + n0;
+    }
     t.nkt = max(1, (t.rows + 63) >> 6);
   };
   int G = 0;
@@ -142,7 +190,7 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
     for (int i = 0; i < NQX; ++i) {
       const int q = wid + NW * i, kr = 2 * q + (lane >> 5), c = (lane & 31) ^ ((kr & 3) << 2);
       const int t = xk * 64 + kr;
-      const char* src = t < xt.rows ? p.p + (((int64_t)xt.off + t) * p.ldp + xt.m0 + 8 * c) * 2 : p.zero + 16 * c;
+      const char* src = t < xt.rows ? xt.pb + ((int64_t)t * xt.ldp + 8 * c) * 2 : p.zero + 16 * c;
       dma16<0>(src, base + q * 1024);
     }
     if (++xk == xt.nkt) {
@@ -161,7 +209,7 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
       int r0 = 0, r1 = 0;
       if (wt.rows > 0) {
         const int a0 = wt.off + min(t0, wt.rows - 1), a1 = wt.off + min(t0 + 1, wt.rows - 1);
-        if (p.gather_q) {
+        if (p.nseg == 0 && p.gather_q) {
           const i32x2 g = sload_pair(p.gather_q + a0, p.gather_q + a1);
           r0 = g.x / p.gk;
           r1 = g.y / p.gk;
@@ -172,7 +220,7 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
       }
       const int t = t0 + (lane >> 5);
       const int row = (lane >> 5) ? r1 : r0;
-      const char* src = t < wt.rows ? p.q + ((int64_t)row * p.ldq + wt.n0 + 8 * c) * 2 : p.zero + 16 * c;
+      const char* src = t < wt.rows ? wt.qb + ((int64_t)row * wt.ldq + 8 * c) * 2 : p.zero + 16 * c;
       dma16<0>(src, base + q * 1024);
     }
     if (++wk == wt.nkt) {
@@ -188,7 +236,7 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
     // block (i, j), register 4 g + r: row m = wt0 + 32 j + 8 g + 4 (lane / 32)
     // + r, column n = wf0 + 32 i + lane % 32; one store instruction writes two
     // 128-byte row segments
-    float* ce = p.c + (int64_t)ct.e * p.M * p.N + ((int64_t)ct.m0 + wt0 + 4 * (lane >> 5)) * p.N + ct.n0 + wf0 + (lane & 31);
+    float* ce = ct.cb + (int64_t)(wt0 + 4 * (lane >> 5)) * ct.ldc + wf0 + (lane & 31);
 #pragma unroll
     for (int i = 0; i < FI; ++i)
 #pragma unroll
@@ -196,7 +244,7 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ce[(int64_t)(32 * j + 8 * g + r) * p.N + 32 * i] = acc[i][j][4 * g + r];
+          for (int r = 0; r < 4; ++r) ce[(int64_t)(32 * j + 8 * g + r) * ct.ldc + 32 * i] = acc[i][j][4 * g + r];
   };
 
   // prologue and iterations as gemm3p_kernel: X(0), W(0), W(1); iteration g
