@@ -493,6 +493,11 @@ struct ExpertDownProb {
 //   dz rows = dG W_g[e] + dV W_v[e]   (two segments, K = I each, F = L)
 template <class Cfg, typename CT>
 struct ExpertTGradProb {
+  // vector stores (at least) a wave's epilogue issues per 32-row token block
+  // whose rows are all valid: the persistent loop's next wait lets them drain
+  // (declared where the fp32 output tile is large; on the forward's bf16
+  // expert GEMMs it measured no better)
+  static constexpr int kEpiStores = Cfg::FI * 4;
   ExpertTiles<Cfg> et;
   const char* x[2];   // [T*k, kd[s]]
   const char* w[2];   // [E, kd[s], F]
@@ -538,13 +543,14 @@ struct ExpertTGradProb {
 // with each W_s read as the forward stores it (features contiguous) and
 // transposed between LDS and the MFMAs.  The F features may span several
 // matrices of fsplit features each (a stack, wms elements apart: the shared
-// experts' out matrices); a 256-wide feature tile lies in one of them.
+// experts' out matrices); each 8-feature chunk lies in one of them.
 //   dn = dy W_up;  dh = dy [W_so[0] | W_so[1] ...];
 //   dx = dz W_dn + dg_s W_sg + dv_s W_sv  (three K segments)
 // X_s: bf16 [T, ldx], C: fp32 [T, ldo].
 template <class Cfg, typename CT>
 struct DenseTProb {
   static constexpr bool kDenseRows = false;
+  static constexpr int kEpiStores = Cfg::FI * 4;  // as ExpertTGradProb
   int64_t T;
   int F, fsplit;      // features; features per stacked matrix
   int nks, ntt, nft;

@@ -705,6 +705,41 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3_kernel(const Prob p) {
 // iteration, after its wait and barrier (with bf16 weights after that
 // iteration's DMAs, with e4m3 weights before them).
 // ---------------------------------------------------------------------------
+// Vector stores a wave's epilogue issues, at least, per 32-row token block
+// whose rows are all valid (0: not declared).
+template <class P, class = void>
+struct epi_stores : std::integral_constant<int, 0> {};
+template <class P>
+struct epi_stores<P, std::void_t<decltype(P::kEpiStores)>> : std::integral_constant<int, P::kEpiStores> {};
+
+// wait_vmcnt_barrier<min(63, (W ? NQW : 0) + NB * SB)> for a runtime NB in
+// 0 .. 4: the count past the awaited DMAs of the youngest weight tile (when
+// issued) and of the previous epilogue's stores.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_barrier_c() {
+  wait_vmcnt_barrier<(N < 63 ? N : 63)>();
+}
+template <int NQW, int SB>
+__device__ __forceinline__ void wait_past_stores(bool w, int nb) {
+  if (w) {
+    switch (nb) {
+      case 0: wait_vmcnt_barrier_c<NQW>(); break;
+      case 1: wait_vmcnt_barrier_c<NQW + SB>(); break;
+      case 2: wait_vmcnt_barrier_c<NQW + 2 * SB>(); break;
+      case 3: wait_vmcnt_barrier_c<NQW + 3 * SB>(); break;
+      default: wait_vmcnt_barrier_c<NQW + 4 * SB>(); break;
+    }
+  } else {
+    switch (nb) {
+      case 0: wait_vmcnt_barrier_c<0>(); break;
+      case 1: wait_vmcnt_barrier_c<SB>(); break;
+      case 2: wait_vmcnt_barrier_c<2 * SB>(); break;
+      case 3: wait_vmcnt_barrier_c<3 * SB>(); break;
+      default: wait_vmcnt_barrier_c<4 * SB>(); break;
+    }
+  }
+}
+
 template <class Cfg, class Prob>
 __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -894,11 +929,26 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
     p.epilogue(cst, acc, wf0, wt0, lane);
   };
   bool pending = false;  // a finished tile's accumulators await their epilogue
+  // bf16 weights: the epilogue's stores follow the iteration's DMAs, and the
+  // next wait lets those this wave certainly issued stay in flight (vector
+  // memory operations complete in issue order, so they count past X(g)):
+  // eb = the finished tile's 32-row token blocks all of whose rows, and all
+  // of the wave's features, are valid
+  constexpr int SB = Cfg::WF8 ? 0 : epi_stores<Prob>::value;
+  static_assert(SB == 0 || TI <= 4, "wait_past_stores covers four token blocks");
+  int eb = 0;
   for (int g = 0; g < G; ++g) {
-    if (g + SW - 2 < G) wait_vmcnt_barrier<NQW>();
-    else wait_vmcnt_barrier<0>();
+    if constexpr (SB > 0) {
+      wait_past_stores<NQW, SB>(g + SW - 2 < G, eb);
+      eb = 0;
+    } else {
+      if (g + SW - 2 < G) wait_vmcnt_barrier<NQW>();
+      else wait_vmcnt_barrier<0>();
+    }
     auto retire = [&]() __attribute__((always_inline)) {
       if (pending) {
+        if constexpr (SB > 0)
+          eb = wf0 + Cfg::FW <= p.feats_valid(cst) ? min(TI, max(0, (p.tokens_valid(cst) - wt0) >> 5)) : 0;
         finish();
         zero();
         ++cj;
@@ -909,10 +959,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm3p_kernel(const Prob p) {
     };
     // bf16 weights: this iteration's DMAs go out before the finished tile's
     // epilogue, so its VALU work does not hold up the weight stream (measured
-    // 4% on the gate/value GEMM; with e4m3 weights the other order measured
-    // better).  Either order is safe for the waits: loads complete in issue
-    // order, so vmcnt(NQW) still leaves only the youngest weight tile in
-    // flight, however many epilogue stores are outstanding.
+    // 4% on the gate/value GEMM) and its stores can drain under the next
+    // k-tiles (the wait above); with e4m3 weights the other order measured
+    // better, and the next wait then covers the stores too.
     if constexpr (Cfg::WF8) retire();
     if (g + 1 < G) issue_x((g + 1) & 1);
     if (g + SW - 1 < G) issue_w((g + SW - 1) % SW);
