@@ -420,31 +420,41 @@ __global__ __launch_bounds__(256, MODE != BG_DENSE ? 4 : 1) void bgemm_kernel(co
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bw_sigmoid(float u) { return 1.f / (1.f + expf(-u)); }
 
-// SiTU-GLU on flat arrays: mode 0 writes a = silu(cap g) cap v; mode 1
-// writes dg, dv of a given da.  Outputs are bf16 (the next GEMM's operand
-// precision).
+// SiTU-GLU on flat arrays, four elements per thread (n a multiple of 4):
+// mode 0 writes a = silu(cap g) cap v; mode 1 writes dg, dv of a given da.
+// Outputs are bf16 (the next GEMM's operand precision).
 __global__ __launch_bounds__(256) void bw_situ_kernel(int mode, const float* g, const float* v, const float* da,
                                                       unsigned short* o1, unsigned short* o2, int64_t n, float cap,
                                                       float inv_cap) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= n) return;
-  const float gg = g[i], vv = v[i];
-  float cg = gg, cv = vv, dcg = 1.f, dcv = 1.f;
-  if (inv_cap > 0.f) {
-    const float tg = tanhf(gg * inv_cap), tv = tanhf(vv * inv_cap);
-    cg = cap * tg;
-    cv = cap * tv;
-    dcg = 1.f - tg * tg;
-    dcv = 1.f - tv * tv;
+  const f32x4 g4 = *reinterpret_cast<const f32x4*>(g + i), v4 = *reinterpret_cast<const f32x4*>(v + i);
+  f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
+  if (mode != 0) d4 = *reinterpret_cast<const f32x4*>(da + i);
+  unsigned short a1[4], a2[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float gg = g4[e], vv = v4[e];
+    float cg = gg, cv = vv, dcg = 1.f, dcv = 1.f;
+    if (inv_cap > 0.f) {
+      const float tg = tanhf(gg * inv_cap), tv = tanhf(vv * inv_cap);
+      cg = cap * tg;
+      cv = cap * tv;
+      dcg = 1.f - tg * tg;
+      dcv = 1.f - tv * tv;
+    }
+    const float sg = bw_sigmoid(cg);
+    if (mode == 0) {
+      a1[e] = f2bf(cg * sg * cv);
+    } else {
+      const float d = d4[e];
+      a1[e] = f2bf(d * cv * sg * (1.f + cg * (1.f - sg)) * dcg);
+      a2[e] = f2bf(d * cg * sg * dcv);
+    }
   }
-  const float sg = bw_sigmoid(cg);
-  if (mode == 0) {
-    o1[i] = f2bf(cg * sg * cv);
-  } else {
-    const float d = da[i];
-    o1[i] = f2bf(d * cv * sg * (1.f + cg * (1.f - sg)) * dcg);
-    o2[i] = f2bf(d * cg * sg * dcv);
-  }
+  *reinterpret_cast<uint2*>(o1 + i) = uint2{a1[0] | ((unsigned)a1[1] << 16), a1[2] | ((unsigned)a1[3] << 16)};
+  if (mode != 0)
+    *reinterpret_cast<uint2*>(o2 + i) = uint2{a2[0] | ((unsigned)a2[1] << 16), a2[2] | ((unsigned)a2[3] << 16)};
 }
 
 // Block sum of one float per thread (256 threads); every thread gets it.
@@ -457,53 +467,87 @@ __device__ __forceinline__ float bw_block_sum(float v, float* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
-// Per token: c = sum_j w_tj O[pos(t, j)] (fp32, j ascending), r = (mean c^2 +
-// eps)^-1/2, n = gamma c r.  Writes c (fp32), n (bf16) and r.
 __device__ __forceinline__ float bf2f(unsigned short h) { return __uint_as_float((unsigned)h << 16); }
-
-// (O is the expert output rows in bf16, as the forward stores them.)
-__global__ __launch_bounds__(256) void bw_combine_norm_kernel(const unsigned short* O, const int32_t* pos, const float* w,
-                                                              const float* gamma, int L, int k, float eps, float* c,
-                                                              unsigned short* n, float* r) {
-  __shared__ float red[4];
-  const int64_t t = blockIdx.x;
-  float ss = 0.f;
-  for (int l = threadIdx.x; l < L; l += 256) {
-    float acc = 0.f;
-    for (int j = 0; j < k; ++j) acc += w[t * k + j] * bf2f(O[(int64_t)pos[t * k + j] * L + l]);
-    c[t * L + l] = acc;
-    ss += acc * acc;
-  }
-  const float rr = 1.f / sqrtf(bw_block_sum(ss, red) / L + eps);
-  for (int l = threadIdx.x; l < L; l += 256) n[t * L + l] = f2bf(gamma[l] * c[t * L + l] * rr);
-  if (threadIdx.x == 0) r[t] = rr;
-}
 
 // Per token: dc = r u - r^3 c (u . c) / L with u = gamma dn; then for each
 // slot j, dO[pos(t, j)] = w_tj dc (bf16) and dw_tj = dc . O[pos(t, j)] (fp32
-// dc).  dc is recomputed per element and slot rather than stored.
+// dc).  Thread c holds 8-element chunks c, c + 256, ... of the row (L a
+// multiple of 8, at most 256 * 8 * MAXC): dc stays in registers across the
+// k slots, every load and store moves 16 or 32 bytes per lane, and the k
+// dot products are reduced together at the end.
+template <int MAXC>
 __global__ __launch_bounds__(256) void bw_norm_combine_grad_kernel(const float* dn, const float* c, const float* r,
                                                                    const float* gamma, const unsigned short* O,
                                                                    const int32_t* pos, const float* w, int L, int k,
                                                                    unsigned short* dO, float* dw) {
+  constexpr int KMAX = 64;
   __shared__ float red[4];
+  __shared__ float part[4 * KMAX];
   const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nch = L / 8;
   const float rr = r[t];
+  float dc[MAXC][8];
   float uc = 0.f;
-  for (int l = threadIdx.x; l < L; l += 256) uc += gamma[l] * dn[t * L + l] * c[t * L + l];
+#pragma unroll
+  for (int q = 0; q < MAXC; ++q) {
+    const int ch = tid + q * 256;
+    if (ch < nch) {
+      const int64_t o = t * L + ch * 8;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dn + o + 4 * h);
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(c + o + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ge = gamma[ch * 8 + 4 * h + e];  // a caller's pointer: element loads
+          uc += ge * d4[e] * c4[e];
+          dc[q][4 * h + e] = rr * ge * d4[e];  // the c part is subtracted below
+        }
+      }
+    }
+  }
   const float coef = rr * rr * rr * bw_block_sum(uc, red) / L;
+#pragma unroll
+  for (int q = 0; q < MAXC; ++q) {
+    const int ch = tid + q * 256;
+    if (ch < nch) {
+      const int64_t o = t * L + ch * 8;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(c + o + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dc[q][4 * h + e] -= coef * c4[e];
+      }
+    }
+  }
   for (int j = 0; j < k; ++j) {
     const int64_t a = pos[t * k + j];
     const float wj = w[t * k + j];
     float dot = 0.f;
-    for (int l = threadIdx.x; l < L; l += 256) {
-      const float dc = rr * gamma[l] * dn[t * L + l] - coef * c[t * L + l];
-      dO[a * L + l] = f2bf(wj * dc);
-      dot += dc * bf2f(O[a * L + l]);
+#pragma unroll
+    for (int q = 0; q < MAXC; ++q) {
+      const int ch = tid + q * 256;
+      if (ch < nch) {
+        const uint4 ov = *reinterpret_cast<const uint4*>(O + a * L + ch * 8);
+        const unsigned ow[4] = {ov.x, ov.y, ov.z, ov.w};
+        unsigned pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = dc[q][2 * e], hi = dc[q][2 * e + 1];
+          dot += lo * bf2f((unsigned short)(ow[e] & 0xffffu)) + hi * bf2f((unsigned short)(ow[e] >> 16));
+          pk[e] = f2bf(wj * lo) | ((unsigned)f2bf(wj * hi) << 16);
+        }
+        *reinterpret_cast<uint4*>(dO + a * L + ch * 8) = uint4{pk[0], pk[1], pk[2], pk[3]};
+      }
     }
-    const float s = bw_block_sum(dot, red);
-    if (threadIdx.x == 0) dw[t * k + j] = s;
+    // wave partial of slot j (j < KMAX: the shape check bounds k by 64)
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
+    if (lane == 0) part[wv * KMAX + j] = dot;
   }
+  __syncthreads();
+  for (int j = tid; j < k; j += 256) dw[t * k + j] = part[j] + part[KMAX + j] + part[2 * KMAX + j] + part[3 * KMAX + j];
 }
 
 // dgamma partials: part[y, l] = sum over tokens t of chunk y of dn c r.
@@ -547,16 +591,24 @@ __global__ __launch_bounds__(256) void bw_route_grad_kernel(const float* logits,
 }
 
 // dz_t = sum_j dzrows[pos(t, j)] (j ascending, fp32); written as fp32 to
-// out32, or as bf16 to out16 (the next GEMM's operand).
+// out32, or as bf16 to out16 (the next GEMM's operand).  Four consecutive
+// elements per thread (L a multiple of 4).
 __global__ __launch_bounds__(256) void bw_gather_sum_kernel(const float* rows, const int32_t* pos, int L, int k,
                                                             float* out32, unsigned short* out16) {
   const int64_t t = blockIdx.y;
-  const int l = blockIdx.x * 256 + threadIdx.x;
+  const int l = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (l >= L) return;
-  float s = 0.f;
-  for (int j = 0; j < k; ++j) s += rows[(int64_t)pos[t * k + j] * L + l];
-  if (out16) out16[t * L + l] = f2bf(s);
-  else out32[t * L + l] = s;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(rows + (int64_t)pos[t * k + j] * L + l);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] += v[e];
+  }
+  if (out16)
+    *reinterpret_cast<uint2*>(out16 + t * L + l) =
+        uint2{f2bf(s[0]) | ((unsigned)f2bf(s[1]) << 16), f2bf(s[2]) | ((unsigned)f2bf(s[3]) << 16)};
+  else
+    *reinterpret_cast<f32x4*>(out32 + t * L + l) = s;
 }
 
 // bf16 -> fp32 of n elements.

@@ -319,11 +319,14 @@ hipError_t launch_tiles(const int32_t* offsets, int E, int bt_a, int4* tiles_a, 
 // in fp32, the block reduces the sum of squares, and the normalised row is
 // written in the activation dtype.
 // ---------------------------------------------------------------------------
+// The backward's recompute also takes the combined row c (fp32, c_out) and
+// the row's 1/rms (r_out); the forward passes NULL for both.
 template <typename CT, int MAXC>
 __global__ __launch_bounds__(256) void combine_norm_kernel(const CT* __restrict__ O, const int32_t* __restrict__ pos,
                                                            const float* __restrict__ w,
                                                            const float* __restrict__ gamma, int L, int k, float eps,
-                                                           CT* __restrict__ out) {
+                                                           CT* __restrict__ out, float* __restrict__ c_out,
+                                                           float* __restrict__ r_out) {
   constexpr int EPC = 16 / sizeof(CT);
   typedef CT vec_t __attribute__((ext_vector_type(EPC)));
   __shared__ float red[4];
@@ -384,22 +387,30 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(const CT* __restrict_
 #pragma unroll
       for (int i = 0; i < EPC; ++i) o[i] = from_f32<CT>(gamma[ch * EPC + i] * acc[c][i] * inv);
       *reinterpret_cast<vec_t*>(out + t * L + ch * EPC) = o;
+      if (c_out) {
+#pragma unroll
+        for (int i = 0; i < EPC; i += 4)
+          *reinterpret_cast<f32x4*>(c_out + t * L + ch * EPC + i) =
+              f32x4{acc[c][i], acc[c][i + 1], acc[c][i + 2], acc[c][i + 3]};
+      }
     }
   }
+  if (r_out && tid == 0) r_out[t] = inv;
 }
 
 hipError_t launch_combine_norm(bool bf16_act, const void* O, const int32_t* pos, const float* w, const float* gamma,
-                               int64_t T, int L, int k, float eps, void* n, hipStream_t st) {
+                               int64_t T, int L, int k, float eps, void* n, hipStream_t st, float* c_out,
+                               float* r_out) {
   if (T == 0) return hipSuccess;
   if (bf16_act && L <= 2 * 256 * 8)
     hipLaunchKernelGGL((combine_norm_kernel<bf16, 2>), dim3((unsigned)T), dim3(256), 0, st, (const bf16*)O, pos, w,
-                       gamma, L, k, eps, (bf16*)n);
+                       gamma, L, k, eps, (bf16*)n, c_out, r_out);
   else if (bf16_act)
     hipLaunchKernelGGL((combine_norm_kernel<bf16, 4>), dim3((unsigned)T), dim3(256), 0, st, (const bf16*)O, pos, w,
-                       gamma, L, k, eps, (bf16*)n);
+                       gamma, L, k, eps, (bf16*)n, c_out, r_out);
   else
     hipLaunchKernelGGL((combine_norm_kernel<float, 8>), dim3((unsigned)T), dim3(256), 0, st, (const float*)O, pos, w,
-                       gamma, L, k, eps, (float*)n);
+                       gamma, L, k, eps, (float*)n, c_out, r_out);
   return hipGetLastError();
 }
 

@@ -24,8 +24,10 @@ hipError_t launch_permute_small(const int32_t* idx, int64_t T, int E, int k, int
 hipError_t launch_tiles(const int32_t* offsets, int E, int bt_a, int4* tiles_a, int32_t* cnt_a, int bt_b,
                         int4* tiles_b, int32_t* cnt_b, hipStream_t st);
 
+// c_out / r_out (optional, fp32): the combined rows and each row's 1/rms.
 hipError_t launch_combine_norm(bool bf16, const void* O, const int32_t* pos, const float* w, const float* gamma,
-                               int64_t T, int L, int k, float eps, void* n, hipStream_t st);
+                               int64_t T, int L, int k, float eps, void* n, hipStream_t st, float* c_out = nullptr,
+                               float* r_out = nullptr);
 
 // Quantile Balancing: bias[e] = -(1 - k/E) quantile of sigmoid(logits[:, e]);
 // keys: T * E uint32 scratch.

@@ -888,8 +888,9 @@ hipError_t bg(BgOp a, BgOp b, void* c, int64_t ldc, int M, int N, int K, int acc
 hipError_t bw_situ(int mode, const float* g, const float* v, const float* da, void* o1, void* o2, int64_t n,
                    const lmoe_shape* sh, hipStream_t st) {
   if (n == 0) return hipSuccess;
+  if (n % 4) return hipErrorInvalidValue;  // whole 4-element groups (I, Is are multiples of 64)
   const float inv = isinf(sh->cap) ? 0.f : 1.f / sh->cap;
-  hipLaunchKernelGGL(bw_situ_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, mode, g, v, da,
+  hipLaunchKernelGGL(bw_situ_kernel, dim3((unsigned)cdiv(n / 4, 256)), dim3(256), 0, st, mode, g, v, da,
                      static_cast<unsigned short*>(o1), static_cast<unsigned short*>(o2), n, sh->cap, inv);
   return hipGetLastError();
 }
@@ -1274,7 +1275,7 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
     LMOE_HIP((expert_down<T2ExpertDn, bf16>(cx, A, offsets, tiles2, tc2, O)), "expert down");
   }
   if (T > 0)
-    hipLaunchKernelGGL(bw_combine_norm_kernel, dim3(T), dim3(256), 0, st, O, pos, tw, w->gamma, L, k, sh->rms_eps, c, n, r);
+    LMOE_HIP(launch_combine_norm(true, O, pos, tw, w->gamma, T, L, k, sh->rms_eps, n, st, c, r), "combine + RMSNorm");
   LMOE_HIP(hipGetLastError(), "combine + norm");
 
   if (lmoe_status s = record(ev, 1, st)) return s;
@@ -1310,9 +1311,14 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
     LMOE_HIP(hipGetLastError(), "dn");
   }
   // --- RMSNorm and combine ------------------------------------------------
-  if (T > 0)
-    hipLaunchKernelGGL(bw_norm_combine_grad_kernel, dim3(T), dim3(256), 0, st, dn, c, r, w->gamma, O, pos, tw, L, k, dO,
-                       dw);
+  if (T > 0) {
+    if (L <= 2 * 256 * 8)
+      hipLaunchKernelGGL(bw_norm_combine_grad_kernel<2>, dim3(T), dim3(256), 0, st, dn, c, r, w->gamma, O, pos, tw, L, k,
+                         dO, dw);
+    else
+      hipLaunchKernelGGL(bw_norm_combine_grad_kernel<4>, dim3(T), dim3(256), 0, st, dn, c, r, w->gamma, O, pos, tw, L, k,
+                         dO, dw);
+  }
   LMOE_HIP(hipGetLastError(), "norm / combine gradient");
   {
     const int64_t chunk = cdiv(std::max<int64_t>(sh->T, 1), kBwChunks);
@@ -1377,7 +1383,7 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   if (lmoe_status s = record(ev, 3, st)) return s;
   // --- latent projection and dx --------------------------------------------
   if (T > 0) {
-    hipLaunchKernelGGL(bw_gather_sum_kernel, dim3((unsigned)cdiv(L, 256), T), dim3(256), 0, st, zr, pos, L, k,
+    hipLaunchKernelGGL(bw_gather_sum_kernel, dim3((unsigned)cdiv(L, 1024), T), dim3(256), 0, st, zr, pos, L, k,
                        w->w_down ? nullptr : gr->dx, w->w_down ? dz : nullptr);
     LMOE_HIP(hipGetLastError(), "dz");
   }
