@@ -573,10 +573,15 @@ __global__ __launch_bounds__(256) void bw_sum_rows_kernel(const float* part, int
 // Router: per token, dlogit = ds s (1 - s) at the selected experts (0
 // elsewhere), ds_j = (dw_j - sum_j' dw_j' w_j') / S, S = sum of the selected
 // sigmoid scores, w_j = s_j / S.
+// dl16 (optional): the same row in bf16, the operand precision of the
+// GEMMs that consume it.
 __global__ __launch_bounds__(256) void bw_route_grad_kernel(const float* logits, const int32_t* idx, const float* dw,
-                                                            int E, int k, float* dlogits) {
+                                                            int E, int k, float* dlogits, unsigned short* dl16) {
   const int64_t t = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += 256) dlogits[t * E + e] = 0.f;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    dlogits[t * E + e] = 0.f;
+    if (dl16) dl16[t * E + e] = 0;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     float S = 0.f, dot = 0.f;
@@ -585,7 +590,9 @@ __global__ __launch_bounds__(256) void bw_route_grad_kernel(const float* logits,
     for (int j = 0; j < k; ++j) {
       const int e = idx[t * k + j];
       const float s = bw_sigmoid(logits[t * E + e]);
-      dlogits[t * E + e] = (dw[t * k + j] - dot) / S * s * (1.f - s);
+      const float d = (dw[t * k + j] - dot) / S * s * (1.f - s);
+      dlogits[t * E + e] = d;
+      if (dl16) dl16[t * E + e] = f2bf(d);
     }
   }
 }

@@ -810,7 +810,7 @@ constexpr int kBwChunks = 64;  // token chunks of the dgamma reduction
 
 struct BPlan {
   size_t logits, z, idx, w, bcounts, offsets, sorted, pos, tiles, tcount, tiles2, tcount2;
-  size_t G, V, A, dA, dG, dV, O, zr, dO, c, n, dn, dz, r, dw, dl, gs, vs, hs, dhs, dgs, dvs, dgp, zpage, total;
+  size_t G, V, A, dA, dG, dV, O, zr, dO, c, n, dn, dz, r, dw, dl, dl16, gs, vs, hs, dhs, dgs, dvs, dgp, zpage, total;
 };
 
 BPlan bplan(const lmoe_shape* sh) {
@@ -852,6 +852,7 @@ BPlan bplan(const lmoe_shape* sh) {
   p.r = take(T * 4);
   p.dw = take(tk * 4);
   p.dl = take(T * sh->E * 4);
+  p.dl16 = take(T * sh->E * 2);
   p.gs = take(T * sis * 4);
   p.vs = take(T * sis * 4);
   p.hs = take(T * sis * 2);
@@ -1247,6 +1248,7 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   int32_t* tc = at<int32_t>(ws, pl.tcount);
   float *G = at<float>(ws, pl.G), *V = at<float>(ws, pl.V), *dA = at<float>(ws, pl.dA), *zr = at<float>(ws, pl.zr);
   float *c = at<float>(ws, pl.c), *dn = at<float>(ws, pl.dn), *r = at<float>(ws, pl.r), *dw = at<float>(ws, pl.dw);
+  unsigned short* dl16 = at<unsigned short>(ws, pl.dl16);
   float *dl = at<float>(ws, pl.dl), *gs = at<float>(ws, pl.gs), *vs = at<float>(ws, pl.vs), *dhs = at<float>(ws, pl.dhs);
   unsigned short *A = at<unsigned short>(ws, pl.A), *dG = at<unsigned short>(ws, pl.dG), *dV = at<unsigned short>(ws, pl.dV);
   unsigned short *dO = at<unsigned short>(ws, pl.dO), *n = at<unsigned short>(ws, pl.n), *dz = at<unsigned short>(ws, pl.dz);
@@ -1381,33 +1383,46 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
              "dW_value");
   }
   if (lmoe_status s = record(ev, 3, st)) return s;
-  // --- latent projection and dx --------------------------------------------
+  // --- latent projection, router and dx ----------------------------------------
   if (T > 0) {
     hipLaunchKernelGGL(bw_gather_sum_kernel, dim3((unsigned)cdiv(L, 1024), T), dim3(256), 0, st, zr, pos, L, k,
                        w->w_down ? nullptr : gr->dx, w->w_down ? dz : nullptr);
     LMOE_HIP(hipGetLastError(), "dz");
+    // the router's logit gradients, fp32 and bf16 (the GEMMs below read them
+    // in bf16 either way)
+    hipLaunchKernelGGL(bw_route_grad_kernel, dim3(T), dim3(256), 0, st, logits, idx, dw, E, k, dl, dl16);
+    LMOE_HIP(hipGetLastError(), "router gradient");
   }
+  // dx = dz W_dn + dl W_r as one pass of the persistent engine when the
+  // router's K (E) is whole 64-column k-tiles
+  const bool rtg = dtg && E % 64 == 0;
   if (w->w_down) {
     if (dtg) {
-      const void* xs[1] = {dz};
-      const int64_t lx[1] = {L};
-      const int kd[1] = {L};
-      const void* wsrc[1] = {w->w_down};
-      const int64_t wm[1] = {0};
-      LMOE_HIP(dense_tgrad(cx, 1, xs, lx, kd, wsrc, wm, H, H, gr->dx, H, 0), "dx (latent)");
+      const void* xs[2] = {dz, dl16};
+      const int64_t lx[2] = {L, E};
+      const int kd[2] = {L, E};
+      const void* wsrc[2] = {w->w_down, w->w_router};
+      const int64_t wm[2] = {0, 0};
+      LMOE_HIP(dense_tgrad(cx, rtg ? 2 : 1, xs, lx, kd, wsrc, wm, H, H, gr->dx, H, 0), "dx (latent + router)");
     } else {
       LMOE_HIP((bg<BG_DENSE, 0, 0, 1, 0>(bop(dz, L), bop(w->w_down, H), gr->dx, H, T, H, L, 0, st, sh)), "dx (latent)");
     }
     if (!add_dense(dz, L, x, H, gr->dw_down, L, H))
       LMOE_HIP((bg<BG_DENSE, 1, 0, 1, 0>(bop(dz, L), bop(x, H), gr->dw_down, H, L, H, T, 0, st, sh)), "dW_down");
+  } else if (rtg) {
+    const void* xs[1] = {dl16};
+    const int64_t lx[1] = {E};
+    const int kd[1] = {E};
+    const void* wsrc[1] = {w->w_router};
+    const int64_t wm[1] = {0};
+    LMOE_HIP(dense_tgrad(cx, 1, xs, lx, kd, wsrc, wm, H, H, gr->dx, H, 1), "dx (router)");
   }
-  // --- router ---------------------------------------------------------------
-  if (T > 0) {
-    hipLaunchKernelGGL(bw_route_grad_kernel, dim3(T), dim3(256), 0, st, logits, idx, dw, E, k, dl);
-    LMOE_HIP(hipGetLastError(), "router gradient");
-  }
-  LMOE_HIP((bg<BG_DENSE, 0, 1, 1, 0>(bop(dl, E), bop(w->w_router, H), gr->dx, H, T, H, E, 1, st, sh)), "dx (router)");
-  LMOE_HIP((bg<BG_DENSE, 1, 1, 1, 0>(bop(dl, E), bop(x, H), gr->dw_router, H, E, H, T, 0, st, sh)), "dW_router");
+  if (!rtg)
+    LMOE_HIP((bg<BG_DENSE, 0, 1, 1, 0>(bop(dl, E), bop(w->w_router, H), gr->dx, H, T, H, E, 1, st, sh)), "dx (router)");
+  // dW_router (E rows: usually not whole 256-row tiles) stays on the
+  // register-staged GEMM; a whole-tile E joins the dense weight gradients
+  if (!add_dense(dl16, E, x, H, gr->dw_router, E, H))
+    LMOE_HIP((bg<BG_DENSE, 1, 1, 1, 0>(bop(dl, E), bop(x, H), gr->dw_router, H, E, H, T, 0, st, sh)), "dW_router");
   if (lmoe_status s = record(ev, 4, st)) return s;
   // --- shared experts ---------------------------------------------------------
   if (S > 0) {

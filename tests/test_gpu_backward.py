@@ -66,12 +66,15 @@ def _run(cfg, dev):
 
 @pytest.mark.parametrize("name,T,E", [("small_bf16", None, None), ("small_identity_bf16", None, None),
                                       ("small_full_k", None, None), ("small_bf16", 40, None), ("small_bf16", 700, None),
-                                      ("small_wide_bf16", None, None), ("small_wide_bf16", 700, 8)])
+                                      ("small_wide_bf16", None, None), ("small_wide_bf16", 700, 8),
+                                      ("small_bf16", 700, 64), ("small_identity_bf16", 700, 64)])
 def test_backward_matches_oracle(dev, name, T, E):
     """small_wide_bf16 runs the persistent expert-gradient kernels: at its own
     size some of the 160 experts get no rows (their weight gradients must be
     exact zeros), and at T = 700 over 8 experts each expert spans several
-    64-row k-tiles with a partial last one."""
+    64-row k-tiles with a partial last one.  E = 64 at T = 700 routes the
+    router's dx through the persistent data-gradient engine (with the latent
+    segment, or alone onto dx when there is no latent projection)."""
     cfg = get_config(name)
     if T is not None:
         cfg = replace(cfg, T=T, name=f"{name}_T{T}")
