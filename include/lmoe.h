@@ -36,6 +36,10 @@
  *   - Every tensor pointer is a device pointer owned by the caller.  The library
  *     never allocates or frees device memory; scratch comes from `ws`, a caller
  *     buffer of at least lmoe_workspace_bytes(shape) bytes, 256-byte aligned.
+ *   - Weight matrices, activations and gradients move through 16-byte vector
+ *     loads, DMAs and stores: their base pointers must be 16-byte aligned
+ *     (LMOE_EINVAL otherwise, the message naming the pointer); scale, bias,
+ *     gamma, index and routing-weight arrays need only their element size.
  *   - Inputs are read only.  Outputs must not alias inputs or each other.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
  *     stream) and never synchronise with the host; no work depends on a

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <mutex>
 
 #include "backward.hpp"
@@ -78,8 +79,20 @@ bool is_f8(const lmoe_shape* sh) { return sh->w_expert == LMOE_F8E4M3; }
 // Which weights an entry point reads.
 enum : unsigned { NEED_ROUTE = 1, NEED_EXPERT = 2, NEED_UP = 4, NEED_NORM = 8 };
 
+// Matrices and activations move through 16-byte vector loads, DMAs and
+// stores, so their base pointers must be 16-byte aligned (NULL passes).
+lmoe_status check_align16(std::initializer_list<std::pair<const void*, const char*>> ptrs) {
+  for (const auto& [p, name] : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) & 15) return fail(LMOE_EINVAL, "%s must be 16-byte aligned", name);
+  return LMOE_OK;
+}
+
 lmoe_status check_weights(const lmoe_shape* sh, const lmoe_weights* w, unsigned need) {
   if (!w) return fail(LMOE_EINVAL, "weights is NULL");
+  if (lmoe_status s = check_align16({{w->w_router, "w_router"}, {w->w_down, "w_down"}, {w->w_gate, "w_gate"},
+                                      {w->w_value, "w_value"}, {w->w_out, "w_out"}, {w->w_up, "w_up"},
+                                      {w->ws_gate, "ws_gate"}, {w->ws_value, "ws_value"}, {w->ws_out, "ws_out"}}))
+    return s;
   const bool f8 = is_f8(sh);
   if (need & NEED_ROUTE) {
     if (!w->w_router || !w->b_router) return fail(LMOE_EINVAL, "w_router and b_router are required");
@@ -938,6 +951,7 @@ lmoe_status lmoe_route(const lmoe_shape* sh, const lmoe_weights* w, const void* 
   if (lmoe_status s = check_ws(sh, ws, ws_bytes)) return s;
   if (sh->T == 0) return LMOE_OK;
   if (!x || !topk_idx || !topk_w || (w->w_down && !z)) return fail(LMOE_EINVAL, "x, topk_idx, topk_w, z are required");
+  if (lmoe_status s = check_align16({{x, "x"}, {z, "z"}})) return s;
   const Ctx c{sh, w, static_cast<hipStream_t>(stream)};
   const Plan pl = plan(sh);
   float* logits = at<float>(ws, pl.logits);
@@ -970,6 +984,7 @@ lmoe_status lmoe_expert_gemm(const lmoe_shape* sh, const lmoe_weights* w, const 
   if (lmoe_status s = check_ws(sh, ws, ws_bytes)) return s;
   if (sh->T == 0) return LMOE_OK;
   if (!z || !offsets || !sorted || !expert_out) return fail(LMOE_EINVAL, "z, offsets, sorted, expert_out are required");
+  if (lmoe_status s = check_align16({{z, "z"}, {expert_out, "expert_out"}})) return s;
   const Ctx c{sh, w, static_cast<hipStream_t>(stream)};
   const Plan pl = plan(sh);
   void* act = at<void>(ws, pl.act);
@@ -993,6 +1008,7 @@ lmoe_status lmoe_combine_norm(const lmoe_shape* sh, const void* expert_out, cons
   if (lmoe_status s = check_shape(sh)) return s;
   if (sh->T == 0) return LMOE_OK;
   if (!expert_out || !pos || !topk_w || !gamma || !n) return fail(LMOE_EINVAL, "null argument");
+  if (lmoe_status s = check_align16({{expert_out, "expert_out"}, {n, "n"}})) return s;
   LMOE_HIP(launch_combine_norm(bf16_act(sh), expert_out, pos, topk_w, gamma, sh->T, sh->L, sh->k, sh->rms_eps, n,
                                static_cast<hipStream_t>(stream)),
            "combine + norm");
@@ -1007,6 +1023,7 @@ lmoe_status lmoe_up(const lmoe_shape* sh, const lmoe_weights* w, const void* n, 
   if (lmoe_status s = check_ws(sh, ws, ws_bytes)) return s;
   if (sh->T == 0) return LMOE_OK;
   if (!n || !y || (sh->S > 0 && !x)) return fail(LMOE_EINVAL, "n, x, y are required");
+  if (lmoe_status s = check_align16({{n, "n"}, {x, "x"}, {y, "y"}})) return s;
   const Ctx c0{sh, w, static_cast<hipStream_t>(stream)};
   const Plan pl = plan(sh);
   DenseView dv;
@@ -1031,6 +1048,7 @@ lmoe_status forward_impl(const lmoe_shape* sh, const lmoe_weights* w, const void
   if (lmoe_status s = check_ws(sh, ws, ws_bytes)) return s;
   if (sh->T == 0) return LMOE_OK;
   if (!x || !y) return fail(LMOE_EINVAL, "x and y are required");
+  if (lmoe_status s = check_align16({{x, "x"}, {y, "y"}})) return s;
   const Ctx c{sh, w, static_cast<hipStream_t>(stream)};
   const Plan pl = plan(sh);
   const bool bf = bf16_act(sh);
@@ -1160,6 +1178,7 @@ lmoe_status lmoe_router_logits(const lmoe_shape* sh, const lmoe_weights* w, cons
   if (!w || !w->w_router) return fail(LMOE_EINVAL, "w_router is required");
   if (sh->T == 0) return LMOE_OK;
   if (!x || !logits) return fail(LMOE_EINVAL, "x and logits are required");
+  if (lmoe_status s = check_align16({{x, "x"}, {w->w_router, "w_router"}, {logits, "logits"}})) return s;
   const Ctx c{sh, w, static_cast<hipStream_t>(stream)};
   LMOE_HIP(bf16_act(sh) ? xgemm_any<bf16>(c, x, logits, nullptr, nullptr) : xgemm_any<float>(c, x, logits, nullptr,
                                                                                                nullptr),
@@ -1235,6 +1254,11 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   if (!ws) return fail(LMOE_EINVAL, "ws is NULL");
   if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(LMOE_EINVAL, "ws must be 256-byte aligned");
   if (sh->T > 0 && (!x || !dy)) return fail(LMOE_EINVAL, "x and dy are required");
+  if (lmoe_status s = check_align16({{x, "x"}, {dy, "dy"}, {gr->dx, "dx"}, {gr->dw_router, "dw_router"},
+                                      {gr->dw_down, "dw_down"}, {gr->dw_gate, "dw_gate"}, {gr->dw_value, "dw_value"},
+                                      {gr->dw_out, "dw_out"}, {gr->dw_up, "dw_up"}, {gr->dws_gate, "dws_gate"},
+                                      {gr->dws_value, "dws_value"}, {gr->dws_out, "dws_out"}}))
+    return s;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int T = (int)sh->T, H = sh->H, L = sh->L, E = sh->E, k = sh->k, I = sh->I, S = sh->S, Is = sh->Is;
   const int tk = T * k, sis = S * Is;

@@ -147,6 +147,30 @@ def test_null_shape_and_weights(lib):
     assert lib.lmoe_validate(ctypes.byref(sh), None, 1 << 40) == 1
 
 
+def test_misaligned_tensors_are_rejected(lib):
+    """Matrices and activations move in 16-byte vectors: a base address that
+    is not 16-byte aligned is EINVAL, named in the message, before any GPU
+    call (weights through lmoe_validate, activations and gradients at the
+    entry points)."""
+    sh = k3(T=4)
+    need = lmoe.workspace_bytes(sh)
+    ws = ctypes.c_void_p(0x10000)
+    assert lmoe.validate(sh, fake_weights(sh, w_gate=0x1008), 1 << 40) == 1
+    assert "w_gate must be 16-byte aligned" in lmoe.last_error()
+    assert lmoe.validate(sh, fake_weights(sh, ws_out=0x1004), 1 << 40) == 1
+    w = fake_weights(sh)
+    s = lib.lmoe_forward(ctypes.byref(sh), ctypes.byref(w), 0x2008, 0x3000, None, None, ws, need, None, None)
+    assert s == 1 and "x must be 16-byte aligned" in lmoe.last_error()
+    s = lib.lmoe_forward(ctypes.byref(sh), ctypes.byref(w), 0x2000, 0x3002, None, None, ws, need, None, None)
+    assert s == 1 and "y must be 16-byte aligned" in lmoe.last_error()
+    bneed = lib.lmoe_backward_workspace_bytes(ctypes.byref(sh))
+    g = lmoe.Grads(**{n: 0x2000 + 0x100 * i for i, n in enumerate(lmoe.GRAD_FIELDS)})
+    g.dw_value = 0x5008
+    s = lib.lmoe_backward(ctypes.byref(sh), ctypes.byref(w), ctypes.c_void_p(0x8000), ctypes.c_void_p(0x9000), None,
+                          ctypes.byref(g), ctypes.c_void_p(0x200000), bneed, None, None)
+    assert s == 1 and "dw_value must be 16-byte aligned" in lmoe.last_error()
+
+
 def test_entry_points_reject_before_any_gpu_call(lib):
     """Argument errors return before anything touches the device, so they are
     testable here: a short workspace, a misaligned one, null outputs."""
