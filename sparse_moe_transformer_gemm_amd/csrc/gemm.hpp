@@ -211,7 +211,17 @@ struct DenseXProb {
     } else {
       u = st.f0 + r;
     }
-    if (u >= s.rows) return nullptr;
+    if (u >= s.rows) {
+      // Row 0 stands in for every missing row of its tile.  A re-cut
+      // sub-tile can lie wholly past the segment (the second half of a last
+      // big tile with <= BF/2 rows): its stand-in is then the segment's
+      // first row, so its DMAs read in bounds; nothing computed from them is
+      // stored.
+      if (r != 0) return nullptr;
+      u = 0;
+      base = s.w;
+      sb = s.sc;
+    }
     if (s.f8) *scrow = sb + (int64_t)(u >> 7) * (K >> 7);
     return base + (int64_t)u * K * wes;
   }
@@ -275,8 +285,13 @@ struct UpProb {
     return x_row(st, s, min(r0 + (lane >> 3), tokens_valid(st) - 1));
   }
   __device__ const char* w_row(const State& st, int s, int r, const float** scrow) const {
-    const int f = st.ft * Cfg::BF + r;
-    if (f >= N) return nullptr;
+    int f = st.ft * Cfg::BF + r;
+    if (f >= N) {
+      // row 0 of a re-cut sub-tile wholly past N (the stand-in for its
+      // missing rows): the first row, so that its DMAs read in bounds
+      if (r != 0) return nullptr;
+      f = 0;
+    }
     const KSeg& q = ks[s];
     if (q.f8) {
       *scrow = q.sc + (int64_t)(f >> 7) * (q.ldw >> 7);

@@ -4,6 +4,8 @@ in the launch configuration the benchmark times; the oracle checks the
 selection of every token and the outputs of a seeded sample of rows (each
 output row depends only on its own token)."""
 
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -101,6 +103,24 @@ def test_k3_prefill_and_decode_batch_invariant(dev, k3w):
     yd, idd = _run(dcfg, k3w, dev, x=xd)
     assert torch.equal(idd, idx[:64])
     assert torch.equal(yd, y[:64])
+
+
+def test_k3_t2100_recut_router_tiles(dev, k3w):
+    """T = 2100: the route GEMM's 9 x 34 tiles leave a last round of 50,
+    re-cut into 128 x 128 sub-tiles, and it holds the last token tile's
+    router tiles; the second half of the last one (features 896 .. 1023)
+    lies wholly past E, so its DMAs must read inside W_router.  Oracle on
+    every token's selection and on sampled rows, and the first 2048 rows
+    bitwise equal to the T = 2048 batch (whose router tiles all run as
+    256 x 256 tiles)."""
+    base = get_config("k3_prefill_t2048")
+    cfg = replace(base, name="k3_prefill_t2100", T=2100)
+    x = make_x(cfg, dev)
+    assert torch.equal(x[:2048], make_x(base, dev))  # the T = 2048 batch is a prefix
+    y, idx = _run(cfg, k3w, dev, x=x)
+    y0, idx0 = _run(base, k3w, dev, sample=16, x=x[:2048].contiguous())
+    assert torch.equal(idx[:2048], idx0)
+    assert torch.equal(y[:2048], y0)
 
 
 def test_k3_zipf_t16384(dev, k3w):

@@ -115,6 +115,30 @@ def test_route(dev, name):
         assert rowwise_rel_err(to_f64(z), zr) <= zt
 
 
+@pytest.mark.parametrize("T,E,k,ident", [(16484, 896, 16, True), (2049, 896, 16, False), (700, 200, 8, True)])
+def test_route_ragged_router_tiles(dev, T, E, k, ident):
+    """Router tiles at the edges of the route GEMM's tile walk.  At T = 16484
+    with identity projections and no shared expert the GEMM has 4 x 65 router
+    tiles; the last token tile's four run in the re-cut tail launch as
+    128 x 128 sub-tiles, and the second half of the last router tile
+    (features 896 .. 1023) lies wholly past E: its DMAs must stay inside
+    W_router while nothing of it is stored.  T = 2049 leaves one token in the
+    last token tile; E = 200 is one partial router tile.  Every token's
+    selection is checked against the oracle."""
+    base = get_config("small_identity_bf16" if ident else "small_bf16")
+    cfg = replace(base, name=f"route_t{T}_e{E}", T=T, E=E, k=k, S=0, Is=0, I=128)
+    note(f"[route ragged router tiles] T={T} E={E} k={k} identity={ident}")
+    t, g = make_case(cfg, dev)
+    sh, w = _weights(cfg, g)
+    idx, tw, _ = lmoe.route(sh, w, g["x"])
+    torch.cuda.synchronize()
+    inp = host_inputs(t)
+    x = O.decode(inp["x"], cfg.act)
+    r = O.route(x, O.decode(inp["w_router"], cfg.act), inp["b_router"].astype(np.float64), cfg.k)
+    res = check_selection(idx.cpu().numpy(), tw.cpu().numpy(), r)
+    assert res["tokens"] == T
+
+
 def _bruteforce_permute(idx, E):
     """Expected result including the dropping rule for ids out of range and
     repeats within a token."""
