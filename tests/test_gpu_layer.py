@@ -139,6 +139,37 @@ def test_route_ragged_router_tiles(dev, T, E, k, ident):
     assert res["tokens"] == T
 
 
+def test_forward_recut_tails_past_segments(dev):
+    """Re-cut tail launches in which sub-tiles lie wholly past their segment.
+    H = 384, L = 128, E = 200, S*Is = 192 at T = 32800 (129 token tiles):
+    the route GEMM's 516 tiles leave a tail of 4 (the last token tile's
+    router, z and two shared-GLU tiles), re-cut into 128 x 128 sub-tiles, so
+    the second halves of the z tile (rows 128..255 of 128) and of the last
+    GLU tile (units 192..255 of 192) hold no rows; the up GEMM's 258 tiles
+    leave 2, and the second half of its last feature tile (384..511 of 384)
+    holds none.  Every row against the oracle, and the first 32768 rows
+    bitwise equal to the T = 32768 batch (no tail launch there)."""
+    base = get_config("small_bf16")
+    cfg = replace(base, name="recut_tails_t32800", T=32800, H=384, L=128, E=200, k=4, S=3, I=128, Is=64)
+    note(f"[forward re-cut tails] {cfg.name}")
+    t, g = make_case(cfg, dev)
+    sh, w = _weights(cfg, g)
+    y, idx, tw = lmoe.forward(sh, w, g["x"])
+    torch.cuda.synchronize()
+    inp = host_inputs(t)
+    ref = O.forward(inp, spec_of(cfg))
+    check_selection(idx.cpu().numpy(), tw.cpu().numpy(), ref)
+    forced = O.forward(inp, spec_of(cfg), forced_idx=idx.cpu().numpy().astype(np.int64), forced_tol=1e-5)
+    err = rowwise_rel_err(to_f64(y), forced["y"])
+    note(f"    max row rel err {err:.3e}")
+    assert err <= tol_of(cfg)
+    sh0 = lmoe.shape_of(cfg, T=32768)
+    y0, idx0, _ = lmoe.forward(sh0, w, g["x"][:32768].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(idx0, idx[:32768])
+    assert torch.equal(y0, y[:32768])
+
+
 def _bruteforce_permute(idx, E):
     """Expected result including the dropping rule for ids out of range and
     repeats within a token."""
