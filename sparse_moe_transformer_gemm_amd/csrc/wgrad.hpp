@@ -252,10 +252,20 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
   issue_x(0);
   issue_w(0);
   if (1 < G) issue_w(1);
-  bool pending = false;
+  // A tile's stores (SB per wave) follow the DMAs of the iteration that
+  // issues them, so the next iteration's wait lets them stay in flight: it
+  // needs only X(g + 1) and older done, which precede W(g + 2) and the stores.
+  constexpr int SB = FI * TI * 16;
+  static_assert(SB + NQW >= 63, "the cap below is the exact count otherwise");
+  bool pending = false, stored = false;
   for (int g = 0; g < G; ++g) {
-    if (g + 1 < G) wait_vmcnt_barrier<NQW>();
-    else wait_vmcnt_barrier<0>();
+    if (g + 1 < G) {
+      if (stored) wait_vmcnt_barrier<63>();
+      else wait_vmcnt_barrier<NQW>();
+    } else {
+      wait_vmcnt_barrier<0>();
+    }
+    stored = false;
     if (g + 1 < G) issue_x((g + 1) & 1);
     if (g + 2 < G) issue_w((g + 2) % 3);
     if (pending) {
@@ -263,6 +273,7 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
       zero();
       locate(++cj, ct);
       pending = false;
+      stored = true;
     }
     mma_ktile_tt<FI, TI>(acc, smem + (g % 3) * Cfg::WSTAGE, smem + Cfg::X_OFF + (g & 1) * Cfg::XSTAGE, wf0, wt0,
                          lane);
