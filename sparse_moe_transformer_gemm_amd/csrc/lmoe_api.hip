@@ -592,9 +592,10 @@ hipError_t dense_tgrad(const Ctx& c, int nks, const void* const* x, const int64_
   return launch_gemm<Cfg, bf16>(p, persistent_grid(), c.st);
 }
 
-hipError_t launch_wgrad(const Ctx& c, const WGradArgs& a) {
+template <int KR>
+hipError_t launch_wgrad_kr(const Ctx& c, const WGradArgs& a) {
   using Cfg = TWGrad;
-  auto kern = wgrad3p_kernel<Cfg>;
+  auto kern = wgrad3p_kernel<Cfg, KR>;
   static std::once_flag once[kMaxDevices];
   static hipError_t attr[kMaxDevices];
   auto set_attr = [&] {
@@ -612,6 +613,10 @@ hipError_t launch_wgrad(const Ctx& c, const WGradArgs& a) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)persistent_grid()), dim3(Cfg::NT), Cfg::LDS, c.st, a);
   return hipGetLastError();
+}
+// routed experts: 32-row stages; dense segments: 64-row stages
+hipError_t launch_wgrad(const Ctx& c, const WGradArgs& a) {
+  return a.nseg == 0 ? launch_wgrad_kr<32>(c, a) : launch_wgrad_kr<64>(c, a);
 }
 
 // Expert weight gradients on the persistent pipeline: C_e = P_e^T Q_e for

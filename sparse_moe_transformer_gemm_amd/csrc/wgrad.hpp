@@ -66,8 +66,8 @@ typedef Tile3<256, 256, 4, 4, 0, 1, 0, 3, 0, 1> TWGrad;
 __global__ __launch_bounds__(128) void zero_page_kernel(uint32_t* z) { z[threadIdx.x] = 0u; }
 
 // Both operands from transposed stages (wtr_off layout): 16 k per MFMA,
-// 4 k-steps per 64-row k-tile.
-template <int FI, int TI>
+// KS k-steps per stage of 16 KS k-rows.
+template <int FI, int TI, int KS>
 __device__ __forceinline__ void mma_ktile_tt(f32x16 (&acc)[FI][TI], const char* sW, const char* sX, int wf0, int wt0,
                                              int lane) {
   const int G = lane >> 4, q = lane & 15;
@@ -80,7 +80,7 @@ __device__ __forceinline__ void mma_ktile_tt(f32x16 (&acc)[FI][TI], const char* 
     return *reinterpret_cast<const bf16x8*>(v);
   };
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     const int kr = ks * 16 + 8 * (G >> 1) + (q >> 2);
     bf16x8 a[FI], b[TI];
 #pragma unroll
@@ -97,11 +97,22 @@ __device__ __forceinline__ void mma_ktile_tt(f32x16 (&acc)[FI][TI], const char* 
   }
 }
 
-template <class Cfg>
+template <class Cfg, int KR>
 __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  constexpr int FI = Cfg::FI, TI = Cfg::TI, NQW = Cfg::NQW, NQX = Cfg::NQX, NW = Cfg::NW;
-  static_assert(NQW == NQX && Cfg::QW == 32 && Cfg::QX == 32, "32 DMA instructions per operand per k-tile");
+  constexpr int FI = Cfg::FI, TI = Cfg::TI, NW = Cfg::NW;
+  // Stages of KR k-rows (a k-row holds the tile's 256 columns, 512 bytes),
+  // as many as fit per operand in half the LDS: 32 k-rows 5 deep (the DMAs
+  // run D = 4 stages ahead) for the routed experts, whose K is a few hundred
+  // rows and whose stores bound them; 64 k-rows 2 deep for the dense
+  // segments (K = T), whose MFMA loop gains from the longer k-tiles.  One
+  // DMA instruction stages two k-rows.
+  static_assert(KR == 32 || KR == 64, "stage height");
+  constexpr int STG = KR * 512, P = Cfg::LDS / 2 / STG, D = P - 1;
+  constexpr int NQ = KR / 2 / NW;
+  static_assert(NQ * NW * 2 == KR && Cfg::BF == 256 && Cfg::BT == 256, "DMAs split evenly over the waves");
+  static_assert(D >= 1 && D <= 4, "the stage wait counts up to three later groups");
+  static_assert(2 * P * STG <= Cfg::LDS, "the rings fit the launch's LDS");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wf0 = (wid % Cfg::WF) * Cfg::FW;  // columns n of the tile (Q side, MFMA A operand)
@@ -157,7 +168,7 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
       t.qb = sg.q + (int64_t)n0 * 2;
       t.cb = sg.c + (int64_t)m0 * sg.N + n0;
     }
-    t.nkt = max(1, (t.rows + 63) >> 6);
+    t.nkt = max(1, (t.rows + KR - 1) / KR);
   };
   int G = 0;
   for (int j = 0; j < ntile; ++j) {
@@ -185,11 +196,11 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
   // instruction q of a k-tile stages k-rows 2 q and 2 q + 1 of it; lane l the
   // chunk that belongs at position l % 32 of k-row 2 q + l / 32
   auto issue_x = [&](int buf) __attribute__((always_inline)) {
-    char* base = smem + Cfg::X_OFF + buf * Cfg::XSTAGE;
+    char* base = smem + P * STG + buf * STG;
 #pragma unroll
-    for (int i = 0; i < NQX; ++i) {
+    for (int i = 0; i < NQ; ++i) {
       const int q = wid + NW * i, kr = 2 * q + (lane >> 5), c = (lane & 31) ^ ((kr & 3) << 2);
-      const int t = xk * 64 + kr;
+      const int t = xk * KR + kr;
       const char* src = t < xt.rows ? xt.pb + ((int64_t)t * xt.ldp + 8 * c) * 2 : p.zero + 16 * c;
       dma16<0>(src, base + q * 1024);
     }
@@ -199,13 +210,13 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
     }
   };
   auto issue_w = [&](int buf) __attribute__((always_inline)) {
-    char* base = smem + buf * Cfg::WSTAGE;
+    char* base = smem + buf * STG;
 #pragma unroll
-    for (int i = 0; i < NQW; ++i) {
+    for (int i = 0; i < NQ; ++i) {
       const int q = wid + NW * i, c = (lane & 31) ^ (((2 * q + (lane >> 5)) & 3) << 2);
       // the two k-rows' Q rows, read through the scalar cache (no vector
       // load may join the DMA count); clamped into the expert's rows
-      const int t0 = wk * 64 + 2 * q;
+      const int t0 = wk * KR + 2 * q;
       int r0 = 0, r1 = 0;
       if (wt.rows > 0) {
         const int a0 = wt.off + min(t0, wt.rows - 1), a1 = wt.off + min(t0 + 1, wt.rows - 1);
@@ -247,36 +258,47 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
           for (int r = 0; r < 4; ++r) ce[(int64_t)(32 * j + 8 * g + r) * ct.ldc + 32 * i] = acc[i][j][4 * g + r];
   };
 
-  // prologue and iterations as gemm3p_kernel: X(0), W(0), W(1); iteration g
-  // issues X(g + 1) then W(g + 2), after waiting for X(g) and W(g)
-  issue_x(0);
-  issue_w(0);
-  if (1 < G) issue_w(1);
-  // A tile's stores (SB per wave) follow the DMAs of the iteration that
-  // issues them, so the next iteration's wait lets them stay in flight: it
-  // needs only X(g + 1) and older done, which precede W(g + 2) and the stores.
+  // Group g = X(g) then W(g), NQ instructions each per wave.  The prologue
+  // issues groups 0 .. D-1; iteration g waits for group g, issues group
+  // g + D into the stages group g - 1 used, multiplies stage g, and before
+  // that stores a finished tile (64 stores per wave) after its DMAs.  The
+  // wait needs group g done; after it the wave has issued the groups up to
+  // g + D - 1 and the stores of the last D iterations.  When any of those
+  // iterations stored, at least 64 operations follow group g, so
+  // vmcnt(63) covers it and leaves the stores in flight; otherwise the
+  // count is exact: 2 NQ per later group.
   constexpr int SB = FI * TI * 16;
-  static_assert(SB + NQW >= 63, "the cap below is the exact count otherwise");
-  bool pending = false, stored = false;
+  static_assert(SB >= 63, "a tile's stores alone exceed the wait's cap");
+  for (int g = 0; g < D && g < G; ++g) {
+    issue_x(g);
+    issue_w(g);
+  }
+  bool pending = false;
+  unsigned hist = 0;  // bit i: iteration g - 1 - i stored a tile
   for (int g = 0; g < G; ++g) {
-    if (g + 1 < G) {
-      if (stored) wait_vmcnt_barrier<63>();
-      else wait_vmcnt_barrier<NQW>();
+    if (hist & ((1u << D) - 1)) {
+      wait_vmcnt_barrier<63>();
     } else {
-      wait_vmcnt_barrier<0>();
+      switch (min(D - 1, G - 1 - g)) {
+        case 0: wait_vmcnt_barrier<0>(); break;
+        case 1: wait_vmcnt_barrier_c<2 * NQ>(); break;
+        case 2: wait_vmcnt_barrier_c<4 * NQ>(); break;
+        default: wait_vmcnt_barrier_c<6 * NQ>(); break;
+      }
     }
-    stored = false;
-    if (g + 1 < G) issue_x((g + 1) & 1);
-    if (g + 2 < G) issue_w((g + 2) % 3);
+    if (g + D < G) {
+      issue_x((g + D) % P);
+      issue_w((g + D) % P);
+    }
+    hist <<= 1;
     if (pending) {
       finish();
       zero();
       locate(++cj, ct);
       pending = false;
-      stored = true;
+      hist |= 1;
     }
-    mma_ktile_tt<FI, TI>(acc, smem + (g % 3) * Cfg::WSTAGE, smem + Cfg::X_OFF + (g & 1) * Cfg::XSTAGE, wf0, wt0,
-                         lane);
+    mma_ktile_tt<FI, TI, KR / 16>(acc, smem + (g % P) * STG, smem + P * STG + (g % P) * STG, wf0, wt0, lane);
     if (++ckt == ct.nkt) {
       ckt = 0;
       pending = true;
