@@ -372,7 +372,19 @@ struct ExpertGVProb {
   __device__ int seg_ktiles(int) const { return L * (int)sizeof(CT) / 128; }
   __device__ bool seg_f8(const State&, int) const { return f8; }
   __device__ int tokens_valid(const State& st) const { return st.rows; }
-  __device__ int feats_valid(const State&) const { return Cfg::BF; }
+  // GLU rows: 64-row groups of 32 gate and 32 value rows of one 32-unit
+  // range, so a wave's rows [wf0, wf0 + FW) hold only valid units iff
+  // wf0 + FW <= 2 * (units left in the tile).  The raw-output instantiation
+  // reports that (its epilogue stores are counted past the next wait, which
+  // needs every counted block's stores issued); the others keep the whole
+  // tile (missing units load as zeros and are never stored).
+  __device__ int feats_valid(const State& st) const {
+    if constexpr (RAW == 1) return min(Cfg::BF, 2 * (I - st.ft * (Cfg::BF / 2)));
+    return Cfg::BF;
+  }
+  // RAW = 1: vector stores per wave per fully valid 32-row token block (a
+  // gate and a value store4 per accumulator group)
+  static constexpr int kEpiStores = RAW == 1 ? Cfg::FI * 4 : 0;
   __device__ int64_t xes() const { return a8 ? 1 : (int64_t)sizeof(CT); }
   __device__ const char* x_row(const State& st, int, int r) const {
     if (r >= st.rows) return nullptr;
