@@ -657,10 +657,10 @@ hipError_t wgrad_dense(const Ctx& c, const WgDense* d, int n, const void* zero) 
   a.zero = static_cast<const char*>(zero);
   int tiles = 0;
   for (int s = 0; s < n; ++s) {
-    if (d[s].M % 256 || d[s].N % 256) return hipErrorInvalidValue;
+    if (d[s].M % 8 || d[s].M <= 0 || d[s].N % 256) return hipErrorInvalidValue;
     a.seg[s] = WgSeg{static_cast<const char*>(d[s].p), static_cast<const char*>(d[s].q), d[s].c, d[s].ldp, d[s].ldq,
                      d[s].M, d[s].N, tiles};
-    tiles += (d[s].M / 256) * (d[s].N / 256);
+    tiles += (int)cdiv(d[s].M, 256) * (d[s].N / 256);
   }
   a.tiles = tiles;
   return launch_wgrad(c, a);
@@ -1313,13 +1313,14 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   // --- up-projection ------------------------------------------------------
   // dense data gradients on the persistent engine above 256 tokens
   const bool dtg = T > 256 && LMOE_BW_DENSE_TGRAD;
-  // The dense weight gradients whose matrices are whole 256 x 256 tiles are
-  // queued and run together at the end on the persistent weight-gradient
-  // pipeline (their inputs all stay in the workspace until then).
+  // The dense weight gradients whose matrices have whole 256-column tiles
+  // (and rows in multiples of 8) are queued and run together at the end on
+  // the persistent weight-gradient pipeline (their inputs all stay in the
+  // workspace until then).
   WgDense dseg[kWgSegs];
   int nd = 0;
   auto add_dense = [&](const void* pp, int64_t ldp, const void* qq, int64_t ldq, float* cc, int M, int N) {
-    if (!(T > 256 && LMOE_BW_DENSE_WGRAD) || M % 256 || N % 256 || nd == kWgSegs) return false;
+    if (!(T > 256 && LMOE_BW_DENSE_WGRAD) || M % 8 || N % 256 || nd == kWgSegs) return false;
     dseg[nd++] = WgDense{pp, ldp, qq, ldq, cc, M, N};
     return true;
   };
@@ -1448,8 +1449,8 @@ lmoe_status lmoe_backward(const lmoe_shape* sh, const lmoe_weights* w, const voi
   }
   if (!rtg)
     LMOE_HIP((bg<BG_DENSE, 0, 1, 1, 0>(bop(dl, E), bop(w->w_router, H), gr->dx, H, T, H, E, 1, st, sh)), "dx (router)");
-  // dW_router (E rows: usually not whole 256-row tiles) stays on the
-  // register-staged GEMM; a whole-tile E joins the dense weight gradients
+  // dW_router (E rows; the last 256-row tile partial) joins the dense weight
+  // gradients when E is a multiple of 8, else the register-staged GEMM
   if (!add_dense(dl16, E, x, H, gr->dw_router, E, H))
     LMOE_HIP((bg<BG_DENSE, 1, 1, 1, 0>(bop(dl, E), bop(x, H), gr->dw_router, H, E, H, T, 0, st, sh)), "dW_router");
   if (lmoe_status s = record(ev, 4, st)) return s;

@@ -30,7 +30,9 @@ namespace lmoe {
 constexpr int kWgSegs = 12;
 
 // A dense product C = P^T Q over all rows [0, rows) of P [rows, ldp] and
-// Q [rows, ldq] (bf16), C fp32 [M, N] row-major; M and N multiples of 256.
+// Q [rows, ldq] (bf16), C fp32 [M, N] row-major; N a multiple of 256, M of 8
+// (the last 256-row tile stores only C's rows below M, and reads P's
+// columns past M from the zero page).
 struct WgSeg {
   const char* p;
   const char* q;
@@ -133,6 +135,7 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
     float* cb;       // C at (m0, n0)
     int64_t ldp, ldq, ldc;
     int off, rows, nkt;
+    int mv;          // rows of C in the tile (dense segments: M - m0, up to 256)
   };
   // experts: expert-major, then m tiles, then n tiles; dense: segment after
   // segment, m tiles, then n tiles
@@ -151,6 +154,7 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
       t.pb = p.p + ((int64_t)t.off * p.ldp + m0) * 2;
       t.qb = p.q + (int64_t)n0 * 2;
       t.cb = p.c + (int64_t)e * p.M * p.N + (int64_t)m0 * p.N + n0;
+      t.mv = 256;
     } else {
       int s = 0;
 #pragma unroll
@@ -167,6 +171,7 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
       t.pb = sg.p + (int64_t)m0 * 2;
       t.qb = sg.q + (int64_t)n0 * 2;
       t.cb = sg.c + (int64_t)m0 * sg.N + n0;
+      t.mv = min(256, sg.M - m0);
     }
     t.nkt = max(1, (t.rows + KR - 1) / KR);
   };
@@ -201,7 +206,9 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
     for (int i = 0; i < NQ; ++i) {
       const int q = wid + NW * i, kr = 2 * q + (lane >> 5), c = (lane & 31) ^ ((kr & 3) << 2);
       const int t = xk * KR + kr;
-      const char* src = t < xt.rows ? xt.pb + ((int64_t)t * xt.ldp + 8 * c) * 2 : p.zero + 16 * c;
+      // dense segments: P's columns past M come from the zero page too
+      const bool in = t < xt.rows && (KR == 32 || 8 * c < xt.mv);
+      const char* src = in ? xt.pb + ((int64_t)t * xt.ldp + 8 * c) * 2 : p.zero + 16 * c;
       dma16<0>(src, base + q * 1024);
     }
     if (++xk == xt.nkt) {
@@ -247,7 +254,11 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
     // block (i, j), register 4 g + r: row m = wt0 + 32 j + 8 g + 4 (lane / 32)
     // + r, column n = wf0 + 32 i + lane % 32; one store instruction writes two
     // 128-byte row segments
-    float* ce = ct.cb + (int64_t)(wt0 + 4 * (lane >> 5)) * ct.ldc + wf0 + (lane & 31);
+    const int m1 = wt0 + 4 * (lane >> 5);
+    float* ce = ct.cb + (int64_t)m1 * ct.ldc + wf0 + (lane & 31);
+    // dense segments: only rows of C below M (lim < 128 only in a last,
+    // partial 256-row tile)
+    const int lim = KR == 32 ? 256 : ct.mv - m1;
 #pragma unroll
     for (int i = 0; i < FI; ++i)
 #pragma unroll
@@ -255,7 +266,8 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ce[(int64_t)(32 * j + 8 * g + r) * ct.ldc + 32 * i] = acc[i][j][4 * g + r];
+          for (int r = 0; r < 4; ++r)
+            if (KR == 32 || 32 * j + 8 * g + r < lim) ce[(int64_t)(32 * j + 8 * g + r) * ct.ldc + 32 * i] = acc[i][j][4 * g + r];
   };
 
   // Group g = X(g) then W(g), NQ instructions each per wave.  The prologue
