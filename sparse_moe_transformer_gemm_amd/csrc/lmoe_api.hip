@@ -541,10 +541,7 @@ hipError_t expert_down(const Ctx& c, const void* act, const int32_t* offsets, co
 // Backward data gradients of the routed experts on the persistent engine,
 // weights transposed on the way into the MFMAs: out = x0 W0[e] (+ x1 W1[e]),
 // x_s [T*k, k_s] bf16 in expert order, W_s [E, k_s, F], out fp32 [T*k, F].
-#ifndef LMOE_T_TGRAD
-#define LMOE_T_TGRAD Tile3<256, 256, 4, 4, 0, 1, 0, 3, 0, 1>
-#endif
-typedef LMOE_T_TGRAD T2ExpertTGrad;
+typedef Tile3<256, 256, 4, 4, 0, 1, 0, 3, 0, 1> T2ExpertTGrad;
 hipError_t expert_tgrad(const Ctx& c, const int32_t* offsets, const int4* tiles, const int32_t* tcount, int F,
                         const void* x0, const void* w0, int k0, const void* x1, const void* w1, int k1, float* out) {
   using Cfg = T2ExpertTGrad;
