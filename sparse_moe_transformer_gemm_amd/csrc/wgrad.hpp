@@ -278,7 +278,10 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
   // g + D - 1 and the stores of the last D iterations.  When any of those
   // iterations stored, at least 64 operations follow group g, so
   // vmcnt(63) covers it and leaves the stores in flight; otherwise the
-  // count is exact: 2 NQ per later group.
+  // count is exact: 2 NQ per later group.  A wave whose rows of a dense
+  // segment's last, partial tile hold fewer than 64 rows of C skips the
+  // stores of the missing rows (their instructions are branched over), so
+  // it drains its counter right after its stores instead.
   constexpr int SB = FI * TI * 16;
   static_assert(SB >= 63, "a tile's stores alone exceed the wait's cap");
   for (int g = 0; g < D && g < G; ++g) {
@@ -304,7 +307,9 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad3p_kernel(const WGradArgs p) {
     }
     hist <<= 1;
     if (pending) {
+      const bool all_rows = KR == 32 || ct.mv - wt0 >= Cfg::TW;  // uniform over the wave
       finish();
+      if (!all_rows) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       zero();
       locate(++cj, ct);
       pending = false;
