@@ -132,7 +132,7 @@ struct DenseWalk {
   int first, count;   // big tiles of this launch
   int sf, st;         // sub-tiles per big tile
   __device__ int num_logical() const { return count * sf * st; }
-  __device__ bool map(int lg, int& ttb, int& ftb, int& qf, int& qt) const {
+  __host__ __device__ bool map(int lg, int& ttb, int& ftb, int& qf, int& qt) const {
     const int n = sf * st;
     if (lg >= count * n) return false;
     const int b = first + lg / n, q = lg - (lg / n) * n;

@@ -325,8 +325,56 @@ To with_cfg(const From& f) {
   return t;
 }
 
+// Side stream of the current device (created once, default priority): the
+// route GEMM's re-cut last round runs there when all its tiles belong to the
+// shared experts' segment, whose output only the up GEMM reads, so it
+// overlaps top-k and the permutation instead of delaying them.
+hipStream_t side_stream() {
+  static std::once_flag once[kMaxDevices];
+  static hipStream_t s[kMaxDevices];
+  const int dev = current_device();
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(once[dev], [&] {
+    if (hipStreamCreateWithFlags(&s[dev], hipStreamNonBlocking) != hipSuccess) s[dev] = nullptr;
+  });
+  return s[dev];
+}
+
+// One call's fork of work onto the side stream and its join back.  The
+// events are the call's own, so calls on other streams do not share them;
+// the destructor joins a fork that was never joined (an error path), so the
+// caller's stream stays ordered after the side work.
+struct TailFork {
+  hipStream_t main = nullptr, side = nullptr;
+  int defer_ft = 1 << 30;  // first big feature tile that may be deferred
+  hipEvent_t join = nullptr;
+  bool forked = false, joined = false;
+
+  hipError_t fork(hipStream_t st) {
+    hipEvent_t f = nullptr;
+    hipError_t e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&join, hipEventDisableTiming)) == hipSuccess &&
+        (e = hipEventRecord(f, st)) == hipSuccess && (e = hipStreamWaitEvent(side, f, 0)) == hipSuccess) {
+      main = st;
+      forked = true;
+    }
+    hipEventDestroy(f);
+    return e;
+  }
+  hipError_t wait(hipStream_t st) {
+    if (!forked || joined) return hipSuccess;
+    joined = true;
+    return hipStreamWaitEvent(st, join, 0);
+  }
+  ~TailFork() {
+    if (forked && !joined) hipStreamWaitEvent(main, join, 0);
+    if (join) hipEventDestroy(join);
+  }
+};
+
 template <class Cfg, typename CT, template <class, typename> class Prob>
-hipError_t launch_dense(Prob<Cfg, CT>& p, int nft, int ntt, hipStream_t st) {
+hipError_t launch_dense(Prob<Cfg, CT>& p, int nft, int ntt, hipStream_t st, TailFork* fk = nullptr) {
   const int ntiles = nft * ntt;
   p.walk = DenseWalk{nft, ntt, 0, ntiles, 1, 1};
   if constexpr (std::is_same_v<Cfg, T2Dense>) {
@@ -337,16 +385,32 @@ hipError_t launch_dense(Prob<Cfg, CT>& p, int nft, int ntt, hipStream_t st) {
       p.padded = (int)pad8(full);
       hipError_t e = launch_gemm<Cfg, CT>(p, p.padded, st);
       if (e != hipSuccess) return e;
+      // a tail wholly in the deferrable segment runs on the side stream
+      if (fk && fk->side) {
+        bool defer = true;
+        for (int b = 0; b < tail && defer; ++b) {
+          int ttb, ftb, qf, qt;
+          DenseWalk{nft, ntt, full, tail, 1, 1}.map(b, ttb, ftb, qf, qt);
+          defer = ftb >= fk->defer_ft;
+        }
+        if (defer) {
+          if ((e = fk->fork(st)) != hipSuccess) return e;
+          st = fk->side;
+        }
+      }
       if (4 * tail <= ncu) {
         auto q = with_cfg<Prob<T2DenseQuarter, CT>>(p);
         q.walk = DenseWalk{nft, ntt, full, tail, 2, 2};
         q.padded = (int)pad8((int64_t)tail * 4);
-        return launch_gemm<T2DenseQuarter, CT>(q, q.padded, st);
+        e = launch_gemm<T2DenseQuarter, CT>(q, q.padded, st);
+      } else {
+        auto q = with_cfg<Prob<T2DenseHalf, CT>>(p);
+        q.walk = DenseWalk{nft, ntt, full, tail, 2, 1};
+        q.padded = (int)pad8((int64_t)tail * 2);
+        e = launch_gemm<T2DenseHalf, CT>(q, q.padded, st);
       }
-      auto q = with_cfg<Prob<T2DenseHalf, CT>>(p);
-      q.walk = DenseWalk{nft, ntt, full, tail, 2, 1};
-      q.padded = (int)pad8((int64_t)tail * 2);
-      return launch_gemm<T2DenseHalf, CT>(q, q.padded, st);
+      if (e == hipSuccess && fk && fk->forked) e = hipEventRecord(fk->join, fk->side);
+      return e;
     }
   }
   p.padded = (int)pad8(ntiles);
@@ -358,7 +422,8 @@ hipError_t launch_dense(Prob<Cfg, CT>& p, int nft, int ntt, hipStream_t st) {
 // z_f32: z is written in fp32 (the W8A8 quantiser's input) instead of the
 // act dtype.
 template <class Cfg, typename CT>
-hipError_t xgemm(const Ctx& c, const void* x, float* logits, void* z, void* hs, bool z_f32 = false) {
+hipError_t xgemm(const Ctx& c, const void* x, float* logits, void* z, void* hs, bool z_f32 = false,
+                 TailFork* fk = nullptr) {
   const lmoe_shape* sh = c.sh;
   DenseXProb<Cfg, CT> p{};
   p.x = static_cast<const char*>(x);
@@ -407,11 +472,12 @@ hipError_t xgemm(const Ctx& c, const void* x, float* logits, void* z, void* hs, 
     s.kind = EPI_GLU;
     s.vec = 1;
     s.ft0 = ft;
+    if (fk) fk->defer_ft = ft;
     ft += (int)cdiv((int64_t)sh->S * sh->Is, Cfg::BF / 2);
   }
   if (ns == 0 || sh->T == 0) return hipSuccess;
   p.nseg = ns;
-  return launch_dense<Cfg, CT>(p, ft, (int)cdiv(sh->T, Cfg::BT), c.st);
+  return launch_dense<Cfg, CT>(p, ft, (int)cdiv(sh->T, Cfg::BT), c.st, fk);
 }
 
 // Two fp32 products of x in one pass: out_s = x . w_s^T ([T, rows_s], row
@@ -755,11 +821,12 @@ hipError_t dense_view(const Ctx& c, const Plan& pl, void* ws, DenseView& v) {
 
 // Dispatch on (dtype, tile).
 template <typename CT>
-hipError_t xgemm_any(const Ctx& c, const void* x, float* logits, void* z, void* hs, bool z_f32 = false) {
+hipError_t xgemm_any(const Ctx& c, const void* x, float* logits, void* z, void* hs, bool z_f32 = false,
+                    TailFork* fk = nullptr) {
   if constexpr (sizeof(CT) == 2) {
     if (!(hs && is_f8(c.sh)))
       return dense_small(c.sh) ? xgemm<T2Thin, CT>(c, x, logits, z, hs, z_f32)
-                               : xgemm<T2Dense, CT>(c, x, logits, z, hs, z_f32);
+                               : xgemm<T2Dense, CT>(c, x, logits, z, hs, z_f32, fk);
   }
   return dense_small(c.sh) ? xgemm<CfgSmall, CT>(c, x, logits, z, hs, z_f32)
                            : xgemm<CfgBig, CT>(c, x, logits, z, hs, z_f32);
@@ -1047,8 +1114,10 @@ lmoe_status lmoe_up(const lmoe_shape* sh, const lmoe_weights* w, const void* n, 
 namespace lmoe {
 namespace {
 
+// overlap: the route GEMM's last round may run on the side stream (not in the
+// entry point that must allocate nothing, which makes no events).
 lmoe_status forward_impl(const lmoe_shape* sh, const lmoe_weights* w, const void* x, void* y, int32_t* topk_idx,
-                         float* topk_w, void* ws, size_t ws_bytes, void* stream, void* const* ev) {
+                         float* topk_w, void* ws, size_t ws_bytes, void* stream, void* const* ev, bool overlap) {
   if (lmoe_status s = lmoe_validate(sh, w, ws_bytes)) return s;
   if (lmoe_status s = check_ws(sh, ws, ws_bytes)) return s;
   if (sh->T == 0) return LMOE_OK;
@@ -1075,7 +1144,9 @@ lmoe_status forward_impl(const lmoe_shape* sh, const lmoe_weights* w, const void
   DenseView dv;
   LMOE_HIP(dense_view(c, pl, ws, dv), "shared expert decode");
   const Ctx cd{&dv.sh, &dv.w, c.st};  // route and up GEMMs
-  LMOE_HIP(bf ? xgemm_any<bf16>(cd, x, logits, z, hs, zf) : xgemm_any<float>(cd, x, logits, z, hs), "route GEMM");
+  TailFork fk;
+  fk.side = overlap && hs ? side_stream() : nullptr;
+  LMOE_HIP(bf ? xgemm_any<bf16>(cd, x, logits, z, hs, zf, &fk) : xgemm_any<float>(cd, x, logits, z, hs), "route GEMM");
   if (lmoe_status s = record(ev, 1, c.st)) return s;
   LMOE_HIP(launch_topk(logits, w->b_router, sh->T, sh->E, sh->k, idx, tw, c.st), "top-k");
   if (lmoe_status s = record(ev, 2, c.st)) return s;
@@ -1107,6 +1178,7 @@ lmoe_status forward_impl(const lmoe_shape* sh, const lmoe_weights* w, const void
   LMOE_HIP(launch_combine_norm(bf, out, pos, tw, w->gamma, sh->T, sh->L, sh->k, sh->rms_eps, n, c.st),
            "combine + norm");
   if (lmoe_status s = record(ev, 6, c.st)) return s;
+  LMOE_HIP(fk.wait(c.st), "join of the route GEMM's last round");
   LMOE_HIP(bf ? upgemm_any<bf16>(cd, n, hs, y) : upgemm_any<float>(cd, n, hs, y), "up GEMM");
   if (lmoe_status s = record(ev, 7, c.st)) return s;
   return LMOE_OK;
@@ -1156,7 +1228,7 @@ extern "C" {
 lmoe_status lmoe_forward(const lmoe_shape* sh, const lmoe_weights* w, const void* x, void* y, int32_t* topk_idx,
                          float* topk_w, void* ws, size_t ws_bytes, void* stream, void* const* ev) {
   g_err[0] = 0;
-  return forward_impl(sh, w, x, y, topk_idx, topk_w, ws, ws_bytes, stream, ev);
+  return forward_impl(sh, w, x, y, topk_idx, topk_w, ws, ws_bytes, stream, ev, true);
 }
 
 lmoe_status lmoe_forward_noalloc(const lmoe_shape* sh, const lmoe_weights* w, const void* x, void* y,
@@ -1173,7 +1245,7 @@ lmoe_status lmoe_forward_noalloc(const lmoe_shape* sh, const lmoe_weights* w, co
   if (sh->T == 0) return LMOE_OK;
   void* ws = nullptr;
   if (lmoe_status s = scratch_on_device(&ws)) return s;
-  return forward_impl(sh, w, x, y, topk_idx, topk_w, ws, LMOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+  return forward_impl(sh, w, x, y, topk_idx, topk_w, ws, LMOE_NOALLOC_SCRATCH_BYTES, stream, nullptr, false);
 }
 
 lmoe_status lmoe_router_logits(const lmoe_shape* sh, const lmoe_weights* w, const void* x, float* logits,
