@@ -157,7 +157,12 @@ size_t lmoe_workspace_bytes(const lmoe_shape *shape);
  * and combine weights if not NULL.  stage_events: NULL, or an array of
  * LMOE_NUM_STAGES + 1 hipEvent_t recorded on `stream` before the first stage
  * and after each stage (route GEMM, top-k, permute, expert gate/value GEMM,
- * expert down GEMM, combine + norm, up GEMM), for timing.                        */
+ * expert down GEMM, combine + norm, up GEMM), for timing.  Part of the route
+ * GEMM (its last round of shared-expert tiles) may run on a library-owned side
+ * stream of the device, forked from `stream` after the route GEMM's main launch
+ * and joined back before the up GEMM, so all the layer's work precedes what is
+ * enqueued on `stream` after the call; the route GEMM's stage event then
+ * covers its main launch only.                                                 */
 #define LMOE_NUM_STAGES 7
 lmoe_status lmoe_forward(const lmoe_shape *shape, const lmoe_weights *w, const void *x, void *y,
                          int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
