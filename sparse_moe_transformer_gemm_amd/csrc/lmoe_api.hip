@@ -1144,8 +1144,13 @@ lmoe_status forward_impl(const lmoe_shape* sh, const lmoe_weights* w, const void
   DenseView dv;
   LMOE_HIP(dense_view(c, pl, ws, dv), "shared expert decode");
   const Ctx cd{&dv.sh, &dv.w, c.st};  // route and up GEMMs
+  // the side stream belongs to the current device: fork only when `stream`
+  // does too
   TailFork fk;
-  fk.side = overlap && hs ? side_stream() : nullptr;
+  bool same_dev = c.st == nullptr;
+  hipDevice_t sdev = -1;
+  if (!same_dev && hipStreamGetDevice(c.st, &sdev) == hipSuccess) same_dev = (int)sdev == current_device();
+  fk.side = overlap && hs && same_dev ? side_stream() : nullptr;
   LMOE_HIP(bf ? xgemm_any<bf16>(cd, x, logits, z, hs, zf, &fk) : xgemm_any<float>(cd, x, logits, z, hs), "route GEMM");
   if (lmoe_status s = record(ev, 1, c.st)) return s;
   LMOE_HIP(launch_topk(logits, w->b_router, sh->T, sh->E, sh->k, idx, tw, c.st), "top-k");
